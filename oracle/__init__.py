@@ -1,0 +1,3 @@
+"""CPU oracle of the MoE FFN forward (fp64).  Test infrastructure only: see moe_oracle."""
+from .moe_oracle import *  # noqa: F401,F403
+from .moe_oracle import __all__  # noqa: F401

@@ -1,0 +1,260 @@
+"""Plain fp64 CPU oracle of the fine-grained MoE FFN forward.
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; nothing in the library (``include/``,
+``sparse_mixture_experts_gemm_amd/``) imports, links or runs it, and it shares no code
+with the HIP path.  It is slow on purpose: every step is the plain definition, in fp64,
+on the exact values of the stored inputs (bf16 / fp32 / e4m3 x scale decoded exactly).
+
+Sources (web pages, cited by title and section):
+
+* [MoE-Eng] "大模型工程（一）：Transformer 到 MoE":
+  - section "混合专家：更多参数，相同 FLOPs", the MoEBlock listing: a bias-free gate
+    ``Linear(d_model, n_experts)``, top-k over the gate scores, softmax over the k
+    selected values, and for every slot and expert a masked, weighted sum of SwiGLU
+    expert outputs.
+  - section "MoE 数学：路由、容量与平衡详解": the router is the linear map g(x) = W_g x,
+    deterministic top-k with a fixed k per token, an always-on shared expert next to the
+    routed ones, and capacity c = infinity at inference (no token is dropped).
+  - section "变了什么，为什么变", item 3: SwiGLU (a gated FFN with gate, up and down
+    projections), citing Shazeer's "GLU variants" paper.
+* [FusionLLM] "FusionLLM：融合 MLA、GDN 与 MoE 的高效混合架构大模型训练框架":
+  - section "混合专家（MoE）": fine-grained DeepSeekMoE, 64 routed / 6 active experts,
+    group-limited routing and bias-free sigmoid gating.
+  - section "融合内核": a fused Linear+ReLU^2 FFN kernel and grouped GEMM after routing.
+  - section "模型配置与规模" (YAML): dim 2048, n_routed_experts 64,
+    n_activated_experts 6, n_shared_experts 4, moe_inter_dim 1536.
+* [MoE-Explainer] "开源混合架构大模型技术解析", section "四、工作原理：稀疏激活如何运行":
+  gate scores -> top-k experts -> only those experts run -> outputs merged by the gate
+  weights.
+
+Readings where the pages are silent (each one is a convention, stated here and in the
+design notes):
+
+* Group-limited routing is only named.  Groups are contiguous blocks of E/G experts; a
+  group's score is the sum of its n_g largest expert scores (n_g = 1: the group max);
+  the Gk best groups are kept and the top-k is taken over experts of kept groups.
+  PARITY UNPINNED as a reading: the pages fix no group-scoring rule; the brute-force
+  tests pin only that this module computes the rule stated here.
+* Ties: equal scores -> lower expert index first; equal group scores -> lower group
+  index first.  Slot order: score descending.
+* Weights: renormalised over the k selected scores, times route_scale (1.0).
+* Selection is decided on fp32 scores (the kernel's precision): ``route`` rounds the
+  fp64 scores to fp32 before selecting; group sums for n_g = 2 are fp32 adds.
+  The weights use the fp64 scores.
+* Shared experts: S independent FFNs of inter dim I, weight 1, applied to every token.
+* ReLU^2 expert: W2 (max(W1 x, 0))^2, no gate/up pair.
+* e4m3 expert weights: W[n, :] = scale[n] * e4m3(code[n, :]) (OCP e4m3, bias 7, max 448,
+  0x7F/0xFF NaN); activations stay bf16.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16", "decode_e4m3", "decode_weight", "router_logits", "gate_scores",
+    "group_scores", "select_experts", "routing_weights", "route", "silu", "expert_ffn",
+    "moe_forward", "permute", "expert_weights", "shared_weights", "decode_act",
+]
+
+
+# ----------------------------------------------------------------------------- codecs
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp64.  A bf16 value is the upper half of an IEEE fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """OCP e4m3 (FN) codes -> fp64: sign s, 4-bit exponent E (bias 7), 3-bit mantissa M.
+
+    normal (E > 0): (-1)^s 2^(E-7) (1 + M/8); subnormal (E = 0): (-1)^s 2^-6 (M/8);
+    E = 15 and M = 7 is NaN (no infinities).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def decode_act(a, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(a)
+    raise ValueError(dtype)
+
+
+def decode_weight(w, dtype: str, scale=None) -> np.ndarray:
+    """Stored expert weight -> fp64; e4m3 rows are multiplied by their fp32 scale."""
+    if dtype in ("f32", "bf16"):
+        return decode_act(w, dtype)
+    if dtype == "e4m3":
+        return decode_e4m3(w) * np.asarray(scale, dtype=np.float64)[..., None]
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------- routing
+def router_logits(x, w_r, logit_bias=None) -> np.ndarray:
+    """l[t, e] = sum_c x[t, c] W_r[e, c] (+ b[e]).  [MoE-Eng] g(x) = W_g x, no bias term
+    in the gate itself; b is the optional per-expert logit offset of the skewed workload."""
+    l = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64).T
+    if logit_bias is not None:
+        l = l + np.asarray(logit_bias, np.float64)[None, :]
+    return l
+
+
+def gate_scores(logits, fn: str) -> np.ndarray:
+    """sigmoid per expert ([FusionLLM] sigmoid gating) or softmax over all experts."""
+    l = np.asarray(logits, np.float64)
+    if fn == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-l))
+    if fn == "softmax":
+        z = np.exp(l - l.max(axis=-1, keepdims=True))
+        return z / z.sum(axis=-1, keepdims=True)
+    raise ValueError(fn)
+
+
+def group_scores(scores, G: int, n_g: int) -> np.ndarray:
+    """Score of each of G contiguous expert groups: sum of its n_g largest scores.
+
+    Computed in the dtype of ``scores`` (fp32 input -> fp32 adds)."""
+    s = np.asarray(scores)
+    T, E = s.shape
+    sg = np.sort(s.reshape(T, G, E // G), axis=-1)[..., ::-1]
+    acc = sg[..., 0].copy()
+    for i in range(1, n_g):
+        acc = acc + sg[..., i]
+    return acc
+
+
+def select_experts(scores, k: int, G: int = 1, Gk: int = 1, n_g: int = 1) -> np.ndarray:
+    """Group-limited top-k.  Returns idx [T, k] int32, slot order score-descending.
+
+    1. rank groups by (group score desc, group index asc) and keep the first Gk;
+    2. rank experts of kept groups by (score desc, expert index asc) and take k.
+    The comparisons are made on the values of ``scores`` exactly as given."""
+    s = np.asarray(scores)
+    T, E = s.shape
+    if G > 1 and Gk < G:
+        gs = group_scores(s, G, n_g)
+        gidx = np.broadcast_to(np.arange(G), (T, G))
+        gorder = np.lexsort((gidx, -gs), axis=-1)          # primary: -gs, then index
+        kept = np.zeros((T, G), dtype=bool)
+        np.put_along_axis(kept, gorder[:, :Gk], True, axis=-1)
+        eligible = np.repeat(kept, E // G, axis=1)
+    else:
+        eligible = np.ones((T, E), dtype=bool)
+    eidx = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((eidx, -s, ~eligible), axis=-1)     # eligible first, -s, index
+    return order[:, :k].astype(np.int32)
+
+
+def routing_weights(scores64, idx, renormalize: bool = True, route_scale: float = 1.0):
+    """w_j = route_scale * s_{e_j} / sum_i s_{e_i} (fp64).  [MoE-Eng] MoEBlock: softmax
+    over the selected values, i.e. the selected probabilities renormalised to sum 1."""
+    sel = np.take_along_axis(np.asarray(scores64, np.float64), np.asarray(idx, np.int64), axis=-1)
+    if renormalize:
+        sel = sel / sel.sum(axis=-1, keepdims=True)
+    return sel * route_scale
+
+
+def route(layer, tokens=None):
+    """Router of a stored layer: returns dict(logits, scores, idx, w) in fp64 (idx int32).
+
+    The selection is decided on the fp32-rounded scores (group sums in fp32)."""
+    s = layer.shape
+    x = decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
+    w_r = decode_act(layer.router, s.act_dtype)
+    l = router_logits(x, w_r, layer.logit_bias)
+    sc = gate_scores(l, s.score)
+    idx = select_experts(sc.astype(np.float32), s.k, s.G, s.Gk, s.n_g)
+    w = routing_weights(sc, idx, s.renormalize, s.route_scale)
+    return {"x": x, "logits": l, "scores": sc, "idx": idx, "w": w}
+
+
+# ----------------------------------------------------------------------------- experts
+def silu(z):
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x, w1, w3, w2, act: str):
+    """One expert on rows x [n, d]: SwiGLU W2 (silu(W1 x) * (W3 x)), or ReLU^2
+    W2 (max(W1 x, 0))^2.  Weights in nn.Linear layout [out, in]."""
+    a = x @ w1.T
+    if act == "swiglu":
+        h = silu(a) * (x @ w3.T)
+    elif act == "relu2":
+        h = np.maximum(a, 0.0) ** 2
+    else:
+        raise ValueError(act)
+    return h @ w2.T
+
+
+def expert_weights(layer, e: int):
+    s = layer.shape
+    dt = s.weight_dtype
+    sc = lambda a: None if a is None else a[e]
+    w1 = decode_weight(layer.w_gate[e], dt, sc(layer.s_gate))
+    w3 = None if layer.w_up is None else decode_weight(layer.w_up[e], dt, sc(layer.s_up))
+    w2 = decode_weight(layer.w_down[e], dt, sc(layer.s_down))
+    return w1, w3, w2
+
+
+def shared_weights(layer, i: int):
+    s = layer.shape
+    dt = s.weight_dtype
+    sc = lambda a: None if a is None else a[i]
+    w1 = decode_weight(layer.sh_gate[i], dt, sc(layer.sh_s_gate))
+    w3 = None if layer.sh_up is None else decode_weight(layer.sh_up[i], dt, sc(layer.sh_s_up))
+    w2 = decode_weight(layer.sh_down[i], dt, sc(layer.sh_s_down))
+    return w1, w3, w2
+
+
+def moe_forward(layer, tokens=None):
+    """out[t] = sum_j w_j FFN_{e_j}(x_t) + sum_s FFN^shared_s(x_t)  (fp64).
+
+    The masked per-(slot, expert) loop of the MoEBlock listing, with the slot loop folded
+    into the mask: for each expert, the tokens that picked it in any slot.  ``tokens``
+    restricts the computation to a subset of rows (every step is per token)."""
+    s = layer.shape
+    r = route(layer, tokens)
+    x, idx, w = r["x"], r["idx"], r["w"]
+    out = np.zeros_like(x)
+    for e in range(s.E):
+        rows, slots = np.nonzero(idx == e)
+        if rows.size == 0:
+            continue
+        w1, w3, w2 = expert_weights(layer, e)
+        out[rows] += w[rows, slots][:, None] * expert_ffn(x[rows], w1, w3, w2, s.act)
+    for i in range(s.S):
+        w1, w3, w2 = shared_weights(layer, i)
+        out += expert_ffn(x, w1, w3, w2, s.act)
+    r["out"] = out
+    return r
+
+
+# ----------------------------------------------------------------------------- permutation
+def permute(idx, E: int):
+    """Rows grouped by expert: order of (expert asc, token asc) over all (t, j) slots.
+
+    Returns counts [E], offsets [E+1] (exclusive scan of counts), perm_token [T*k]
+    (token of permuted row p) and slot_pos [T*k] (permuted row of slot t*k + j)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    e_flat = idx.reshape(-1)
+    t_flat = np.repeat(np.arange(T), k)
+    order = np.lexsort((t_flat, e_flat))            # stable: expert, then token
+    counts = np.bincount(e_flat, minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    perm_token = t_flat[order].astype(np.int32)
+    slot_pos = np.empty(T * k, dtype=np.int32)
+    slot_pos[order] = np.arange(T * k, dtype=np.int32)
+    return counts, offsets, perm_token, slot_pos

@@ -1,0 +1,471 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Every check here compares the oracle with something other than itself: exhaustive
+closed forms, library routines (torch dtype conversions, Python's sorted), brute force
+in pure Python on tiny inputs, identities of the method, and values printed on the pages
+(tests/golden).  The mutation tests at the end plant plausible mistakes in the oracle and
+check that a pin catches each one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32layer(**kw):
+    """A tiny fp32 layer (values exact in fp64) built by the shared seeded generator."""
+    base = dict(act_dtype="f32", weight_dtype="f32", T=5, d=6, E=4, k=2, S=0, I=3,
+                G=1, Gk=1, score="softmax")
+    base.update(kw)
+    return W.make_layer(W.small_shape(**base), cache=False)
+
+
+# ----------------------------------------------------------------------------- codecs
+def test_decode_bf16_exhaustive_matches_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = O.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_decode_bf16_closed_form_anchors():
+    # 1.0 = 0x3F80, -2.0 = 0xC000, smallest subnormal 2^-133 = 0x0001, max finite
+    assert O.decode_bf16([0x3F80])[0] == 1.0
+    assert O.decode_bf16([0xC000])[0] == -2.0
+    assert O.decode_bf16([0x0001])[0] == math.ldexp(1.0, -133)
+    assert O.decode_bf16([0x7F7F])[0] == math.ldexp(1 + 127 / 128, 127)
+
+
+def test_decode_e4m3_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.decode_e4m3(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_decode_e4m3_anchors():
+    d = O.decode_e4m3
+    assert d([0x7E])[0] == 448.0          # max normal
+    assert d([0x08])[0] == 2.0 ** -6      # min normal
+    assert d([0x01])[0] == 2.0 ** -9      # min subnormal
+    assert d([0x38])[0] == 1.0
+    assert np.isnan(d([0x7F])[0]) and np.isnan(d([0xFF])[0])
+    pos = d(np.arange(127, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)       # strictly increasing over the finite codes
+    assert np.array_equal(d(np.arange(128, 255, dtype=np.uint8)), -pos)
+
+
+def test_generator_bf16_encoder_is_rne():
+    rng = np.random.default_rng(5)
+    a = np.concatenate([rng.standard_normal(20000).astype(np.float32),
+                        np.array([1.00390625, 1.01171875, -3.0e-39, 65504.0], np.float32)])
+    ours = W.encode_bf16(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_generator_e4m3_quantiser_matches_torch_and_bounds_error():
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((16, 64)).astype(np.float32)
+    codes, scale = W.encode_e4m3_rows(w)
+    y = torch.from_numpy(w / scale[:, None])
+    ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    deq = O.decode_weight(codes, "e4m3", scale)
+    # RNE on a 3-bit mantissa: relative error <= 2^-4 for normals
+    big = np.abs(w) > scale[:, None] * 2.0 ** -6
+    assert np.all(np.abs(deq - w)[big] <= np.abs(w)[big] * 2.0 ** -4 + 1e-12)
+    assert np.allclose(np.max(np.abs(deq), axis=1), np.max(np.abs(w), axis=1), rtol=1e-6)
+
+
+# ----------------------------------------------------------------------------- router
+def test_router_logits_brute_force():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 5))
+    w = rng.standard_normal((4, 5))
+    b = rng.standard_normal(4)
+    got = O.router_logits(x, w, b)
+    for t in range(3):
+        for e in range(4):
+            ref = math.fsum([x[t, c] * w[e, c] for c in range(5)] + [b[e]])
+            assert abs(got[t, e] - ref) <= 1e-12 * (1 + abs(ref))
+    assert np.allclose(O.router_logits(x, w), got - b[None, :], atol=1e-13)
+
+
+def test_sigmoid_closed_forms():
+    s = O.gate_scores(np.array([[0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0]]), "sigmoid")[0]
+    assert s[0] == 0.5
+    assert abs(s[1] - 0.75) < 1e-15 and abs(s[2] - 0.25) < 1e-15
+    assert abs(s[3] - 1.0) < 1e-15 and 0.0 < s[4] < 1e-17
+
+
+def test_softmax_closed_forms():
+    l = np.array([[0.0, math.log(2.0), math.log(5.0)], [1000.0, 1000.0, -1000.0]])
+    s = O.gate_scores(l, "softmax")
+    assert np.allclose(s[0], [1 / 8, 2 / 8, 5 / 8], rtol=0, atol=1e-15)
+    assert np.allclose(s[1], [0.5, 0.5, 0.0], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(8)
+    r = O.gate_scores(rng.standard_normal((50, 9)), "softmax")
+    assert np.allclose(r.sum(axis=1), 1.0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- selection
+def _bf_select(s, k, G, Gk, n_g):
+    """Brute force from the definition for DISTINCT values: the kept groups are the Gk-subset
+    of groups with the largest total group score, and the selection is the k-subset of
+    eligible experts with the largest total score, listed by score descending."""
+    E = len(s)
+    gsz = E // G
+    def gscore(g):
+        mem = [np.float32(s[g * gsz + i]) for i in range(gsz)]
+        best = None
+        for c in itertools.combinations(mem, n_g):
+            acc = np.float32(0)
+            for v in sorted(c, reverse=True):
+                acc = np.float32(acc + v)           # fp32 adds, as the decision precision
+            best = acc if best is None else max(best, acc)
+        return float(best)
+    best_groups = max(itertools.combinations(range(G), Gk), key=lambda c: sum(gscore(g) for g in c))
+    elig = [e for e in range(E) if e // gsz in best_groups]
+    best = max(itertools.combinations(elig, k), key=lambda c: sum(float(s[e]) for e in c))
+    return sorted(best, key=lambda e: -float(s[e]))
+
+
+@pytest.mark.parametrize("E,G,Gk,n_g,k", [(6, 1, 1, 1, 2), (8, 4, 2, 1, 3), (8, 4, 2, 2, 3),
+                                          (12, 3, 1, 2, 4), (12, 6, 3, 1, 5), (9, 3, 2, 2, 1)])
+def test_select_brute_force_distinct(E, G, Gk, n_g, k):
+    rng = np.random.default_rng(100 + E * 7 + k)
+    for trial in range(40):
+        s = rng.random(E).astype(np.float32)                               # distinct values
+        gs = O.group_scores(s[None, :], G, n_g)[0]
+        if len(set(s.tolist())) < E or len(set(gs.tolist())) < G:
+            continue
+        got = O.select_experts(s[None, :], k, G, Gk, n_g)[0].tolist()
+        assert got == _bf_select(s, k, G, Gk, n_g), (s, got)
+
+
+def test_select_without_group_limit_is_stable_argsort():
+    rng = np.random.default_rng(9)
+    s = (rng.integers(0, 6, size=(200, 16)) / 8.0).astype(np.float32)      # many ties
+    got = O.select_experts(s, 5)
+    ref = np.argsort(-s, axis=1, kind="stable")[:, :5]
+    assert np.array_equal(got, ref)
+    # Gk = G gives the same result as no group limit
+    assert np.array_equal(O.select_experts(s, 5, G=4, Gk=4, n_g=2), ref)
+
+
+def test_select_k1_is_argmax():
+    rng = np.random.default_rng(10)
+    s = (rng.integers(0, 4, size=(300, 8)) / 4.0).astype(np.float32)
+    assert np.array_equal(O.select_experts(s, 1)[:, 0], np.argmax(s, axis=1))
+
+
+def test_select_hand_written_tie_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "tie_cases.json")))["cases"]
+    for c in cases:
+        s = np.array([c["scores"]], dtype=np.float32)
+        got = O.select_experts(s, c["k"], c["G"], c["Gk"], c["n_g"])[0].tolist()
+        assert got == c["expect"], c
+
+
+def test_group_scores_top2_brute_force_fp32():
+    rng = np.random.default_rng(11)
+    s = rng.random((40, 12)).astype(np.float32)
+    gs = O.group_scores(s, 4, 2)
+    assert gs.dtype == np.float32
+    for t in range(40):
+        for g in range(4):
+            mem = s[t, 3 * g:3 * g + 3]
+            ref = max(np.float32(a) + np.float32(b) for a, b in itertools.combinations(mem, 2))
+            assert gs[t, g] == ref
+
+
+def test_every_token_lands_in_exactly_k_distinct_experts():
+    rng = np.random.default_rng(12)
+    s = rng.random((500, 64)).astype(np.float32)
+    idx = O.select_experts(s, 6, 8, 4, 1)
+    assert idx.shape == (500, 6)
+    assert all(len(set(r)) == 6 for r in idx.tolist())
+    assert np.all((idx >= 0) & (idx < 64))
+    # at most Gk distinct groups are used per token
+    assert all(len(set(e // 8 for e in r)) <= 4 for r in idx.tolist())
+
+
+# ----------------------------------------------------------------------------- weights
+def test_weights_sum_to_one_and_positive():
+    rng = np.random.default_rng(13)
+    sc = O.gate_scores(rng.standard_normal((100, 16)), "sigmoid")
+    idx = O.select_experts(sc.astype(np.float32), 4, 4, 2, 1)
+    w = O.routing_weights(sc, idx)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-15)
+    assert np.all(w > 0)
+    w2 = O.routing_weights(sc, idx, renormalize=False, route_scale=2.5)
+    assert np.allclose(w2, 2.5 * np.take_along_axis(sc, idx.astype(np.int64), axis=1))
+
+
+def test_renormalised_topk_softmax_is_softmax_of_selected_logits():
+    """MoEBlock listing: softmax over the top-k gate values.  Equal to renormalising the
+    full softmax over the selected experts."""
+    rng = np.random.default_rng(14)
+    l = rng.standard_normal((64, 8)) * 2
+    sc = O.gate_scores(l, "softmax")
+    idx = O.select_experts(sc.astype(np.float32), 2)
+    w = O.routing_weights(sc, idx)
+    top_l = torch.from_numpy(np.take_along_axis(l, idx.astype(np.int64), axis=1))
+    ref = torch.softmax(top_l, dim=-1).numpy()
+    assert np.allclose(w, ref, rtol=0, atol=1e-14)
+    # and the top-k over softmax scores equals the top-k over the logits
+    assert np.array_equal(idx, np.argsort(-l, axis=1, kind="stable")[:, :2])
+
+
+# ----------------------------------------------------------------------------- experts
+def _bf_ffn(xr, w1, w3, w2, act):
+    I, d = len(w1), len(xr)
+    h = []
+    for i in range(I):
+        a = math.fsum(w1[i][c] * xr[c] for c in range(d))
+        if act == "swiglu":
+            b = math.fsum(w3[i][c] * xr[c] for c in range(d))
+            h.append(a / (1.0 + math.exp(-a)) * b)
+        else:
+            h.append(max(a, 0.0) ** 2)
+    return [math.fsum(w2[n][i] * h[i] for i in range(I)) for n in range(len(w2))]
+
+
+def test_silu_closed_forms_and_torch():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 30.0, -30.0, 1.5])
+    got = O.silu(z)
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(got[2] + 0.25 * math.log(3.0)) < 1e-15
+    assert np.allclose(got, torch.nn.functional.silu(torch.from_numpy(z)).numpy(), rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu2"])
+def test_expert_ffn_brute_force(act):
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((3, 5))
+    w1, w3, w2 = rng.standard_normal((4, 5)), rng.standard_normal((4, 5)), rng.standard_normal((6, 4))
+    got = O.expert_ffn(x, w1, w3 if act == "swiglu" else None, w2, act)
+    for t in range(3):
+        ref = _bf_ffn(x[t].tolist(), w1.tolist(), w3.tolist(), w2.tolist(), act)
+        assert np.allclose(got[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_relu2_closed_form():
+    # W1 = I, W2 = I: out = max(x, 0)^2 elementwise
+    x = np.array([[-2.0, -0.5, 0.0, 0.5, 3.0]])
+    eye = np.eye(5)
+    assert np.array_equal(O.expert_ffn(x, eye, None, eye, "relu2")[0], [0, 0, 0, 0.25, 9.0])
+
+
+# ----------------------------------------------------------------------------- whole layer
+def test_single_expert_equals_dense_swiglu_ffn():
+    lay = f32layer(E=1, k=1, G=1, Gk=1, score="sigmoid", T=4, d=5, I=3)
+    out = O.moe_forward(lay)["out"]
+    w1, w3, w2 = [a.astype(np.float64).tolist() for a in (lay.w_gate[0], lay.w_up[0], lay.w_down[0])]
+    for t in range(4):
+        ref = _bf_ffn(lay.x[t].astype(np.float64).tolist(), w1, w3, w2, "swiglu")
+        assert np.allclose(out[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_k_equals_E_softmax_is_dense_gate_weighted_sum():
+    lay = f32layer(E=4, k=4, G=1, Gk=1, score="softmax", T=5, d=6, I=3)
+    out = O.moe_forward(lay)["out"]
+    for t in range(5):
+        xr = lay.x[t].astype(np.float64).tolist()
+        logits = [math.fsum(xr[c] * float(lay.router[e, c]) for c in range(6)) for e in range(4)]
+        m = max(logits)
+        z = [math.exp(v - m) for v in logits]
+        p = [v / math.fsum(z) for v in z]
+        ref = [0.0] * 6
+        for e in range(4):
+            y = _bf_ffn(xr, lay.w_gate[e].astype(np.float64).tolist(), lay.w_up[e].astype(np.float64).tolist(),
+                        lay.w_down[e].astype(np.float64).tolist(), "swiglu")
+            ref = [a + p[e] * b for a, b in zip(ref, y)]
+        assert np.allclose(out[t], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_sparse_mixture_brute_force_with_groups_and_shared():
+    """Full layer on a tiny case: brute force per token from the definition."""
+    lay = f32layer(E=6, k=2, G=3, Gk=2, n_g=2, score="sigmoid", T=4, d=5, I=3, S=2)
+    r = O.moe_forward(lay)
+    for t in range(4):
+        xr = lay.x[t].astype(np.float64).tolist()
+        logits = [math.fsum(xr[c] * float(lay.router[e, c]) for c in range(5)) for e in range(6)]
+        s = [1.0 / (1.0 + math.exp(-v)) for v in logits]
+        sel = _bf_select(np.array(s, np.float32), 2, 3, 2, 2)
+        tot = math.fsum(s[e] for e in sel)
+        ref = [0.0] * 5
+        for e in sel:
+            y = _bf_ffn(xr, lay.w_gate[e].astype(np.float64).tolist(), lay.w_up[e].astype(np.float64).tolist(),
+                        lay.w_down[e].astype(np.float64).tolist(), "swiglu")
+            ref = [a + s[e] / tot * b for a, b in zip(ref, y)]
+        for i in range(2):
+            y = _bf_ffn(xr, lay.sh_gate[i].astype(np.float64).tolist(), lay.sh_up[i].astype(np.float64).tolist(),
+                        lay.sh_down[i].astype(np.float64).tolist(), "swiglu")
+            ref = [a + b for a, b in zip(ref, y)]
+        assert r["idx"][t].tolist() == sel
+        assert np.allclose(r["out"][t], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_shared_experts_equal_one_concatenated_ffn():
+    lay = f32layer(E=2, k=1, S=3, T=6, d=8, I=4, score="sigmoid")
+    no_routed = O.moe_forward(lay)["out"] - _routed_part(lay)
+    x = lay.x.astype(np.float64)
+    w1 = np.concatenate(list(lay.sh_gate.astype(np.float64)), axis=0)     # [S*I, d]
+    w3 = np.concatenate(list(lay.sh_up.astype(np.float64)), axis=0)
+    w2 = np.concatenate(list(lay.sh_down.astype(np.float64)), axis=1)     # [d, S*I]
+    ref = np.array([_bf_ffn(x[t].tolist(), w1.tolist(), w3.tolist(), w2.tolist(), "swiglu") for t in range(6)])
+    assert np.allclose(no_routed, ref, rtol=1e-11, atol=1e-12)
+
+
+def _routed_part(lay):
+    r = O.route(lay)
+    out = np.zeros((lay.shape.T, lay.shape.d))
+    for t in range(lay.shape.T):
+        for j in range(lay.shape.k):
+            e = int(r["idx"][t, j])
+            out[t] += r["w"][t, j] * np.array(_bf_ffn(r["x"][t].tolist(), lay.w_gate[e].astype(np.float64).tolist(),
+                                                      lay.w_up[e].astype(np.float64).tolist(),
+                                                      lay.w_down[e].astype(np.float64).tolist(), "swiglu"))
+    return out
+
+
+def test_e4m3_layer_equals_dequantised_fp64_layer():
+    """e4m3 weights: the oracle's expert is the bf16/fp64 expert of the dequantised weights."""
+    lay = W.make_layer(W.small_shape(T=4, d=32, E=4, k=2, G=1, Gk=1, S=1, I=16, act="relu2",
+                                     weight_dtype="e4m3", seed=21), cache=False)
+    r = O.moe_forward(lay)
+    x = O.decode_bf16(lay.x)
+    for t in range(4):
+        ref = np.zeros(32)
+        for j, e in enumerate(r["idx"][t]):
+            w1 = O.decode_e4m3(lay.w_gate[e]) * lay.s_gate[e][:, None].astype(np.float64)
+            w2 = O.decode_e4m3(lay.w_down[e]) * lay.s_down[e][:, None].astype(np.float64)
+            ref += r["w"][t, j] * np.array(_bf_ffn(x[t].tolist(), w1.tolist(), None, w2.tolist(), "relu2"))
+        w1 = O.decode_e4m3(lay.sh_gate[0]) * lay.sh_s_gate[0][:, None].astype(np.float64)
+        w2 = O.decode_e4m3(lay.sh_down[0]) * lay.sh_s_down[0][:, None].astype(np.float64)
+        ref += np.array(_bf_ffn(x[t].tolist(), w1.tolist(), None, w2.tolist(), "relu2"))
+        assert np.allclose(r["out"][t], ref, rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- permutation
+def test_permute_matches_python_sorted():
+    rng = np.random.default_rng(16)
+    s = rng.random((37, 16)).astype(np.float32)
+    idx = O.select_experts(s, 3, 4, 2, 1)
+    counts, offsets, perm_token, slot_pos = O.permute(idx, 16)
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(37) for j in range(3))
+    assert perm_token.tolist() == [t for (_, t, _) in pairs]
+    assert [slot_pos[t * 3 + j] for (_, t, j) in pairs] == list(range(37 * 3))
+    assert counts.tolist() == [sum(1 for p in pairs if p[0] == e) for e in range(16)]
+    assert offsets[0] == 0 and offsets[-1] == 37 * 3
+    assert np.array_equal(np.diff(offsets), counts)
+    # inverse bijection: the slot at permuted row p belongs to token perm_token[p]
+    assert np.array_equal(perm_token[slot_pos], np.repeat(np.arange(37), 3))
+    assert sorted(slot_pos.tolist()) == list(range(37 * 3))
+
+
+def test_permute_empty_experts_and_single_token():
+    idx = np.array([[5, 2]], dtype=np.int32)
+    counts, offsets, perm_token, slot_pos = O.permute(idx, 8)
+    assert counts.tolist() == [0, 0, 1, 0, 0, 1, 0, 0]
+    assert offsets.tolist() == [0, 0, 0, 1, 1, 1, 2, 2, 2]
+    assert perm_token.tolist() == [0, 0] and slot_pos.tolist() == [1, 0]
+
+
+# ----------------------------------------------------------------------------- workloads
+def test_fusionllm_shapes_match_the_yaml():
+    y = json.load(open(os.path.join(GOLDEN, "fusionllm_moe_yaml.json")))
+    for name in ("fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2"):
+        s = W.SHAPES[name]
+        assert (s.d, s.E, s.k, s.S, s.I) == (y["dim"], y["n_routed_experts"], y["n_activated_experts"],
+                                            y["n_shared_experts"], y["moe_inter_dim"])
+
+
+def test_ffn_flop_and_param_accounting_matches_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "llama70b_ffn_counts.json")))
+    s = W.small_shape(d=g["d_model"], I=g["d_ffn"], E=1, k=1, S=0, G=1, Gk=1)
+    ffn_flops = s.flops_per_token - 2 * s.d * s.E       # one SwiGLU FFN, no router
+    assert abs(ffn_flops - g["ffn_flops_per_token_printed"]) <= g["ffn_flops_rounding"]
+    assert abs(3 * s.d * s.I - g["ffn_params_printed"]) <= g["ffn_params_rounding"]
+    assert W.SHAPES["fusionllm_bf16"].flops_per_token == 189_005_824
+
+
+def test_decode_routing_is_prefix_of_prefill_routing():
+    """Routing is per token, and the decode workload takes the prefill layer's first 64
+    x rows and weights, so its selection equals rows 0..63 of the prefill selection."""
+    pre = W.make_layer("fusionllm_bf16")
+    dec = W.make_layer("decode_bf16")
+    r_pre = O.route(pre, tokens=np.arange(64))
+    r_dec = O.route(dec)
+    assert np.array_equal(r_pre["idx"], r_dec["idx"])
+    assert np.array_equal(r_pre["w"], r_dec["w"])
+
+
+# ----------------------------------------------------------------------------- mutations
+def _swapped_ffn(x, w1, w3, w2, act):
+    return O.expert_ffn(x, w3 if w3 is not None else w1, w1, w2, act)
+
+
+@pytest.mark.parametrize("mutation", ["swap_gate_up", "no_renorm", "tie_high_index",
+                                      "token_desc_perm", "drop_shared", "transpose_down"])
+def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
+    """Each mutation is a plausible slip in the oracle; the named pin must then fail."""
+    if mutation == "swap_gate_up":
+        monkeypatch.setattr(O.moe_oracle, "expert_ffn", _swapped_ffn)
+        check = test_single_expert_equals_dense_swiglu_ffn
+    elif mutation == "no_renorm":
+        orig = O.moe_oracle.routing_weights
+        monkeypatch.setattr(O.moe_oracle, "routing_weights",
+                            lambda s, i, renormalize=True, route_scale=1.0: orig(s, i, False, route_scale))
+        check = test_k_equals_E_softmax_is_dense_gate_weighted_sum
+        # softmax scores over all E already sum to 1 at k = E; use the grouped case instead
+        check = test_sparse_mixture_brute_force_with_groups_and_shared
+    elif mutation == "tie_high_index":
+        orig_sel = O.select_experts
+        def bad(s, k, G=1, Gk=1, n_g=1):
+            s = np.asarray(s)
+            E = s.shape[1]
+            return (E - 1 - orig_sel(s[:, ::-1], k, 1, 1, n_g)) if (G == 1 or Gk == G) else orig_sel(s, k, G, Gk, n_g)
+        monkeypatch.setattr(O, "select_experts", bad)
+        check = test_select_hand_written_tie_cases
+    elif mutation == "token_desc_perm":
+        orig_perm = O.permute
+        def bad(idx, E):
+            c, o, _, _ = orig_perm(idx, E)
+            idx = np.asarray(idx)
+            T, k = idx.shape
+            order = np.lexsort((-np.repeat(np.arange(T), k), idx.reshape(-1)))
+            pt = np.repeat(np.arange(T), k)[order].astype(np.int32)
+            sp = np.empty(T * k, np.int32)
+            sp[order] = np.arange(T * k)
+            return c, o, pt, sp
+        monkeypatch.setattr(O, "permute", bad)
+        check = test_permute_matches_python_sorted
+    elif mutation == "drop_shared":
+        monkeypatch.setattr(O.moe_oracle, "shared_weights",
+                            lambda lay, i: tuple(np.zeros_like(a) if a is not None else None
+                                                 for a in O.moe_oracle.expert_weights(lay, 0)))
+        check = test_shared_experts_equal_one_concatenated_ffn
+    elif mutation == "transpose_down":
+        def bad_ffn(x, w1, w3, w2, act):
+            a = x @ w1.T
+            h = O.silu(a) * (x @ w3.T) if act == "swiglu" else np.maximum(a, 0) ** 2
+            return h @ w2[:, ::-1].T                      # wrong column order of W2
+        monkeypatch.setattr(O.moe_oracle, "expert_ffn", bad_ffn)
+        check = test_single_expert_equals_dense_swiglu_ffn
+    with pytest.raises(AssertionError):
+        check()
