@@ -1,0 +1,261 @@
+"""Benchmark of the MoE FFN forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one pass of the whole layer (route -> permute -> grouped GEMMs for routed and
+shared experts -> combine) over one batch of seeded synthetic tokens, with inputs and
+weights resident in HBM.  Prints ONE JSON line.  The headline workload is the
+FusionLLM-shape layer (T=4096, dim 2048, 64 routed + 4 shared experts, top-6, bf16);
+the decode-shaped layer (T=64, same weights) is reported alongside with its HBM rate.
+Per-stage times come from HIP events recorded between the stage launches on the stream
+they run on; the step calls the same C-ABI entry points moe_forward chains.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+STAGES = ["route", "permute", "up_routed", "up_shared", "down_routed", "down_shared", "combine"]
+
+
+def stage_flops(s, T):
+    """Algorithmic FLOPs of each stage (padding and masked work excluded)."""
+    c_up = 4 if s.act == "swiglu" else 2
+    return {
+        "route": 2 * T * s.d * s.E,
+        "permute": 0,
+        "up_routed": T * s.k * c_up * s.d * s.I,
+        "up_shared": T * s.S * c_up * s.d * s.I,
+        "down_routed": T * s.k * 2 * s.d * s.I,
+        "down_shared": T * s.S * 2 * s.d * s.I,
+        "combine": 0,
+    }
+
+
+def weight_bytes_per_expert(s):
+    wb = 1 if s.weight_dtype == "e4m3" else (4 if s.weight_dtype == "f32" else 2)
+    n_mats = 3 if s.act == "swiglu" else 2
+    scales = 4 * (s.I * (n_mats - 1) + s.d) if s.weight_dtype == "e4m3" else 0
+    return n_mats * s.d * s.I * wb + scales
+
+
+def to_dev(a):
+    """numpy array in its stored encoding -> device tensor (bf16 bits travel as int16)."""
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+    return t.to("cuda")
+
+
+class Runner:
+    """Device-resident layer and the per-stage C-ABI calls of one forward."""
+
+    def __init__(self, shape, lay, weights=None):
+        import torch
+        import sparse_mixture_experts_gemm_amd as moe
+        self.torch, self.moe, self.s = torch, moe, shape
+        s = shape
+        self.cfg = moe.make_config(s.T, s.d, s.E, s.k, G=s.G, Gk=s.Gk, n_g=s.n_g, S=s.S, I=s.I,
+                                   score=s.score, renormalize=s.renormalize,
+                                   route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
+                                   weight_dtype=s.weight_dtype)
+        if weights is None:
+            t = {n: to_dev(getattr(lay, n)) for n in
+                 ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                  "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]}
+            weights = moe.Weights(**t)
+        self.w = weights
+        self.x = to_dev(lay.x)
+        dev = "cuda"
+        T, k, E, d, I, S = s.T, s.k, s.E, s.d, s.I, s.S
+        adt = torch.int16 if s.act_dtype == "bf16" else torch.float32
+        i32, f32 = torch.int32, torch.float32
+        self.idx = torch.empty(T * k, dtype=i32, device=dev)
+        self.tw = torch.empty(T * k, dtype=f32, device=dev)
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.pt = torch.empty(T * k, dtype=i32, device=dev)
+        self.sp = torch.empty(T * k, dtype=i32, device=dev)
+        self.pw = torch.empty(T * k, dtype=f32, device=dev)
+        self.pws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        self.h = torch.empty((T * k, I), dtype=adt, device=dev)
+        self.hs = torch.empty((T, max(S, 1) * I), dtype=adt, device=dev)
+        self.y = torch.empty((T * k, d), dtype=adt, device=dev)
+        self.ys = torch.empty((T, d), dtype=adt, device=dev)
+        self.out = torch.empty((T, d), dtype=adt, device=dev)
+        self.ws = torch.empty(moe.workspace_size(self.cfg), dtype=torch.uint8, device=dev)
+
+    def stage_calls(self):
+        m, c, s = self.moe, self.cfg, self.s
+        T, Tk = s.T, s.T * s.k
+        calls = [
+            ("route", lambda: m.route(c, self.x, self.w.tensors["router"],
+                                      self.w.tensors["logit_bias"], None, self.idx, self.tw)),
+            ("permute", lambda: m.permute(c, self.idx, self.tw, self.counts, self.offsets, self.pt,
+                                          self.sp, self.pw, self.pws)),
+            ("up_routed", lambda: m.grouped_gemm(c, m.MOE_STAGE_UP, m.MOE_EXPERTS_ROUTED, self.x,
+                                                 self.pt, self.offsets, Tk, self.w, None, self.h)),
+            ("up_shared", lambda: m.grouped_gemm(c, m.MOE_STAGE_UP, m.MOE_EXPERTS_SHARED, self.x,
+                                                 None, None, T, self.w, None, self.hs)),
+            ("down_routed", lambda: m.grouped_gemm(c, m.MOE_STAGE_DOWN, m.MOE_EXPERTS_ROUTED, self.h,
+                                                   None, self.offsets, Tk, self.w, self.pw, self.y)),
+            ("down_shared", lambda: m.grouped_gemm(c, m.MOE_STAGE_DOWN, m.MOE_EXPERTS_SHARED,
+                                                   self.hs, None, None, T, self.w, None, self.ys)),
+            ("combine", lambda: m.combine(c, self.y, self.sp, self.ys if s.S > 0 else None,
+                                          self.out)),
+        ]
+        if s.S == 0:
+            calls = [cl for cl in calls if cl[0] not in ("up_shared", "down_shared")]
+        return calls
+
+    def forward(self):
+        self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+
+    def timed(self, steps, warmup):
+        """Stage-wise steps with HIP events between the stages on the current stream."""
+        torch = self.torch
+        calls = self.stage_calls()
+        for _ in range(warmup):
+            for _, f in calls:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record()
+            for j, (_, f) in enumerate(calls):
+                f()
+                ev[i][j + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_stage = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+                     for j, (name, _) in enumerate(calls)}
+        step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]))
+        total_ms = ev[0][0].elapsed_time(ev[-1][-1])
+        return step_ms, total_ms, wall, per_stage
+
+    def timed_forward(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.forward()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            self.forward()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+
+def decode_bytes(s, counts):
+    touched = int((counts > 0).sum())
+    ab = 2 if s.act_dtype == "bf16" else 4
+    return (touched + s.S) * weight_bytes_per_expert(s) + s.E * s.d * ab + 2 * s.T * s.d * ab, touched
+
+
+def cpu_baseline(lay, n_tokens):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                    or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    O.moe_forward(lay, tokens=np.arange(n_tokens))
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle forward of the first {n_tokens} tokens of the same layer "
+                      f"(decode of all expert weights included), {dt:.1f} s wall"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fusionllm_bf16")
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
+              "sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+
+    shape = W.SHAPES[args.workload]
+    lay = W.make_layer(shape)
+    run = Runner(shape, lay)
+    step_ms, total_ms, wall, per_stage = run.timed(args.steps, args.warmup)
+    fwd_ms = run.timed_forward(args.steps, args.warmup)
+    T = shape.T
+    fl = stage_flops(shape, T)
+    total_flops = sum(fl.values())
+    dom = max(per_stage, key=lambda k: per_stage[k])
+    achieved = fl[dom] / (per_stage[dom] * 1e-3) / 1e12
+    res = {
+        "metric": "MoE fwd tokens/s & % MFMA peak, d2048 E64 k6 T4096; decode T64 % HBM BW",
+        "value": T / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.act_dtype if shape.weight_dtype != "e4m3" else "bf16-act/e4m3-weight",
+        "data": "synthetic (seeded Gaussian x and weights, N(0,1/fan_in))",
+        "config": {"workload": shape.name, "tokens": T, "dim": shape.d, "experts": shape.E,
+                   "shared_experts": shape.S, "top_k": shape.k, "groups": shape.G,
+                   "topk_groups": shape.Gk, "inter_dim": shape.I, "act": shape.act,
+                   "weights": shape.weight_dtype},
+        "layer_tflops": total_flops / (step_ms * 1e-3) / 1e12,
+        "layer_mfma_frac": total_flops / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "forward_call_ms": fwd_ms,
+        "stage_ms": per_stage,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_decode:
+        dshape = W.SHAPES["decode_bf16"]
+        dlay = W.make_layer(dshape)
+        drun = Runner(dshape, dlay, weights=run.w)     # same weights as the prefill layer
+        d_ms, _, _, d_stage = drun.timed(args.steps, args.warmup)
+        d_fwd = drun.timed_forward(args.steps, args.warmup)
+        nbytes, touched = decode_bytes(dshape, drun.counts.cpu().numpy())
+        res["decode"] = {"workload": dshape.name, "tokens": dshape.T, "ms_per_step": d_ms,
+                         "forward_call_ms": d_fwd, "tokens_per_s": dshape.T / (d_ms * 1e-3),
+                         "algorithmic_bytes": nbytes, "experts_touched": touched,
+                         "hbm_GBps": nbytes / (d_ms * 1e-3) / 1e9,
+                         "hbm_frac": nbytes / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "stage_ms": d_stage}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(lay, args.cpu_tokens)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

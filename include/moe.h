@@ -1,0 +1,183 @@
+/*
+ * libmoe — forward pass of a fine-grained MoE FFN layer on MI355X (gfx950).
+ *
+ * The layer (as the pages state it):
+ *   router      l = W_r x (+ b)            "大模型工程（一）：Transformer 到 MoE", section
+ *                                           "MoE 数学：路由、容量与平衡详解" (g(x) = W_g x, no bias)
+ *   scores      s = sigmoid(l) or softmax(l)  "FusionLLM：融合 MLA、GDN 与 MoE 的高效混合架构大模型训练框架",
+ *                                           section "混合专家（MoE）" (sigmoid gating); MoEBlock listing (softmax)
+ *   selection   group-limited top-k, weights renormalised over the k picks
+ *   experts     SwiGLU  W2 (silu(W1 x) * (W3 x))   or  ReLU^2  W2 (max(W1 x, 0))^2
+ *   shared      S always-on experts added with weight 1
+ *   combine     out[t] = sum_j w_j FFN_{e_j}(x_t) + sum_s FFN^sh_s(x_t)
+ *
+ * Conventions of every call:
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller; the library
+ *     keeps no pointer after a call returns, allocates no device memory and never
+ *     synchronises.  Work is enqueued on `stream` (NULL = the default stream).
+ *   - Weights use the nn.Linear layout [out, in], stacked over experts on dim 0.
+ *   - Arguments are validated on the host before anything is enqueued; a call that
+ *     returns an error has enqueued nothing.  Asynchronous device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses this interface.
+ *   - act_dtype applies to x, the router weight, the intermediates and the output
+ *     (MOE_F32 or MOE_BF16); weight_dtype applies to the expert weights (MOE_F32 with
+ *     MOE_F32 activations; MOE_BF16 or MOE_FP8_E4M3 with MOE_BF16 activations).
+ *   - Limits: 1 <= E <= 64, 1 <= k <= E, E % G == 0, 1 <= Gk <= G, k <= Gk*E/G,
+ *     n_g in {1, 2} and n_g <= E/G; dim and inter_dim multiples of 64 (bf16/e4m3) or
+ *     of 4 (fp32); num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned.
+ *     Violations return MOE_ERR_INVALID_ARG (bad values) or MOE_ERR_UNSUPPORTED
+ *     (valid but not implemented).
+ *   - Calls are re-entrant; calls that share output or workspace buffers on the same
+ *     stream are ordered by the stream, on different streams they race.
+ */
+#ifndef LIBMOE_MOE_H
+#define LIBMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, out-of-range or inconsistent value */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request outside what this build implements        */
+  MOE_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required          */
+  MOE_ERR_HIP = 4,          /* a HIP launch or runtime call failed (see moe_last_hip_error) */
+  MOE_ERR_INTERNAL = 5      /* unexpected internal failure                              */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
+typedef enum { MOE_STAGE_UP = 0, MOE_STAGE_DOWN = 1 } moe_stage;
+typedef enum { MOE_EXPERTS_ROUTED = 0, MOE_EXPERTS_SHARED = 1 } moe_expert_set;
+
+typedef struct {
+  int32_t num_tokens;        /* T                                                        */
+  int32_t dim;               /* d                                                        */
+  int32_t num_experts;       /* E routed experts                                         */
+  int32_t top_k;             /* k experts per token                                      */
+  int32_t num_groups;        /* G contiguous groups of E/G experts (1 = no group limit)  */
+  int32_t topk_groups;       /* Gk groups kept per token                                 */
+  int32_t group_score_topn;  /* n_g: a group's score is the sum of its n_g best scores   */
+  int32_t num_shared;        /* S always-on shared experts (0 allowed)                   */
+  int32_t inter_dim;         /* I, inter dim of every routed and shared expert           */
+  moe_score_fn score_fn;     /* sigmoid or softmax over the E logits                     */
+  int32_t renormalize;       /* 1: w = s / sum(selected s); 0: w = s                     */
+  float route_scale;         /* multiplies every routing weight (1.0f)                   */
+  moe_act act;               /* SwiGLU (gate, up, down) or ReLU^2 (gate, down)           */
+  moe_dtype act_dtype;       /* MOE_F32 or MOE_BF16                                      */
+  moe_dtype weight_dtype;    /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3                        */
+} moe_config;
+
+/* Expert weights.  [out, in] per expert, stacked on dim 0.  e4m3 weights carry one fp32
+ * scale per output channel (per row): W[n, :] = scale[n] * e4m3(code[n, :]). */
+typedef struct {
+  const void* router;        /* [E, d] act_dtype                                           */
+  const float* logit_bias;   /* [E] added to the logits before scoring, or NULL            */
+  const void* w_gate;        /* [E, I, d]                                                  */
+  const void* w_up;          /* [E, I, d]; NULL for MOE_ACT_RELU2                          */
+  const void* w_down;        /* [E, d, I]                                                  */
+  const float* s_gate;       /* [E, I]  e4m3 scales, else NULL                             */
+  const float* s_up;         /* [E, I]                                                     */
+  const float* s_down;       /* [E, d]                                                     */
+  const void* sh_gate;       /* [S, I, d]  (NULL when S = 0)                               */
+  const void* sh_up;         /* [S, I, d]                                                  */
+  const void* sh_down;       /* [S, d, I]                                                  */
+  const float* sh_s_gate;    /* [S, I]                                                     */
+  const float* sh_s_up;      /* [S, I]                                                     */
+  const float* sh_s_down;    /* [S, d]                                                     */
+} moe_weights;
+
+/* Bytes of device workspace moe_forward needs for this config (host only, no HIP call).
+ * moe_permute and moe_grouped_gemm need at most the same amount. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Router, scoring and group-limited top-k for T tokens.
+ *   l[t,e] = sum_c x[t,c] router[e,c] (+ logit_bias[e]), fp32 accumulation;
+ *   s = sigmoid(l) or softmax over e;
+ *   groups g = experts [g*E/G, (g+1)*E/G); group score = sum of its n_g largest s;
+ *   keep the Gk best groups (ties: lower group index), then the k best experts of the
+ *   kept groups (ties: lower expert index), slot order score-descending;
+ *   w_j = route_scale * s_j / sum_i s_i (or route_scale * s_j without renormalisation).
+ * x [T, d] act_dtype; router [E, d] act_dtype; scores [T, E] fp32 (optional, NULL = not
+ * written); topk_idx [T, k] int32; topk_w [T, k] fp32.
+ * Source: the MoEBlock listing and section "MoE 数学：路由、容量与平衡详解" of
+ * "大模型工程（一）：Transformer 到 MoE"; group-limited sigmoid gating in section
+ * "混合专家（MoE）" of the FusionLLM training-framework page. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
+                     const float* logit_bias, float* scores, int32_t* topk_idx,
+                     float* topk_w, hipStream_t stream);
+
+/* The selection step of moe_route alone, on given fp32 scores [T, E] (every score must be
+ * finite and >= 0, as sigmoid and softmax values are).  Same outputs and tie rules. */
+moe_status moe_select(const moe_config* cfg, const float* scores, int32_t* topk_idx,
+                      float* topk_w, hipStream_t stream);
+
+/* Expert-sorted permutation of the T*k (token, slot) pairs: rows ordered by
+ * (expert ascending, token ascending); deterministic.
+ *   counts[e]      number of slots routed to expert e                    [E]
+ *   offsets[e]     exclusive prefix sum of counts; offsets[E] = T*k       [E+1]
+ *   perm_token[p]  token of permuted row p                               [T*k]
+ *   slot_pos[t*k+j] permuted row of slot j of token t                    [T*k]
+ *   perm_weight[p] topk_w of permuted row p (optional: both topk_w and perm_weight
+ *                  NULL, or both set)                                    [T*k]
+ * All int32/fp32 device buffers.  ws: at least moe_workspace_size bytes.
+ * Source: token routing to experts and per-expert batching ("MoE 数学" section and the
+ * expert-parallel paragraph of "大模型工程（一）"; "批处理策略" of "开源混合架构大模型技术解析"). */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                       int32_t* slot_pos, float* perm_weight, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* One stage of the expert FFNs as a grouped GEMM over expert segments.
+ *   set = MOE_EXPERTS_ROUTED: segment e is rows [offsets[e], offsets[e+1]) of a row space
+ *         of `rows` rows (offsets: device [E+1], from moe_permute); routed weights.
+ *   set = MOE_EXPERTS_SHARED: one segment of `rows` rows; the S shared experts act as one
+ *         expert of inter dim S*I (offsets ignored).
+ *   A row r of the row space is a[row_index[r]] when row_index is given (a gather, e.g.
+ *   perm_token over x), else a[r].
+ *   stage UP:   a rows have d elements (act_dtype); out[r] = act(a_r W_gate^T, a_r W_up^T),
+ *               [rows, I] (routed) or [rows, S*I] (shared), act_dtype;
+ *               SwiGLU: silu(g) * u; ReLU^2: max(g, 0)^2.
+ *   stage DOWN: a rows have I (routed) or S*I (shared) elements; out[r] =
+ *               row_weight[r] * (a_r W_down^T) (row_weight NULL = 1), [rows, d], act_dtype;
+ *               for the shared set the S experts' outputs are summed.
+ * e4m3 weights are multiplied by their per-output-channel scales.  fp32 accumulation.
+ * ws: at least moe_workspace_size bytes.
+ * Source: grouped GEMM after routing and the fused Linear+ReLU^2 kernel, section
+ * "融合内核" of the FusionLLM training-framework page; SwiGLU in item 3 of section
+ * "变了什么，为什么变" of "大模型工程（一）". */
+moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_set set,
+                            const void* a, const int32_t* row_index, const int32_t* offsets,
+                            int32_t rows, const moe_weights* w, const float* row_weight,
+                            void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* out[t] = sum_{j<k} y_perm[slot_pos[t*k+j]] + y_shared[t], summed in that fixed order in
+ * fp32, rounded to act_dtype.  y_perm [T*k, d], y_shared [T, d] or NULL, out [T, d].
+ * Source: the weighted merge of the selected experts' outputs (MoEBlock listing;
+ * "四、工作原理" of "开源混合架构大模型技术解析") plus the always-on shared experts. */
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
+                       const void* y_shared, void* out, hipStream_t stream);
+
+/* The whole layer: route -> permute -> UP/DOWN grouped GEMMs (routed and shared) ->
+ * combine.  x [T, d] and out [T, d] act_dtype; ws at least moe_workspace_size bytes
+ * (16-byte aligned).  The per-stage tensors (topk_idx, topk_w, counts, offsets,
+ * perm_token, slot_pos, intermediates) live in ws. */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status status);
+
+/* The hipError_t of the last MOE_ERR_HIP returned on the calling thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMOE_MOE_H */

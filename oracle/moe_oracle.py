@@ -56,6 +56,7 @@ import numpy as np
 __all__ = [
     "decode_bf16", "decode_e4m3", "decode_weight", "router_logits", "gate_scores",
     "group_scores", "select_experts", "routing_weights", "route", "silu", "expert_ffn",
+    "expert_up", "expert_down", "combine",
     "moe_forward", "permute", "expert_weights", "shared_weights", "decode_act",
 ]
 
@@ -185,17 +186,37 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+def expert_up(x, w1, w3, act: str):
+    """First half of an expert on rows x [n, d]: silu(W1 x) * (W3 x) for SwiGLU, or
+    max(W1 x, 0)^2 for ReLU^2.  Weights in nn.Linear layout [out, in]."""
+    a = x @ w1.T
+    if act == "swiglu":
+        return silu(a) * (x @ w3.T)
+    if act == "relu2":
+        return np.maximum(a, 0.0) ** 2
+    raise ValueError(act)
+
+
+def expert_down(h, w2):
+    """Down projection W2 h of the inter activations h [n, I]; W2 is [d, I]."""
+    return h @ w2.T
+
+
 def expert_ffn(x, w1, w3, w2, act: str):
     """One expert on rows x [n, d]: SwiGLU W2 (silu(W1 x) * (W3 x)), or ReLU^2
     W2 (max(W1 x, 0))^2.  Weights in nn.Linear layout [out, in]."""
-    a = x @ w1.T
-    if act == "swiglu":
-        h = silu(a) * (x @ w3.T)
-    elif act == "relu2":
-        h = np.maximum(a, 0.0) ** 2
-    else:
-        raise ValueError(act)
-    return h @ w2.T
+    return expert_down(expert_up(x, w1, w3, act), w2)
+
+
+def combine(y_perm, slot_pos, y_shared, k: int):
+    """out[t] = sum_j y_perm[slot_pos[t*k + j]] (+ y_shared[t]): the merge of the k weighted
+    expert outputs of every token back into token order."""
+    y = np.asarray(y_perm, np.float64)
+    sp = np.asarray(slot_pos, np.int64).reshape(-1, k)
+    out = y[sp].sum(axis=1)
+    if y_shared is not None:
+        out = out + np.asarray(y_shared, np.float64)
+    return out
 
 
 def expert_weights(layer, e: int):

@@ -1,0 +1,196 @@
+"""Python binding of libmoe (MoE FFN forward on MI355X / gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so``; torch tensors provide device memory and the current stream.  The entry
+points mirror the C ABI in ``include/moe.h`` (same names without the ``moe_`` prefix).
+If the library has not been built, every call raises ``LibraryMissing``; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
+    "workspace_size", "route", "select", "permute", "grouped_gemm", "combine", "forward",
+    "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
+    "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
+    "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
+]
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_INTERNAL = range(6)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_ACT_SWIGLU, MOE_ACT_RELU2 = 0, 1
+MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
+MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
+
+EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_permute",
+                    "moe_grouped_gemm", "moe_combine", "moe_forward", "moe_status_string",
+                    "moe_last_hip_error"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32), ("dim", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+        ("group_score_topn", ctypes.c_int32), ("num_shared", ctypes.c_int32),
+        ("inter_dim", ctypes.c_int32), ("score_fn", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float),
+        ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+    ]
+
+
+_W_FIELDS = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+             "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]
+
+
+class _WeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _W_FIELDS]
+
+
+class Weights:
+    """Device weight tensors of a layer (``None`` for absent ones); keeps them alive."""
+
+    def __init__(self, **tensors):
+        unknown = set(tensors) - set(_W_FIELDS)
+        if unknown:
+            raise TypeError(f"unknown weight fields {sorted(unknown)}")
+        self.tensors = {n: tensors.get(n) for n in _W_FIELDS}
+        self.c = _WeightsC(**{n: _ptr(t) for n, t in self.tensors.items()})
+
+
+_LIB = None
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise LibraryMissing(f"{path} is not built; run "
+                                 "`python -m sparse_mixture_experts_gemm_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cfgp = ctypes.POINTER(Config)
+        wp = ctypes.POINTER(_WeightsC)
+        sig = {
+            "moe_workspace_size": [cfgp, ctypes.POINTER(sz)],
+            "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_select": [cfgp, vp, vp, vp, vp],
+            "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_grouped_gemm": [cfgp, i32, i32, vp, vp, vp, i32, wp, vp, vp, vp, sz, vp],
+            "moe_combine": [cfgp, vp, vp, vp, vp, vp],
+            "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
+            "moe_last_hip_error": [],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int32
+        L.moe_status_string.argtypes = [ctypes.c_int32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().moe_status_string(int(status)).decode()
+    except LibraryMissing:
+        return "unknown"
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renormalize=True,
+                route_scale=1.0, act="swiglu", act_dtype="bf16", weight_dtype="bf16") -> Config:
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3}
+    return Config(num_tokens=T, dim=d, num_experts=E, top_k=k, num_groups=G, topk_groups=Gk,
+                  group_score_topn=n_g, num_shared=S, inter_dim=I,
+                  score_fn={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score],
+                  renormalize=int(bool(renormalize)), route_scale=float(route_scale),
+                  act={"swiglu": MOE_ACT_SWIGLU, "relu2": MOE_ACT_RELU2}[act],
+                  act_dtype=dt[act_dtype], weight_dtype=dt[weight_dtype])
+
+
+def workspace_size(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def route(cfg, x, router, logit_bias, scores, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(router), _ptr(logit_bias),
+                           _ptr(scores), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_route")
+
+
+def select(cfg, scores, topk_idx, topk_w, stream=None):
+    _check(lib().moe_select(ctypes.byref(cfg), _ptr(scores), _ptr(topk_idx), _ptr(topk_w),
+                            _stream(stream)), "moe_select")
+
+
+def permute(cfg, topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, ws,
+            ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (0 if ws is None else ws.numel() * ws.element_size())
+    _check(lib().moe_permute(ctypes.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                             _ptr(offsets), _ptr(perm_token), _ptr(slot_pos), _ptr(perm_weight),
+                             _ptr(ws), nb, _stream(stream)), "moe_permute")
+
+
+def grouped_gemm(cfg, stage, expert_set, a, row_index, offsets, rows, weights: Weights,
+                 row_weight, out, ws=None, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (0 if ws is None else ws.numel() * ws.element_size())
+    _check(lib().moe_grouped_gemm(ctypes.byref(cfg), int(stage), int(expert_set), _ptr(a),
+                                  _ptr(row_index), _ptr(offsets), int(rows),
+                                  ctypes.byref(weights.c), _ptr(row_weight), _ptr(out), _ptr(ws),
+                                  nb, _stream(stream)), "moe_grouped_gemm")
+
+
+def combine(cfg, y_perm, slot_pos, y_shared, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(cfg), _ptr(y_perm), _ptr(slot_pos), _ptr(y_shared),
+                             _ptr(out), _stream(stream)), "moe_combine")
+
+
+def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
+                             _ptr(ws), nb, _stream(stream)), "moe_forward")

@@ -1,0 +1,367 @@
+// libmoe C ABI: argument validation, workspace carve-up and kernel launches.
+// Declarations and the meaning of every argument are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "internal.h"
+#include "moe.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return MOE_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+moe_status current_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  int v = g_num_cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (v <= 0) v = 1;
+    g_num_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  *cus = v;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_config(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->dim <= 0 || c->num_experts <= 0 || c->top_k <= 0 ||
+      c->num_groups <= 0 || c->topk_groups <= 0 || c->num_shared < 0 || c->inter_dim <= 0)
+    return MOE_ERR_INVALID_ARG;
+  const int E = c->num_experts, G = c->num_groups;
+  if (c->top_k > E || E % G != 0 || c->topk_groups > G) return MOE_ERR_INVALID_ARG;
+  if ((long long)c->top_k > (long long)c->topk_groups * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (c->group_score_topn != 1 && c->group_score_topn != 2) return MOE_ERR_INVALID_ARG;
+  if (c->group_score_topn > E / G) return MOE_ERR_INVALID_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  // implemented combinations and shapes
+  if (E > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->act_dtype == MOE_F32) {
+    if (c->weight_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (c->dim % 16 != 0 || c->inter_dim % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (c->weight_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+    if (c->dim % 64 != 0 || c->inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  const long long Tk = (long long)c->num_tokens * c->top_k;
+  if (Tk > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if ((long long)c->num_shared * c->inter_dim > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe::RouteParams route_params(const moe_config* c) {
+  moe::RouteParams p;
+  p.T = c->num_tokens;
+  p.d = c->dim;
+  p.E = c->num_experts;
+  p.k = c->top_k;
+  p.G = c->num_groups;
+  p.Gk = c->topk_groups;
+  p.n_g = c->group_score_topn;
+  p.score_fn = c->score_fn;
+  p.renormalize = c->renormalize;
+  p.route_scale = c->route_scale;
+  return p;
+}
+
+size_t act_size(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Workspace of moe_forward, in carve order.
+struct Carve {
+  size_t topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, perm_ws;
+  size_t h_routed, h_shared, y_routed, y_shared, total;
+};
+
+Carve carve(const moe_config* c) {
+  const size_t T = (size_t)c->num_tokens, k = (size_t)c->top_k, E = (size_t)c->num_experts;
+  const size_t d = (size_t)c->dim, I = (size_t)c->inter_dim, S = (size_t)c->num_shared;
+  const size_t as = act_size(c);
+  Carve w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align_up(bytes); return at; };
+  w.topk_idx = take(T * k * 4);
+  w.topk_w = take(T * k * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.perm_token = take(T * k * 4);
+  w.slot_pos = take(T * k * 4);
+  w.perm_weight = take(T * k * 4);
+  w.perm_ws = take(moe::permute_ws_bytes((int)T, (int)E));
+  w.h_routed = take(T * k * I * as);
+  w.h_shared = take(T * S * I * as);
+  w.y_routed = take(T * k * d * as);
+  w.y_shared = take(S > 0 ? T * d * as : 0);
+  w.total = o;
+  return w;
+}
+
+moe_status gemm_params(const moe_config* c, moe_stage stage, moe_expert_set set, const void* a,
+                       const int32_t* row_index, const int32_t* offsets, int32_t rows,
+                       const moe_weights* w, const float* row_weight, void* out,
+                       moe::GemmParams* p) {
+  if (w == nullptr || a == nullptr || out == nullptr || rows < 0) return MOE_ERR_INVALID_ARG;
+  if (stage != MOE_STAGE_UP && stage != MOE_STAGE_DOWN) return MOE_ERR_INVALID_ARG;
+  if (set != MOE_EXPERTS_ROUTED && set != MOE_EXPERTS_SHARED) return MOE_ERR_INVALID_ARG;
+  const bool routed = set == MOE_EXPERTS_ROUTED;
+  const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
+  const bool swiglu = c->act == MOE_ACT_SWIGLU;
+  if (routed && offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!routed && c->num_shared == 0) return MOE_ERR_INVALID_ARG;
+  const int I_eff = routed ? c->inter_dim : c->num_shared * c->inter_dim;
+  moe::GemmParams g{};
+  g.a = a;
+  g.row_index = row_index;
+  g.offsets = routed ? offsets : nullptr;
+  g.nseg = routed ? c->num_experts : 1;
+  g.rows = rows;
+  g.d = c->dim;
+  g.I = c->inter_dim;
+  g.S = c->num_shared;
+  g.row_weight = row_weight;
+  g.out = out;
+  if (stage == MOE_STAGE_UP) {
+    g.N = I_eff;
+    g.K = c->dim;
+    g.kblock = c->dim;
+    g.w_gate = routed ? w->w_gate : w->sh_gate;
+    g.w_up = routed ? w->w_up : w->sh_up;
+    g.s_gate = routed ? w->s_gate : w->sh_s_gate;
+    g.s_up = routed ? w->s_up : w->sh_s_up;
+    if (g.w_gate == nullptr || (swiglu && g.w_up == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (fp8 && (g.s_gate == nullptr || (swiglu && g.s_up == nullptr))) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(g.w_gate) || (swiglu && !aligned16(g.w_up))) return MOE_ERR_UNSUPPORTED;
+  } else {
+    g.N = c->dim;
+    g.K = I_eff;
+    g.kblock = c->inter_dim;
+    g.w_down = routed ? w->w_down : w->sh_down;
+    g.s_down = routed ? w->s_down : w->sh_s_down;
+    if (g.w_down == nullptr || (fp8 && g.s_down == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(g.w_down)) return MOE_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(a) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  *p = g;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime or launch error";
+    case MOE_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    *bytes = carve(cfg).total;
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
+                     const float* logit_bias, float* scores, int32_t* topk_idx, float* topk_w,
+                     hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (x == nullptr || router == nullptr || topk_idx == nullptr || topk_w == nullptr)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(router)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_route(route_params(cfg), cfg->act_dtype, x, router, logit_bias,
+                                        scores, topk_idx, topk_w, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_select(const moe_config* cfg, const float* scores, int32_t* topk_idx,
+                      float* topk_w, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (scores == nullptr || topk_idx == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_select(route_params(cfg), scores, topk_idx, topk_w, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
+                       float* perm_weight, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (counts == nullptr || offsets == nullptr) return MOE_ERR_INVALID_ARG;
+    if (cfg->num_tokens > 0 && (topk_idx == nullptr || perm_token == nullptr || slot_pos == nullptr))
+      return MOE_ERR_INVALID_ARG;
+    if ((topk_w == nullptr) != (perm_weight == nullptr)) return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::permute_ws_bytes(cfg->num_tokens, cfg->num_experts);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_permute(cfg->num_tokens, cfg->num_experts, cfg->top_k, topk_idx,
+                                          topk_w, counts, offsets, perm_token, slot_pos,
+                                          perm_weight, ws, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_set set,
+                            const void* a, const int32_t* row_index, const int32_t* offsets,
+                            int32_t rows, const moe_weights* w, const float* row_weight,
+                            void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (rows == 0) return MOE_OK;
+    moe::GemmParams p;
+    st = gemm_params(cfg, stage, set, a, row_index, offsets, rows, w, row_weight, out, &p);
+    if (st != MOE_OK) return st;
+    int cus = 0;
+    st = current_cus(&cus);
+    if (st != MOE_OK) return st;
+    return hip_status(moe::launch_grouped_gemm(
+        p, stage == MOE_STAGE_UP ? moe::Stage::Up : moe::Stage::Down, cfg->act, cfg->act_dtype,
+        cfg->weight_dtype, cus, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
+                       const void* y_shared, void* out, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (y_perm == nullptr || slot_pos == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y_perm) || !aligned16(out) || (y_shared != nullptr && !aligned16(y_shared)))
+      return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_combine(cfg->num_tokens, cfg->dim, cfg->top_k, cfg->act_dtype,
+                                          y_perm, slot_pos, y_shared, out, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (w == nullptr) return MOE_ERR_INVALID_ARG;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (x == nullptr || out == nullptr || w->router == nullptr) return MOE_ERR_INVALID_ARG;
+    const Carve cv = carve(cfg);
+    if (ws == nullptr || ws_bytes < cv.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws) || !aligned16(x) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+    char* base = static_cast<char*>(ws);
+    auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+    int32_t* idx = static_cast<int32_t*>(at(cv.topk_idx));
+    float* tw = static_cast<float*>(at(cv.topk_w));
+    int32_t* counts = static_cast<int32_t*>(at(cv.counts));
+    int32_t* offsets = static_cast<int32_t*>(at(cv.offsets));
+    int32_t* perm_token = static_cast<int32_t*>(at(cv.perm_token));
+    int32_t* slot_pos = static_cast<int32_t*>(at(cv.slot_pos));
+    float* perm_weight = static_cast<float*>(at(cv.perm_weight));
+    const int T = cfg->num_tokens, Tk = cfg->num_tokens * cfg->top_k;
+    const bool shared = cfg->num_shared > 0;
+
+    // validate every grouped-GEMM argument before the first launch
+    moe::GemmParams up_r, up_s{}, dn_r, dn_s{};
+    st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_ROUTED, x, perm_token, offsets, Tk, w,
+                     nullptr, at(cv.h_routed), &up_r);
+    if (st != MOE_OK) return st;
+    st = gemm_params(cfg, MOE_STAGE_DOWN, MOE_EXPERTS_ROUTED, at(cv.h_routed), nullptr, offsets,
+                     Tk, w, perm_weight, at(cv.y_routed), &dn_r);
+    if (st != MOE_OK) return st;
+    if (shared) {
+      st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_SHARED, x, nullptr, nullptr, T, w, nullptr,
+                       at(cv.h_shared), &up_s);
+      if (st != MOE_OK) return st;
+      st = gemm_params(cfg, MOE_STAGE_DOWN, MOE_EXPERTS_SHARED, at(cv.h_shared), nullptr, nullptr,
+                       T, w, nullptr, at(cv.y_shared), &dn_s);
+      if (st != MOE_OK) return st;
+    }
+    if (!aligned16(w->router)) return MOE_ERR_UNSUPPORTED;
+    int cus = 0;
+    st = current_cus(&cus);
+    if (st != MOE_OK) return st;
+
+    hipError_t e = moe::launch_route(route_params(cfg), cfg->act_dtype, x, w->router,
+                                     w->logit_bias, nullptr, idx, tw, stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, idx, tw, counts, offsets, perm_token,
+                            slot_pos, perm_weight, at(cv.perm_ws), stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, cfg->act_dtype,
+                                 cfg->weight_dtype, cus, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (shared) {
+      e = moe::launch_grouped_gemm(up_s, moe::Stage::Up, cfg->act, cfg->act_dtype,
+                                   cfg->weight_dtype, cus, stream);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, cfg->act_dtype,
+                                 cfg->weight_dtype, cus, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (shared) {
+      e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, cfg->act_dtype,
+                                   cfg->weight_dtype, cus, stream);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    e = moe::launch_combine(T, cfg->dim, cfg->top_k, cfg->act_dtype, at(cv.y_routed), slot_pos,
+                            shared ? at(cv.y_shared) : nullptr, out, stream);
+    return hip_status(e);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

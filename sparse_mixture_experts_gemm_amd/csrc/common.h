@@ -1,0 +1,84 @@
+// Device-side helpers shared by the libmoe kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> canonical quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Four e4m3 codes (one per byte) -> four bf16 values packed in two uint32.
+// e4m3 (bias 7) placed in the fp32 exponent/mantissa fields and multiplied by 2^120
+// gives the exact value for normals and subnormals alike; three mantissa bits fit
+// bf16 exactly, so the truncation to the upper half is exact.  NaN codes are not
+// produced by the quantiser and are not special-cased.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
+  const float two120 = 1.329227995784916e36f;  // 2^120
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c = (q >> (8 * i)) & 0xffu;
+    float mag = __uint_as_float((c & 0x7fu) << 20) * two120;
+    v[i] = __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+  }
+  lo = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+  hi = (__float_as_uint(v[2]) >> 16) | (__float_as_uint(v[3]) & 0xffff0000u);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl(T v, int src) {
+  return __shfl(v, src, kWave);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Butterfly sum: the same association on every call, so results are reproducible.
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Logical workgroup -> XCD-contiguous order.  Workgroups are dispatched round-robin over
+// the 8 XCDs (workgroup b runs on XCD b % 8), so map workgroup b to a slot such that each
+// XCD walks a contiguous range of logical tiles and its L2 sees their shared operands.
+constexpr int kNumXcd = 8;
+
+}  // namespace moe

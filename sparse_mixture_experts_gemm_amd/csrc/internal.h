@@ -1,0 +1,62 @@
+// Host-side declarations shared between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Routing parameters passed by value to the route / select kernels.
+struct RouteParams {
+  int T, d, E, k, G, Gk, n_g;
+  int score_fn;       // moe_score_fn
+  int renormalize;
+  float route_scale;
+};
+
+// Segments of a grouped GEMM.  Routed: segment e = rows [offsets[e], offsets[e+1]).
+// Shared: one segment of `rows` rows.
+struct GemmParams {
+  const void* a;            // activations (bf16 or fp32), row length K_a
+  const int32_t* row_index; // gather map for A rows (row space -> a row), or null
+  const int32_t* offsets;   // [nseg+1] device, or null for a single segment of `rows` rows
+  int nseg;
+  int rows;                 // rows of the row space (bounds)
+  int d, I, S;              // model dim, expert inter dim, shared count
+  int N;                    // output columns (UP: I_eff; DOWN: d)
+  int K;                    // contraction length (UP: d; DOWN: I_eff)
+  int kblock;               // K is split in blocks of kblock with separate weight slabs
+  // weights for this call (already offset for routed/shared)
+  const void* w_gate;       // UP: [nseg][N][K] (shared: [S*I][d] contiguous)
+  const void* w_up;         // UP SwiGLU
+  const void* w_down;       // DOWN: routed [nseg][d][I]; shared [S][d][I]
+  const float* s_gate;      // e4m3 scales
+  const float* s_up;
+  const float* s_down;
+  const float* row_weight;  // DOWN: per-row multiplier or null
+  void* out;                // [rows][N]
+};
+
+enum class Stage { Up = 0, Down = 1 };
+
+hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, const void* router,
+                        const float* bias, float* scores, int32_t* idx, float* w,
+                        hipStream_t s);
+hipError_t launch_select(const RouteParams& p, const float* scores, int32_t* idx, float* w,
+                         hipStream_t s);
+
+size_t permute_ws_bytes(int T, int E);
+hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* topk_w,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                          int32_t* slot_pos, float* perm_weight, void* ws, hipStream_t s);
+
+hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
+                               int weight_dtype, int num_cus, hipStream_t s);
+
+hipError_t launch_combine(int T, int d, int k, int act_dtype, const void* y_perm,
+                          const int32_t* slot_pos, const void* y_shared, void* out,
+                          hipStream_t s);
+
+}  // namespace moe

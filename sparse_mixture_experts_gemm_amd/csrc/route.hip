@@ -1,0 +1,204 @@
+// Router GEMM, gate scoring and group-limited top-k.
+//
+// The router is the bias-free linear map g(x) = W_g x followed by a deterministic top-k
+// ("大模型工程（一）：Transformer 到 MoE", section "MoE 数学：路由、容量与平衡详解"), with
+// sigmoid gating and group-limited routing as in the FusionLLM MoE ("FusionLLM：融合 MLA、
+// GDN 与 MoE 的高效混合架构大模型训练框架", section "混合专家（MoE）").
+//
+// Layout on the chip: one workgroup owns 16 tokens.  Its four waves split the dim
+// (K) of the 16 x E logit block between them and run bf16 MFMA 16x16x32 on operands read
+// straight from global memory (x rows are read once; the E x d router weight is shared
+// by every workgroup and stays in L2).  The partial logits are summed through LDS in a
+// fixed order, then each wave scores and selects for four tokens with lane = expert:
+// group scores by shuffles inside a group, group rank by comparing against every group,
+// and k rounds of a 64-bit wave max over (score bits, inverted expert index), which
+// picks the higher score and, on equal scores, the lower expert index.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRouteTok = 16;   // tokens per workgroup (bf16 path)
+
+// Score of one expert lane, then selection for token t.  `valid` marks lanes < E.
+__device__ __forceinline__ void score_select_write(float logit, bool valid, int lane,
+                                                   const RouteParams& p, int t, float* scores,
+                                                   int32_t* idx, float* wout,
+                                                   bool from_logit) {
+  float s = logit;
+  if (from_logit) {
+    if (p.score_fn == MOE_SCORE_SIGMOID) {
+      s = 1.0f / (1.0f + expf(-logit));
+    } else {
+      float mx = wave_max_f(valid ? logit : -INFINITY);
+      float e = valid ? expf(logit - mx) : 0.0f;
+      float sum = wave_sum_f(e);
+      s = e / sum;
+    }
+    if (scores != nullptr && valid) scores[(size_t)t * p.E + lane] = s;
+  }
+
+  bool elig = valid;
+  if (p.G > 1 && p.Gk < p.G) {
+    const int gsz = p.E / p.G;
+    const int g = min(lane / gsz, p.G - 1);
+    float b1 = -1.0f, b2 = -1.0f;  // scores are >= 0
+    for (int i = 0; i < gsz; ++i) {
+      float v = wave_shfl(s, g * gsz + i);
+      if (v > b1) {
+        b2 = b1;
+        b1 = v;
+      } else if (v > b2) {
+        b2 = v;
+      }
+    }
+    const float gs = (p.n_g == 2) ? (b1 + b2) : b1;
+    int rank = 0;
+    for (int h = 0; h < p.G; ++h) {
+      float o = wave_shfl(gs, h * gsz);
+      rank += (o > gs) || (o == gs && h < g);
+    }
+    elig = valid && rank < p.Gk;
+  }
+
+  uint64_t key = elig ? ((uint64_t)__float_as_uint(s) << 32) |
+                            (uint64_t)(0xffffffffu - (uint32_t)lane)
+                      : 0ull;
+  float sel = 0.0f;
+  int sel_e = 0;
+  for (int j = 0; j < p.k; ++j) {
+    const uint64_t m = wave_max_u64(key);
+    const int win = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
+    if (lane == win) key = 0ull;
+    if (lane == j) {
+      sel = __uint_as_float((uint32_t)(m >> 32));
+      sel_e = win;
+    }
+  }
+  float sum = 0.0f;
+  for (int j = 0; j < p.k; ++j) sum += wave_shfl(sel, j);
+  if (lane < p.k) {
+    const float wj = (p.renormalize ? sel / sum : sel) * p.route_scale;
+    idx[(size_t)t * p.k + lane] = sel_e;
+    wout[(size_t)t * p.k + lane] = wj;
+  }
+}
+
+// bf16 router: 16 tokens per workgroup, 4 waves split K in 32-wide MFMA steps.
+__global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p,
+                                                         const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wr,
+                                                         const float* __restrict__ bias,
+                                                         float* scores, int32_t* idx,
+                                                         float* wout) {
+  __shared__ float part[4][kRouteTok][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouteTok;
+  const int m = lane & 15;        // token row within the block / expert column in a tile
+  const int g = lane >> 4;        // 8-element K group
+  const int ntiles = (p.E + 15) >> 4;
+  const bool row_ok = (t0 + m) < p.T;
+  const uint16_t* xrow = x + (size_t)(row_ok ? t0 + m : 0) * p.d;
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = p.d >> 5;   // 32 K elements per MFMA
+  for (int st = wave; st < nsteps; st += 4) {
+    const int kk = st * 32 + g * 8;
+    uint4 av = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+    bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (n < ntiles) {
+        const int e = n * 16 + m;
+        uint4 bv = e < p.E ? *reinterpret_cast<const uint4*>(wr + (size_t)e * p.d + kk)
+                           : make_uint4(0, 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv),
+                                                         acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // 16x16 MFMA result: lane holds rows 4*(lane/16)+i of column lane%16.
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][4 * g + i][n * 16 + m] = acc[n][i];
+  }
+  __syncthreads();
+  for (int r = 0; r < 4; ++r) {
+    const int row = wave * 4 + r;
+    const int t = t0 + row;
+    if (t >= p.T) break;  // uniform per wave
+    const bool valid = lane < p.E;
+    float l = 0.0f;
+    if (valid) {
+      l = ((part[0][row][lane] + part[1][row][lane]) + part[2][row][lane]) + part[3][row][lane];
+      if (bias != nullptr) l += bias[lane];
+    }
+    score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
+  }
+}
+
+// fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.
+__global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p, const float* __restrict__ x,
+                                                        const float* __restrict__ wr,
+                                                        const float* __restrict__ bias,
+                                                        float* scores, int32_t* idx,
+                                                        float* wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;  // whole wave
+  const bool valid = lane < p.E;
+  const float* xr = x + (size_t)t * p.d;
+  const float* wrow = wr + (size_t)(valid ? lane : 0) * p.d;
+  float l = 0.0f;
+  if (valid) {
+    for (int c = 0; c < p.d; ++c) l = fmaf(xr[c], wrow[c], l);
+    if (bias != nullptr) l += bias[lane];
+  }
+  score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
+}
+
+__global__ __launch_bounds__(256) void select_kernel(RouteParams p, const float* __restrict__ scores,
+                                                     int32_t* idx, float* wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  const bool valid = lane < p.E;
+  const float s = valid ? scores[(size_t)t * p.E + lane] : 0.0f;
+  score_select_write(s, valid, lane, p, t, nullptr, idx, wout, false);
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, const void* router,
+                        const float* bias, float* scores, int32_t* idx, float* w,
+                        hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  if (act_dtype == MOE_BF16) {
+    dim3 grid((p.T + kRouteTok - 1) / kRouteTok);
+    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(256), 0, s, p,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router),
+                       bias, scores, idx, w);
+  } else {
+    dim3 grid((p.T + 3) / 4);
+    hipLaunchKernelGGL(route_f32_kernel, grid, dim3(256), 0, s, p, static_cast<const float*>(x),
+                       static_cast<const float*>(router), bias, scores, idx, w);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const RouteParams& p, const float* scores, int32_t* idx, float* w,
+                         hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + 3) / 4);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, p, scores, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,140 @@
+"""Host-side checks of the libmoe C ABI (no GPU): the library loads, exports every entry
+point include/moe.h declares, and rejects bad arguments before anything is enqueued.
+The invalid-argument calls below return during host validation, before any HIP call,
+so they are safe without a device (pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mixture_experts_gemm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.library_path()):
+        from sparse_mixture_experts_gemm_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ["moe_route", "moe_select", "moe_permute", "moe_grouped_gemm", "moe_combine",
+                 "moe_forward", "moe_workspace_size", "moe_status_string", "moe_last_hip_error"]:
+        assert name in fns
+    assert sorted(moe.EXPORTED_SYMBOLS) == fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    assert moe.status_string(0) == "ok"
+    assert "workspace" in moe.status_string(3)
+    assert moe.status_string(99) == "unknown status"
+    assert lib.moe_last_hip_error() == 0
+
+
+def cfg(**kw):
+    base = dict(T=4096, d=2048, E=64, k=6, G=8, Gk=4, n_g=1, S=4, I=1536)
+    base.update(kw)
+    T, d, E, k, I = base.pop("T"), base.pop("d"), base.pop("E"), base.pop("k"), base.pop("I")
+    return moe.make_config(T, d, E, k, I=I, **base)
+
+
+def test_workspace_size_is_the_sum_of_the_stages(lib):
+    n = moe.workspace_size(cfg())
+    T, k, d, I, S = 4096, 6, 2048, 1536, 4
+    inter = T * k * I * 2 + T * S * I * 2 + T * k * d * 2 + T * d * 2
+    assert inter <= n <= inter + 8 * 1024 * 1024
+    assert moe.workspace_size(cfg(T=0)) < 64 * 1024
+    assert moe.workspace_size(cfg(T=64)) < moe.workspace_size(cfg(T=128))
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(k=0), 1), (dict(k=65, E=64), 1), (dict(E=60, G=8), 1), (dict(Gk=9), 1),
+    (dict(k=17, Gk=2), 1), (dict(n_g=3), 1), (dict(E=64, G=64, Gk=6, n_g=2), 1),
+    (dict(T=-1), 1), (dict(d=0), 1), (dict(E=128, G=8, k=6), 2), (dict(d=2000), 2),
+    (dict(I=1000), 2), (dict(act_dtype="f32", weight_dtype="bf16"), 2),
+    (dict(act_dtype="bf16", weight_dtype="f32"), 2),
+])
+def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
+    c = cfg(**bad)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == status
+    fake = 4096   # never dereferenced: validation fails first
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, None) == status
+    assert lib.moe_select(ctypes.byref(c), fake, fake, fake, None) == status
+    with pytest.raises(moe.MoeError):
+        moe.workspace_size(c)
+
+
+def test_null_and_workspace_errors_are_reported_before_launch(lib):
+    c = cfg(T=64)
+    fake = 4096
+    w = moe.Weights(router=fake, w_gate=fake, w_up=fake, w_down=fake, sh_gate=fake, sh_up=fake,
+                    sh_down=fake)
+    need = moe.workspace_size(c)
+    # workspace too small
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), fake, fake, fake, need - 1, None) == 3
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), fake, fake, None, need, None) == 3
+    # null x / out / weights
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), None, fake, fake, need, None) == 1
+    assert lib.moe_forward(ctypes.byref(c), None, fake, fake, fake, need, None) == 1
+    w_missing = moe.Weights(router=fake, w_gate=fake, w_down=fake, sh_gate=fake, sh_up=fake,
+                            sh_down=fake)
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w_missing.c), fake, fake, fake, need,
+                           None) == 1
+    # misaligned pointer
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), fake + 2, fake, fake, need, None) == 2
+    # permute: workspace and optional weight pair
+    assert lib.moe_permute(ctypes.byref(c), fake, None, fake, fake, fake, fake, None, None, 0, None) == 3
+    assert lib.moe_permute(ctypes.byref(c), fake, fake, fake, fake, fake, fake, None, fake, 1 << 20,
+                           None) == 1
+    # grouped gemm: routed set needs offsets; shared set needs S > 0; bad stage
+    assert lib.moe_grouped_gemm(ctypes.byref(c), 0, 0, fake, None, None, 10, ctypes.byref(w.c), None,
+                                fake, None, 0, None) == 1
+    c0 = cfg(T=64, S=0)
+    assert lib.moe_grouped_gemm(ctypes.byref(c0), 0, 1, fake, None, None, 10, ctypes.byref(w.c), None,
+                                fake, None, 0, None) == 1
+    assert lib.moe_grouped_gemm(ctypes.byref(c), 7, 0, fake, None, fake, 10, ctypes.byref(w.c), None,
+                                fake, None, 0, None) == 1
+    # combine: null y
+    assert lib.moe_combine(ctypes.byref(c), None, fake, None, fake, None) == 1
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    c = cfg(T=0)
+    fake = 4096
+    w = moe.Weights(router=fake, w_gate=fake, w_up=fake, w_down=fake, sh_gate=fake, sh_up=fake,
+                    sh_down=fake)
+    assert lib.moe_route(ctypes.byref(c), None, None, None, None, None, None, None) == 0
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), None, None, None, 0, None) == 0
+    assert lib.moe_combine(ctypes.byref(c), None, None, None, None, None) == 0
+    assert lib.moe_grouped_gemm(ctypes.byref(c), 0, 0, None, None, None, 0, ctypes.byref(w.c), None,
+                                None, None, 0, None) == 0
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_LIB", None)
+    monkeypatch.setattr(moe, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(moe.LibraryMissing):
+        moe.workspace_size(cfg())

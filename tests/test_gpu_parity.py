@@ -1,0 +1,410 @@
+"""GPU parity of every libmoe entry point against the fp64 CPU oracle.
+
+All inputs come from the seeded generator (workloads) or from the oracle; nothing the GPU
+computes is fed to the oracle.  Bars:
+* selection (moe_select on shared fp32 scores) and permutation: bit-exact;
+* routing by moe_route: GPU scores within 1e-5 of the oracle's fp64 scores; indices
+  identical for every token whose fp64 decision margins exceed 1e-5 (a smaller margin is
+  below the fp32 score error, so either choice is correct: those tokens are checked for
+  validity instead and kept out of output comparisons when their selection differs);
+* float outputs: max|delta| <= 2e-2 max|ref| (bf16) and <= 1e-4 max|ref| (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_gemm_amd as moe
+import workloads as W
+from _dev import act_empty, act_to_f64, config, to_dev, weights, workspace
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+MARGIN = 1e-5
+
+SMALL = {
+    # ragged everything: T not a multiple of the tiles, I and d give partial n-tiles
+    "small_swiglu": W.small_shape(T=300, d=320, E=16, k=4, G=4, Gk=2, S=2, I=192, seed=31),
+    "small_relu2_e4m3": W.small_shape(T=200, d=256, E=8, k=2, G=2, Gk=1, n_g=2, S=2, I=320,
+                                      act="relu2", weight_dtype="e4m3", seed=32),
+    "small_swiglu_e4m3": W.small_shape(T=150, d=192, E=16, k=3, G=1, Gk=1, S=1, I=128,
+                                       weight_dtype="e4m3", seed=33),
+    "small_f32": W.small_shape(T=77, d=48, E=8, k=3, score="softmax", G=1, Gk=1, S=1, I=32,
+                               act_dtype="f32", weight_dtype="f32", seed=34),
+    "single_token": W.small_shape(T=1, d=128, E=64, k=6, G=8, Gk=4, S=1, I=64, seed=35),
+    "topk1_nogroups": W.small_shape(T=130, d=128, E=32, k=1, G=1, Gk=1, S=0, I=64, seed=36,
+                                    renormalize=False, route_scale=2.5),
+}
+
+
+def shape_of(name):
+    return SMALL[name] if name in SMALL else W.SHAPES[name]
+
+
+def layer_of(name):
+    s = shape_of(name)
+    return W.make_layer(s, cache=name in W.SHAPES)
+
+
+def fp32_scores(lay, tokens=None):
+    r = O.route(lay, tokens)
+    return r
+
+
+def margins(scores64, s):
+    """Smallest fp64 decision margin per token (group boundary and top-k order)."""
+    T, E = scores64.shape
+    m = np.full(T, np.inf)
+    if s.G > 1 and s.Gk < s.G:
+        gs = O.group_scores(scores64, s.G, s.n_g)
+        gsrt = -np.sort(-gs, axis=1)
+        m = np.minimum(m, gsrt[:, s.Gk - 1] - gsrt[:, s.Gk])
+        gorder = np.lexsort((np.broadcast_to(np.arange(s.G), gs.shape), -gs), axis=-1)
+        kept = np.zeros_like(gs, dtype=bool)
+        np.put_along_axis(kept, gorder[:, :s.Gk], True, axis=-1)
+        elig = np.repeat(kept, E // s.G, axis=1)
+    else:
+        elig = np.ones((T, E), bool)
+    se = np.where(elig, scores64, -1.0)
+    srt = -np.sort(-se, axis=1)
+    upto = min(s.k + 1, E)
+    gaps = srt[:, :upto - 1] - srt[:, 1:upto]
+    m = np.minimum(m, gaps.min(axis=1))
+    return m
+
+
+def valid_within_margin(row, sc, s, eps=2 * MARGIN):
+    """Is ``row`` a correct group-limited top-k of the fp64 scores ``sc`` once every score
+    may move by eps?  (Checked directly from the definition, without the oracle.)"""
+    row = np.asarray(row)
+    if len(set(row.tolist())) != s.k or row.min() < 0 or row.max() >= s.E:
+        return False
+    gsz = s.E // s.G
+    limited = s.G > 1 and s.Gk < s.G
+    if limited:
+        gs = np.array([np.sort(sc[g * gsz:(g + 1) * gsz])[::-1][:s.n_g].sum() for g in range(s.G)])
+        cut = np.sort(gs)[::-1][s.Gk - 1]
+        used = set((row // gsz).tolist())
+        if len(used) > s.Gk or any(gs[g] < cut - s.n_g * eps for g in used):
+            return False
+        # groups certainly kept (clearly above the Gk-th) plus the used ones are eligible
+        sure = {g for g in range(s.G) if gs[g] > np.sort(gs)[::-1][s.Gk] + s.n_g * eps}
+        elig = np.array([(e // gsz) in (used | sure) for e in range(s.E)])
+    else:
+        elig = np.ones(s.E, bool)
+    low = sc[row].min()
+    others = np.array([e for e in range(s.E) if elig[e] and e not in set(row.tolist())], dtype=int)
+    return others.size == 0 or sc[others].max() <= low + eps
+
+
+def sample_tokens(T, n=128, seed=0):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(32, T - 32), size=n - 64, replace=False)
+    return np.unique(np.concatenate([np.arange(32), mid, np.arange(T - 32, T)]))
+
+
+# ----------------------------------------------------------------------------- select
+SELECT_CASES = ["tiny_fp32", "fusionllm_bf16", "skewed_bf16", "fp8_relu2", "small_swiglu",
+                "small_relu2_e4m3", "topk1_nogroups"]
+
+
+@pytest.mark.parametrize("name", SELECT_CASES)
+def test_select_bit_exact_on_oracle_scores(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    T = min(s.T, 8192)
+    r = O.route(lay, np.arange(T))
+    sc32 = r["scores"].astype(np.float32)
+    cfg = config(s, T=T)
+    idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
+    moe.select(cfg, to_dev(sc32), idx, w)
+    torch.cuda.synchronize()
+    ref_idx = O.select_experts(sc32, s.k, s.G, s.Gk, s.n_g)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    ref_w = O.routing_weights(sc32.astype(np.float64), ref_idx, s.renormalize, s.route_scale)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+def adversarial_scores(T, E, seed):
+    rng = np.random.default_rng(seed)
+    a = (rng.integers(0, 8, size=(T, E)) / 8.0).astype(np.float32)      # heavy ties
+    a[0] = 0.5                                                         # all equal
+    a[1] = 0.0                                                         # all zero
+    a[2] = np.arange(E, dtype=np.float32) / E                          # ascending
+    a[3] = np.arange(E, dtype=np.float32)[::-1] / E                    # descending
+    a[4, ::2] = 0.75                                                   # ties across groups
+    a[5] = 0.25
+    a[5, -1] = 1.0                                                     # winner in last group
+    return a
+
+
+@pytest.mark.parametrize("E,k,G,Gk,n_g", [(64, 6, 8, 4, 1), (64, 6, 8, 4, 2), (64, 8, 1, 1, 1),
+                                          (16, 4, 4, 1, 2), (8, 8, 1, 1, 1), (64, 1, 64, 3, 1),
+                                          (12, 5, 3, 2, 2)])
+def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
+    T = 1000
+    sc = adversarial_scores(T, E, seed=E * 100 + k * 10 + G + n_g)
+    cfg = moe.make_config(T, 64, E, k, G=G, Gk=Gk, n_g=n_g, I=64)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.select(cfg, to_dev(sc), idx, w)
+    torch.cuda.synchronize()
+    ref = O.select_experts(sc, k, G, Gk, n_g)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    sel = np.take_along_axis(sc.astype(np.float64), ref.astype(np.int64), axis=1)
+    tot = sel.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ref_w = sel / tot
+    ok = tot[:, 0] > 0
+    assert np.allclose(w.cpu().numpy()[ok], ref_w[ok], rtol=2e-6, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- route
+ROUTE_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
+               "small_swiglu", "small_f32", "single_token", "topk1_nogroups"]
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_matches_oracle(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    cfg = config(s)
+    T = s.T
+    scores = torch.empty((T, s.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
+    moe.route(cfg, to_dev(lay.x), to_dev(lay.router), to_dev(lay.logit_bias), scores, idx, w)
+    torch.cuda.synchronize()
+    r = O.route(lay)
+    g_sc = scores.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g_sc - r["scores"])) <= 1e-5
+    g_idx = idx.cpu().numpy()
+    mar = margins(r["scores"], s)
+    clear = mar > MARGIN
+    assert np.array_equal(g_idx[clear], r["idx"][clear])
+    # near-tie tokens: the GPU's pick must still be a valid top-k within the margin
+    for t in np.nonzero(~clear)[0]:
+        assert valid_within_margin(g_idx[t], r["scores"][t], s), (t, g_idx[t], r["idx"][t])
+    assert (~clear).sum() <= max(4, T // 200)
+    same = (g_idx == r["idx"]).all(axis=1)
+    assert np.allclose(w.cpu().numpy()[same], r["w"][same], rtol=1e-5, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- permute
+def _check_permute(T, E, k, idx_np, topk_w_np):
+    cfg = moe.make_config(T, 64, E, k, I=64)
+    ws = workspace(cfg)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pt = torch.empty(max(T * k, 1), dtype=torch.int32, device="cuda")
+    sp = torch.empty(max(T * k, 1), dtype=torch.int32, device="cuda")
+    pw = torch.empty(max(T * k, 1), dtype=torch.float32, device="cuda")
+    moe.permute(cfg, to_dev(idx_np), to_dev(topk_w_np), counts, offsets, pt, sp, pw, ws)
+    torch.cuda.synchronize()
+    rc, ro, rpt, rsp = O.permute(idx_np, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(pt.cpu().numpy()[:T * k], rpt)
+    assert np.array_equal(sp.cpu().numpy()[:T * k], rsp)
+    ref_pw = np.empty(T * k, np.float32)
+    ref_pw[rsp] = topk_w_np.reshape(-1)
+    assert np.array_equal(pw.cpu().numpy()[:T * k], ref_pw)
+
+
+@pytest.mark.parametrize("name", ["fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
+                                  "tiny_fp32", "small_swiglu", "single_token"])
+def test_permute_bit_exact_on_oracle_routing(name):
+    s = shape_of(name)
+    r = O.route(layer_of(name))
+    _check_permute(s.T, s.E, s.k, r["idx"], r["w"].astype(np.float32))
+
+
+@pytest.mark.parametrize("T,E,k,pattern", [(1, 64, 6, "random"), (63, 64, 6, "random"),
+                                           (257, 8, 8, "random"), (1000, 64, 1, "one_expert"),
+                                           (700, 64, 6, "first_six"), (5000, 16, 3, "random")])
+def test_permute_edge_cases(T, E, k, pattern):
+    rng = np.random.default_rng(T + E + k)
+    if pattern == "random":
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    elif pattern == "one_expert":
+        idx = np.full((T, k), 5, np.int32)
+    else:
+        idx = np.tile(np.arange(k, dtype=np.int32)[::-1], (T, 1))
+    w = rng.random((T, k)).astype(np.float32)
+    _check_permute(T, E, k, idx, w)
+
+
+# ----------------------------------------------------------------------------- grouped GEMMs
+def _dense(lay, which, e, shared=False):
+    s = lay.shape
+    w1, w3, w2 = (O.shared_weights(lay, e) if shared else O.expert_weights(lay, e))
+    return {"up": (w1, w3), "down": w2}[which]
+
+
+GEMM_CASES = ["small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32", "tiny_fp32",
+              "single_token", "fusionllm_bf16", "fp8_relu2"]
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_grouped_gemm_up_routed(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    r = O.route(lay)
+    counts, offsets, perm_token, _ = O.permute(r["idx"], s.E)
+    Tk = s.T * s.k
+    cfg = config(s)
+    wts = weights(lay)
+    h = act_empty((Tk, s.I), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, to_dev(lay.x),
+                     to_dev(perm_token), to_dev(offsets), Tk, wts, None, h)
+    torch.cuda.synchronize()
+    got = act_to_f64(h, s.act_dtype)
+    x64 = r["x"]
+    rows = sample_tokens(Tk, n=512, seed=1)
+    ref = np.zeros((len(rows), s.I))
+    for e in range(s.E):
+        sel = np.nonzero((rows >= offsets[e]) & (rows < offsets[e + 1]))[0]
+        if sel.size:
+            w1, w3 = _dense(lay, "up", e)
+            ref[sel] = O.expert_up(x64[perm_token[rows[sel]]], w1, w3, s.act)
+    err = np.max(np.abs(got[rows] - ref))
+    assert err <= TOL[s.act_dtype] * np.max(np.abs(ref)), err
+
+
+@pytest.mark.parametrize("name", GEMM_CASES)
+def test_grouped_gemm_down_routed(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    r = O.route(lay)
+    counts, offsets, perm_token, slot_pos = O.permute(r["idx"], s.E)
+    Tk = s.T * s.k
+    pw = np.empty(Tk, np.float32)
+    pw[slot_pos] = r["w"].astype(np.float32).reshape(-1)
+    h_in = W.random_act((Tk, s.I), seed=77, dtype=s.act_dtype, std=0.5)
+    cfg = config(s)
+    wts = weights(lay)
+    y = act_empty((Tk, s.d), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, to_dev(h_in), None,
+                     to_dev(offsets), Tk, wts, to_dev(pw), y)
+    torch.cuda.synchronize()
+    got = act_to_f64(y, s.act_dtype)
+    h64 = O.decode_act(h_in, s.act_dtype)
+    rows = sample_tokens(Tk, n=512, seed=2)
+    ref = np.zeros((len(rows), s.d))
+    for e in range(s.E):
+        sel = np.nonzero((rows >= offsets[e]) & (rows < offsets[e + 1]))[0]
+        if sel.size:
+            ref[sel] = pw[rows[sel]].astype(np.float64)[:, None] * O.expert_down(h64[rows[sel]], _dense(lay, "down", e))
+    err = np.max(np.abs(got[rows] - ref))
+    assert err <= TOL[s.act_dtype] * np.max(np.abs(ref)), err
+
+
+@pytest.mark.parametrize("name", ["small_swiglu", "small_relu2_e4m3", "small_f32", "fusionllm_bf16",
+                                  "fp8_relu2"])
+def test_grouped_gemm_shared(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    cfg = config(s)
+    wts = weights(lay)
+    T = s.T
+    SI = s.S * s.I
+    h = act_empty((T, SI), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_SHARED, to_dev(lay.x), None, None, T,
+                     wts, None, h)
+    h_in = W.random_act((T, SI), seed=78, dtype=s.act_dtype, std=0.5)
+    y = act_empty((T, s.d), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_SHARED, to_dev(h_in), None, None, T,
+                     wts, None, y)
+    torch.cuda.synchronize()
+    rows = sample_tokens(T, n=256, seed=3)
+    x64 = O.decode_act(lay.x[rows], s.act_dtype)
+    h64 = O.decode_act(h_in[rows], s.act_dtype)
+    ref_h = np.concatenate([O.expert_up(x64, *_dense(lay, "up", i, True), s.act) for i in range(s.S)], axis=1)
+    ref_y = sum(O.expert_down(h64[:, i * s.I:(i + 1) * s.I], _dense(lay, "down", i, True)) for i in range(s.S))
+    got_h = act_to_f64(h, s.act_dtype)[rows]
+    got_y = act_to_f64(y, s.act_dtype)[rows]
+    assert np.max(np.abs(got_h - ref_h)) <= TOL[s.act_dtype] * np.max(np.abs(ref_h))
+    assert np.max(np.abs(got_y - ref_y)) <= TOL[s.act_dtype] * np.max(np.abs(ref_y))
+
+
+# ----------------------------------------------------------------------------- combine
+@pytest.mark.parametrize("name,with_shared", [("small_swiglu", True), ("small_f32", True),
+                                              ("fusionllm_bf16", True), ("topk1_nogroups", False)])
+def test_combine(name, with_shared):
+    s = shape_of(name)
+    r = O.route(layer_of(name))
+    _, _, _, slot_pos = O.permute(r["idx"], s.E)
+    y = W.random_act((s.T * s.k, s.d), seed=79, dtype=s.act_dtype)
+    ysh = W.random_act((s.T, s.d), seed=80, dtype=s.act_dtype) if with_shared else None
+    out = act_empty((s.T, s.d), s.act_dtype)
+    moe.combine(config(s), to_dev(y), to_dev(slot_pos), to_dev(ysh), out)
+    torch.cuda.synchronize()
+    ref = O.combine(O.decode_act(y, s.act_dtype), slot_pos,
+                    None if ysh is None else O.decode_act(ysh, s.act_dtype), s.k)
+    got = act_to_f64(out, s.act_dtype)
+    # fp32 sum of k+1 terms, then one rounding to the output dtype
+    rel = 2.0 ** -8 if s.act_dtype == "bf16" else 1e-6
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
+
+
+# ----------------------------------------------------------------------------- forward
+FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
+                 "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
+                 "single_token", "topk1_nogroups"]
+
+
+def run_forward(name):
+    s = shape_of(name)
+    lay = layer_of(name)
+    cfg = config(s)
+    wts = weights(lay)
+    ws = workspace(cfg)
+    x = to_dev(lay.x)
+    out = act_empty((s.T, s.d), s.act_dtype)
+    moe.forward(cfg, wts, x, out, ws)
+    torch.cuda.synchronize()
+    gpu_idx = ws[: s.T * s.k * 4].view(torch.int32).cpu().numpy().reshape(s.T, s.k)
+    return s, lay, cfg, wts, ws, x, out, gpu_idx
+
+
+@pytest.mark.parametrize("name", FORWARD_CASES)
+def test_forward_matches_oracle(name):
+    s, lay, cfg, wts, ws, x, out, gpu_idx = run_forward(name)
+    rows = sample_tokens(s.T, n=128, seed=4)
+    ref = O.moe_forward(lay, tokens=rows)
+    same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
+    mar = margins(ref["scores"], s)
+    assert np.all(same | (mar <= MARGIN)), "routing differs away from a near tie"
+    got = act_to_f64(out, s.act_dtype)[rows]
+    diff = np.max(np.abs(got[same] - ref["out"][same]))
+    scale = np.max(np.abs(ref["out"][same]))
+    print(f"{name}: max|d|/max|ref| = {diff / scale:.3e} over {same.sum()} rows")
+    assert diff <= TOL[s.act_dtype] * scale
+
+
+@pytest.mark.parametrize("name", ["fusionllm_bf16", "small_swiglu_e4m3", "tiny_fp32"])
+def test_forward_is_deterministic(name):
+    s, lay, cfg, wts, ws, x, out, _ = run_forward(name)
+    out2 = torch.empty_like(out)
+    moe.forward(cfg, wts, x, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_forward_error_paths_enqueue_nothing():
+    s = shape_of("small_swiglu")
+    lay = layer_of("small_swiglu")
+    cfg = config(s)
+    wts = weights(lay)
+    ws = workspace(cfg)
+    out = act_empty((s.T, s.d), s.act_dtype)
+    out.fill_(7)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.forward(cfg, wts, to_dev(lay.x), out, ws, ws_bytes=ws.numel() - 1)
+    assert ei.value.status == 3
+    torch.cuda.synchronize()
+    assert bool((out == 7).all())

@@ -281,3 +281,12 @@ def small_shape(**kw) -> MoeShape:
 
 def clear_cache():
     _CACHE.clear()
+
+
+def random_act(shape, seed: int, dtype: str = "bf16", std: float = 1.0) -> np.ndarray:
+    """Seeded N(0, std^2) tensor stored in an activation encoding (bf16 bits or fp32)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    a = g.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return encode_bf16(a) if dtype == "bf16" else a
