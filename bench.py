@@ -7,8 +7,8 @@ shared experts -> combine) over one batch of seeded synthetic tokens, with input
 weights resident in HBM.  Prints ONE JSON line.  The headline workload is the
 FusionLLM-shape layer (T=4096, dim 2048, 64 routed + 4 shared experts, top-6, bf16);
 the decode-shaped layer (T=64, same weights) is reported alongside with its HBM rate.
-Per-stage times come from HIP events recorded between the stage launches on the stream
-they run on; the step calls the same C-ABI entry points moe_forward chains.
+Per-stage times come from HIP events that moe_forward_ex records between its launches on
+the stream they run on.
 """
 from __future__ import annotations
 
@@ -26,8 +26,6 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-
-STAGES = ["route", "permute", "up_routed", "up_shared", "down_routed", "down_shared", "combine"]
 
 
 def stage_flops(s, T):
@@ -62,7 +60,8 @@ def to_dev(a):
 
 
 class Runner:
-    """Device-resident layer and the per-stage C-ABI calls of one forward."""
+    """Device-resident layer; one step = moe_forward_ex with HIP events at its stage
+    boundaries, all recorded on the stream the kernels run on."""
 
     def __init__(self, shape, lay, weights=None):
         import torch
@@ -80,87 +79,60 @@ class Runner:
             weights = moe.Weights(**t)
         self.w = weights
         self.x = to_dev(lay.x)
-        dev = "cuda"
-        T, k, E, d, I, S = s.T, s.k, s.E, s.d, s.I, s.S
         adt = torch.int16 if s.act_dtype == "bf16" else torch.float32
-        i32, f32 = torch.int32, torch.float32
-        self.idx = torch.empty(T * k, dtype=i32, device=dev)
-        self.tw = torch.empty(T * k, dtype=f32, device=dev)
-        self.counts = torch.empty(E, dtype=i32, device=dev)
-        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
-        self.pt = torch.empty(T * k, dtype=i32, device=dev)
-        self.sp = torch.empty(T * k, dtype=i32, device=dev)
-        self.pw = torch.empty(T * k, dtype=f32, device=dev)
-        self.pws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-        self.h = torch.empty((T * k, I), dtype=adt, device=dev)
-        self.hs = torch.empty((T, max(S, 1) * I), dtype=adt, device=dev)
-        self.y = torch.empty((T * k, d), dtype=adt, device=dev)
-        self.ys = torch.empty((T, d), dtype=adt, device=dev)
-        self.out = torch.empty((T, d), dtype=adt, device=dev)
-        self.ws = torch.empty(moe.workspace_size(self.cfg), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((s.T, s.d), dtype=adt, device="cuda")
+        self.ws = torch.empty(moe.workspace_size(self.cfg), dtype=torch.uint8, device="cuda")
 
-    def stage_calls(self):
-        m, c, s = self.moe, self.cfg, self.s
-        T, Tk = s.T, s.T * s.k
-        calls = [
-            ("route", lambda: m.route(c, self.x, self.w.tensors["router"],
-                                      self.w.tensors["logit_bias"], None, self.idx, self.tw)),
-            ("permute", lambda: m.permute(c, self.idx, self.tw, self.counts, self.offsets, self.pt,
-                                          self.sp, self.pw, self.pws)),
-            ("up_routed", lambda: m.grouped_gemm(c, m.MOE_STAGE_UP, m.MOE_EXPERTS_ROUTED, self.x,
-                                                 self.pt, self.offsets, Tk, self.w, None, self.h)),
-            ("up_shared", lambda: m.grouped_gemm(c, m.MOE_STAGE_UP, m.MOE_EXPERTS_SHARED, self.x,
-                                                 None, None, T, self.w, None, self.hs)),
-            ("down_routed", lambda: m.grouped_gemm(c, m.MOE_STAGE_DOWN, m.MOE_EXPERTS_ROUTED, self.h,
-                                                   None, self.offsets, Tk, self.w, self.pw, self.y)),
-            ("down_shared", lambda: m.grouped_gemm(c, m.MOE_STAGE_DOWN, m.MOE_EXPERTS_SHARED,
-                                                   self.hs, None, None, T, self.w, None, self.ys)),
-            ("combine", lambda: m.combine(c, self.y, self.sp, self.ys if s.S > 0 else None,
-                                          self.out)),
-        ]
-        if s.S == 0:
-            calls = [cl for cl in calls if cl[0] not in ("up_shared", "down_shared")]
-        return calls
-
-    def forward(self):
-        self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+    def counts(self):
+        """Per-expert row counts of the last forward (from its workspace)."""
+        import ctypes
+        s = self.s
+        # the workspace starts with topk_idx [T*k] int32; counts follow topk_w, 256-aligned
+        al = lambda n: (n + 255) // 256 * 256
+        off = al(s.T * s.k * 4) * 2
+        return self.ws[off: off + 4 * s.E].view(self.torch.int32).cpu().numpy()
 
     def timed(self, steps, warmup):
-        """Stage-wise steps with HIP events between the stages on the current stream."""
-        torch = self.torch
-        calls = self.stage_calls()
-        for _ in range(warmup):
-            for _, f in calls:
-                f()
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-              for _ in range(steps)]
-        t0 = time.perf_counter()
-        for i in range(steps):
-            ev[i][0].record()
-            for j, (_, f) in enumerate(calls):
-                f()
-                ev[i][j + 1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per_stage = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
-                     for j, (name, _) in enumerate(calls)}
-        step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]))
-        total_ms = ev[0][0].elapsed_time(ev[-1][-1])
-        return step_ms, total_ms, wall, per_stage
-
-    def timed_forward(self, steps, warmup):
+        """K plain forwards bracketed by one event pair (the headline step time)."""
         torch = self.torch
         for _ in range(warmup):
-            self.forward()
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
         a.record()
         for _ in range(steps):
-            self.forward()
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
+        wall = time.perf_counter() - t0
+        return a.elapsed_time(b) / steps, wall
+
+    def staged(self, steps, warmup, stages=None):
+        """K forwards with events at the given stage boundaries (indices into the eight of
+        moe_forward_opts); returns the mean time between consecutive recorded events.  Every
+        recorded event also adds a few microseconds to the stream, so the step time is taken
+        from ``timed`` and these figures only attribute time to stages."""
+        torch = self.torch
+        stages = list(range(8)) if stages is None else stages
+        names = ["route", "permute", "up_routed", "up_shared", "down_routed", "down_shared", "combine"]
+        for _ in range(warmup):
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+        ev = []
+        for _ in range(steps):
+            e = [None] * 8
+            for i in stages:
+                e[i] = torch.cuda.Event(enable_timing=True)
+            ev.append(e)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws, stage_events=ev[i])
+        torch.cuda.synchronize()
+        out = {}
+        for a, b in zip(stages[:-1], stages[1:]):
+            key = "+".join(names[a:b])
+            out[key] = float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)]))
+        return out
 
 
 def decode_bytes(s, counts):
@@ -206,13 +178,15 @@ def main(argv=None):
     shape = W.SHAPES[args.workload]
     lay = W.make_layer(shape)
     run = Runner(shape, lay)
-    step_ms, total_ms, wall, per_stage = run.timed(args.steps, args.warmup)
-    fwd_ms = run.timed_forward(args.steps, args.warmup)
+    step_ms, wall = run.timed(args.steps, args.warmup)
     T = shape.T
     fl = stage_flops(shape, T)
     total_flops = sum(fl.values())
-    dom = max(per_stage, key=lambda k: per_stage[k])
-    achieved = fl[dom] / (per_stage[dom] * 1e-3) / 1e12
+    stage_ms = run.staged(args.steps, args.warmup)
+    # the dominant kernel (the routed up projection), bracketed by its own two events
+    dom = "up_routed"
+    dom_ms = run.staged(args.steps, args.warmup, stages=[2, 3])[dom]
+    achieved = fl[dom] / (dom_ms * 1e-3) / 1e12
     res = {
         "metric": "MoE fwd tokens/s & % MFMA peak, d2048 E64 k6 T4096; decode T64 % HBM BW",
         "value": T / (step_ms * 1e-3),
@@ -232,25 +206,37 @@ def main(argv=None):
                    "weights": shape.weight_dtype},
         "layer_tflops": total_flops / (step_ms * 1e-3) / 1e12,
         "layer_mfma_frac": total_flops / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "forward_call_ms": fwd_ms,
-        "stage_ms": per_stage,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "stage_ms_with_events": stage_ms,
+        "roofline": {"kernel": "grouped GEMM, routed up projection (SwiGLU epilogue)",
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel_ms": dom_ms, "algorithmic_tflop": fl[dom] / 1e12},
     }
     if not args.no_decode:
         dshape = W.SHAPES["decode_bf16"]
         dlay = W.make_layer(dshape)
         drun = Runner(dshape, dlay, weights=run.w)     # same weights as the prefill layer
-        d_ms, _, _, d_stage = drun.timed(args.steps, args.warmup)
-        d_fwd = drun.timed_forward(args.steps, args.warmup)
-        nbytes, touched = decode_bytes(dshape, drun.counts.cpu().numpy())
+        d_ms, _ = drun.timed(args.steps, args.warmup)
+        d_stage = drun.staged(args.steps, args.warmup)
+        d_up_ms = drun.staged(args.steps, args.warmup, stages=[2, 3])["up_routed"]
+        counts = drun.counts()
+        nbytes, touched = decode_bytes(dshape, counts)
+        # the dominant decode kernel streams the up-projection weights of the touched
+        # routed experts and of the shared experts in one launch
+        up_bytes = (touched + dshape.S) * 2 * dshape.d * dshape.I * 2 + dshape.T * dshape.d * 2
         res["decode"] = {"workload": dshape.name, "tokens": dshape.T, "ms_per_step": d_ms,
-                         "forward_call_ms": d_fwd, "tokens_per_s": dshape.T / (d_ms * 1e-3),
+                         "tokens_per_s": dshape.T / (d_ms * 1e-3),
                          "algorithmic_bytes": nbytes, "experts_touched": touched,
                          "hbm_GBps": nbytes / (d_ms * 1e-3) / 1e9,
                          "hbm_frac": nbytes / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                         "stage_ms": d_stage}
+                         "stage_ms_with_events": d_stage,
+                         "roofline": {"kernel": "decode up projection (routed + shared experts, one launch)",
+                                      "bound": "hbm",
+                                      "achieved": up_bytes / (d_up_ms * 1e-3) / 1e9,
+                                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                      "frac": up_bytes / (d_up_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                      "traffic": None, "kernel_ms": d_up_ms,
+                                      "algorithmic_bytes": up_bytes}}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(lay, args.cpu_tokens)
     print(json.dumps(res))

@@ -24,7 +24,8 @@
  *     MOE_F32 activations; MOE_BF16 or MOE_FP8_E4M3 with MOE_BF16 activations).
  *   - Limits: 1 <= E <= 64, 1 <= k <= E, E % G == 0, 1 <= Gk <= G, k <= Gk*E/G,
  *     n_g in {1, 2} and n_g <= E/G; dim and inter_dim multiples of 64 (bf16/e4m3) or
- *     of 4 (fp32); num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned.
+ *     of 16 (fp32); num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned; sizes whose
+ *     element offsets exceed 2^31 - 1 are MOE_ERR_UNSUPPORTED.
  *     Violations return MOE_ERR_INVALID_ARG (bad values) or MOE_ERR_UNSUPPORTED
  *     (valid but not implemented).
  *   - Calls are re-entrant; calls that share output or workspace buffers on the same
@@ -126,7 +127,9 @@ moe_status moe_select(const moe_config* cfg, const float* scores, int32_t* topk_
  *   slot_pos[t*k+j] permuted row of slot j of token t                    [T*k]
  *   perm_weight[p] topk_w of permuted row p (optional: both topk_w and perm_weight
  *                  NULL, or both set)                                    [T*k]
- * All int32/fp32 device buffers.  ws: at least moe_workspace_size bytes.
+ * All int32/fp32 device buffers.  ws: at least moe_workspace_size bytes.  Every row of
+ * topk_idx must hold k distinct experts in [0, E) (as moe_route produces); ids outside
+ * [0, E) are skipped, duplicates within a row give an unspecified permutation.
  * Source: token routing to experts and per-expert batching ("MoE 数学" section and the
  * expert-parallel paragraph of "大模型工程（一）"; "批处理策略" of "开源混合架构大模型技术解析"). */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
@@ -148,7 +151,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
  *               row_weight[r] * (a_r W_down^T) (row_weight NULL = 1), [rows, d], act_dtype;
  *               for the shared set the S experts' outputs are summed.
  * e4m3 weights are multiplied by their per-output-channel scales.  fp32 accumulation.
- * ws: at least moe_workspace_size bytes.
+ * ws / ws_bytes: reserved, may be NULL / 0.
  * Source: grouped GEMM after routing and the fused Linear+ReLU^2 kernel, section
  * "融合内核" of the FusionLLM training-framework page; SwiGLU in item 3 of section
  * "变了什么，为什么变" of "大模型工程（一）". */
@@ -170,6 +173,22 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
  * perm_token, slot_pos, intermediates) live in ws. */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Options of moe_forward_ex. */
+typedef struct {
+  /* Events recorded on `stream` at the stage boundaries of the forward (NULL entries are
+   * skipped): [0] before routing, [1] after routing, [2] after the permutation, [3] after
+   * the routed up projection, [4] after the shared up projection, [5] after the routed
+   * down projection, [6] after the shared down projection, [7] after the combine.  When
+   * routed and shared experts run in one launch (few rows per expert), [3] and [4] (and
+   * [5] and [6]) are recorded back to back after that launch.  Caller-owned events. */
+  hipEvent_t stage_events[8];
+} moe_forward_opts;
+
+/* moe_forward with options (opts may be NULL, which is moe_forward). */
+moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const void* x,
+                          void* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                          const moe_forward_opts* opts);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status status);

@@ -28,8 +28,8 @@ MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 
 EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_permute",
-                    "moe_grouped_gemm", "moe_combine", "moe_forward", "moe_status_string",
-                    "moe_last_hip_error"]
+                    "moe_grouped_gemm", "moe_combine", "moe_forward", "moe_forward_ex",
+                    "moe_status_string", "moe_last_hip_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -79,6 +79,10 @@ class Weights:
         self.c = _WeightsC(**{n: _ptr(t) for n, t in self.tensors.items()})
 
 
+class _OptsC(ctypes.Structure):
+    _fields_ = [("stage_events", ctypes.c_void_p * 8)]
+
+
 _LIB = None
 
 
@@ -101,6 +105,7 @@ def lib():
             "moe_grouped_gemm": [cfgp, i32, i32, vp, vp, vp, i32, wp, vp, vp, vp, sz, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
             "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
+            "moe_forward_ex": [cfgp, wp, vp, vp, vp, sz, vp, ctypes.POINTER(_OptsC)],
             "moe_last_hip_error": [],
         }
         for name, args in sig.items():
@@ -190,7 +195,19 @@ def combine(cfg, y_perm, slot_pos, y_shared, out, stream=None):
                              _ptr(out), _stream(stream)), "moe_combine")
 
 
-def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None):
+def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None, stage_events=None):
+    """The whole layer.  stage_events: optional list of 8 torch.cuda.Event (or None) recorded
+    at the stage boundaries (see moe_forward_opts in include/moe.h)."""
     nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
-    _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
-                             _ptr(ws), nb, _stream(stream)), "moe_forward")
+    if stage_events is None:
+        _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
+                                 _ptr(ws), nb, _stream(stream)), "moe_forward")
+        return
+    opts = _OptsC()
+    for i, ev in enumerate(stage_events):
+        if ev is not None and not ev.cuda_event:
+            ev.record()          # torch creates its events lazily; the library re-records it
+        opts.stage_events[i] = None if ev is None else ev.cuda_event
+    _check(lib().moe_forward_ex(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
+                                _ptr(ws), nb, _stream(stream), ctypes.byref(opts)),
+           "moe_forward_ex")

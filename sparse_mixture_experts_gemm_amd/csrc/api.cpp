@@ -69,6 +69,11 @@ moe_status check_config(const moe_config* c) {
   const long long Tk = (long long)c->num_tokens * c->top_k;
   if (Tk > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if ((long long)c->num_shared * c->inter_dim > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  // the kernels index activations and one expert's weights with 32-bit element offsets
+  const long long widest = c->dim > c->inter_dim ? c->dim : c->inter_dim;
+  if (Tk * widest > INT_MAX || (long long)c->num_tokens * c->num_shared * c->inter_dim > INT_MAX ||
+      (long long)c->num_experts * c->dim * c->inter_dim > INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -290,8 +295,9 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
   }
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
-                       void* ws, size_t ws_bytes, hipStream_t stream) {
+moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
+                          void* ws, size_t ws_bytes, hipStream_t stream,
+                          const moe_forward_opts* opts) {
   try {
     moe_status st = check_config(cfg);
     if (st != MOE_OK) return st;
@@ -334,34 +340,67 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
     st = current_cus(&cus);
     if (st != MOE_OK) return st;
 
-    hipError_t e = moe::launch_route(route_params(cfg), cfg->act_dtype, x, w->router,
-                                     w->logit_bias, nullptr, idx, tw, stream);
-    if (e != hipSuccess) return hip_status(e);
-    e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, idx, tw, counts, offsets, perm_token,
-                            slot_pos, perm_weight, at(cv.perm_ws), stream);
-    if (e != hipSuccess) return hip_status(e);
-    e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, cfg->act_dtype,
-                                 cfg->weight_dtype, cus, stream);
-    if (e != hipSuccess) return hip_status(e);
-    if (shared) {
-      e = moe::launch_grouped_gemm(up_s, moe::Stage::Up, cfg->act, cfg->act_dtype,
-                                   cfg->weight_dtype, cus, stream);
-      if (e != hipSuccess) return hip_status(e);
+    hipError_t e = hipSuccess;
+    auto mark = [&](int i) {
+      if (opts != nullptr && opts->stage_events[i] != nullptr && e == hipSuccess)
+        e = hipEventRecord(opts->stage_events[i], stream);
+    };
+    mark(0);
+    e = moe::launch_route(route_params(cfg), cfg->act_dtype, x, w->router, w->logit_bias,
+                          nullptr, idx, tw, stream);
+    mark(1);
+    if (e == hipSuccess)
+      e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, idx, tw, counts, offsets,
+                              perm_token, slot_pos, perm_weight, at(cv.perm_ws), stream);
+    mark(2);
+    // few rows per expert: the routed and shared experts stream their weights in one
+    // launch per stage
+    const int adt = cfg->act_dtype;
+    const bool decode = moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
+                        (!shared || (moe::decode_gemm_applies(up_s, adt) &&
+                                     moe::decode_gemm_applies(dn_s, adt)));
+    if (decode) {
+      if (e == hipSuccess)
+        e = moe::launch_decode_gemm(up_r, moe::Stage::Up, cfg->act, cfg->weight_dtype, stream,
+                                    shared ? &up_s : nullptr);
+      mark(3);
+      mark(4);
+      if (e == hipSuccess)
+        e = moe::launch_decode_gemm(dn_r, moe::Stage::Down, cfg->act, cfg->weight_dtype, stream,
+                                    shared ? &dn_s : nullptr);
+      mark(5);
+      mark(6);
+    } else {
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
+                                     stream);
+      mark(3);
+      if (shared && e == hipSuccess)
+        e = moe::launch_grouped_gemm(up_s, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
+                                     stream);
+      mark(4);
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
+                                     cus, stream);
+      mark(5);
+      if (shared && e == hipSuccess)
+        e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
+                                     cus, stream);
+      mark(6);
     }
-    e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, cfg->act_dtype,
-                                 cfg->weight_dtype, cus, stream);
-    if (e != hipSuccess) return hip_status(e);
-    if (shared) {
-      e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, cfg->act_dtype,
-                                   cfg->weight_dtype, cus, stream);
-      if (e != hipSuccess) return hip_status(e);
-    }
-    e = moe::launch_combine(T, cfg->dim, cfg->top_k, cfg->act_dtype, at(cv.y_routed), slot_pos,
-                            shared ? at(cv.y_shared) : nullptr, out, stream);
+    if (e == hipSuccess)
+      e = moe::launch_combine(T, cfg->dim, cfg->top_k, adt, at(cv.y_routed), slot_pos,
+                              shared ? at(cv.y_shared) : nullptr, out, stream);
+    mark(7);
     return hip_status(e);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_forward_ex(cfg, w, x, out, ws, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

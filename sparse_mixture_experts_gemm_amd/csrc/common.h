@@ -76,6 +76,35 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// DPP reductions (gfx9 encodings): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t x, int ctrl_sel) {
+  int y;
+  switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false); break;
+    case 1: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false); break;
+    case 2: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false); break;
+    case 3: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false); break;
+    case 4: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xA, 0xF, false); break;
+    default: y = __builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xC, 0xF, false); break;
+  }
+  return x > (uint32_t)y ? x : (uint32_t)y;
+}
+
+// Max of an unsigned value over each aligned group of 8 lanes (every lane gets its group's).
+__device__ __forceinline__ uint32_t group8_max_u32(uint32_t x) {
+  x = dpp_max_step(x, 0);
+  x = dpp_max_step(x, 1);
+  return dpp_max_step(x, 2);
+}
+
+// Max of an unsigned value over the whole wave (uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) x = dpp_max_step(x, i);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Logical workgroup -> XCD-contiguous order.  Workgroups are dispatched round-robin over
 // the 8 XCDs (workgroup b runs on XCD b % 8), so map workgroup b to a slot such that each
 // XCD walks a contiguous range of logical tiles and its L2 sees their shared operands.

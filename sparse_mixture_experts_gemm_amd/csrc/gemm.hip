@@ -96,23 +96,84 @@ __device__ __forceinline__ void store_out(void* out, size_t off, float v, bool b
 
 // ------------------------------------------------------------------------------------
 // bf16 activations, bf16 or e4m3 weights, MFMA 32x32x16.
-template <int STAGE, int ACT, bool FP8>
-__global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
-  constexpr int BM = 128, BN = 128, BK = 64;
-  constexpr int WTM = 64, WTN = 64, FM = 2, FN = 2;
-  constexpr bool SWIGLU = (STAGE == 0) && (ACT == MOE_ACT_SWIGLU);
-  constexpr int BROW = FP8 ? BK : BK * 2;            // bytes per B tile row in LDS
-  constexpr int A_BYTES = BM * BK * 2;
-  constexpr int B_BYTES = BN * BROW;
+//
+// Workgroup tile BM x BN (B columns), 4 waves in a 2 x 2 layout, wave tile (BM/2) x (BN/2)
+// = FM x FN MFMA tiles of 32 x 32.  K advances in slices of BK = 64 through an NSTAGE-deep
+// LDS ring filled by global_load_lds_dwordx4 (global -> LDS without VGPR staging): one
+// instruction writes 1 KB of LDS, 16 bytes per lane at M0 + 16 * lane.  Slice kt + NSTAGE - 1
+// is requested while slice kt is multiplied, and a partial vmcnt wait (loads retire in
+// order) lets the younger slices stay in flight across the barrier.
+//
+// LDS layout: a bf16 operand row holds 64 K values in 8 chunks of 16 bytes; chunk c of row
+// r sits at position c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 8 or 16 lanes
+// that the LDS serves per cycle in an MFMA operand read (32 consecutive rows, one chunk)
+// hit distinct banks.  Each DMA lane therefore fetches the logical chunk that belongs at
+// its physical position.  e4m3 B slices are stored raw (64 bytes per row, 16-byte chunks
+// swizzled by (r >> 1) & 3) and widened to bf16 with v_cvt_scalef32_pk_bf16_fp8 (scale 1,
+// exact) when the operand is read.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
 
-  __shared__ __align__(16) unsigned char lds[2 * (A_BYTES + B_BYTES)];
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  No VGPR is
+// written; the caller waits with vmcnt before reading the LDS.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* src) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 widen_e4m3x8(uint2 q) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Tile shapes: dense segments (the shared experts: every token) use 256 x 256 tiles; the
+// routed segments (a few hundred rows per expert) use 128 x 256 tiles, which waste fewer
+// MFMA rows in each expert's last m-tile.  Eight waves (two per SIMD) per workgroup, so
+// one wave's LDS and barrier waits are covered by its partner's MFMAs.
+template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
+__global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
+  constexpr int NTHR = WAVES * 64;
+  constexpr int BK = 64;
+  constexpr int WM = 2, WN = WAVES / 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  constexpr bool SWIGLU = (STAGE == 0) && (ACT == MOE_ACT_SWIGLU);
+  constexpr int AROW = BK * 2;                      // bytes per A row in LDS
+  constexpr int BROW = FP8 ? BK : BK * 2;           // bytes per B row in LDS
+  constexpr int A_BYTES = BM * AROW, B_BYTES = BN * BROW, ST_BYTES = A_BYTES + B_BYTES;
+  constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;   // 1 KB per DMA instruction
+  constexpr int NDMA = (A_DMA + B_DMA) / WAVES;                    // per wave per slice
+  constexpr int B_RPD = 1024 / BROW;                                // B rows per DMA
+  static_assert((A_DMA + B_DMA) % WAVES == 0, "DMA split");
+  static_assert(!SWIGLU || FN % 2 == 0, "SwiGLU pairs gate/up MFMA tiles");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
+  static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
+
+  __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
   __shared__ int s_tile0[65], s_row0[64], s_rows[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int N = p.N, K = p.K;
   const int hcols_per_tile = SWIGLU ? BN / 2 : BN;
   const int NT = (N + hcols_per_tile - 1) / hcols_per_tile;
@@ -128,114 +189,100 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
   const int lo = (int)(((long long)xcd * total) / kNumXcd);
   const int hi = (int)(((long long)(xcd + 1) * total) / kNumXcd);
 
-  const uint16_t* a_base = static_cast<const uint16_t*>(p.a);
-  const size_t wmat = (size_t)N * K;                  // weights per segment per matrix
+  const unsigned char* a_base = static_cast<const unsigned char*>(p.a);
   const int nblk_k = K / p.kblock;
+  const int nk = K / BK;
+  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  const int sw = swz8(lane & 31);      // swizzle of every operand row this lane reads
 
   for (int L = lo + slot; L < hi; L += per_x) {
     const TileCoord tc = decode_tile(L, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
     const int m0 = tc.m_tile * BM;
 
-    // ---- per-thread global source pointers for this tile
-    // A: 4 chunks of 16 B per thread: row = tid/8 + 32 i, chunk = tid % 8
-    const uint16_t* a_src[4];
-    bool a_ok[4];
+    // ---- source of every DMA this lane takes part in.  Rows past the end of the
+    // segment (or of N) are clamped to a valid row; their results are never stored.
+    const unsigned char* src[NDMA];
+    bool is_b[NDMA];
+    const size_t seg_off = (size_t)tc.seg * N * K;   // weight elements per segment
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      const int r = m0 + row;
-      a_ok[i] = r < tc.rows;
-      int src = tc.row0 + (a_ok[i] ? r : 0);
-      if (p.row_index != nullptr) src = a_ok[i] ? p.row_index[src] : 0;
-      a_src[i] = a_base + (size_t)src * K + (tid & 7) * 8;
-    }
-    // B: bf16: 4 chunks of 16 B (row = tid/8 + 32 i); e4m3: 2 chunks (row = tid/4 + 64 i)
-    constexpr int BCH = FP8 ? 2 : 4;
-    const unsigned char* b_src[BCH];
-    bool b_ok[BCH];
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int n = FP8 ? (tid >> 2) + 64 * i : (tid >> 3) + 32 * i;
-      const int cbyte = FP8 ? (tid & 3) * 16 : (tid & 7) * 16;
-      int wrow;
-      const void* wb;
-      if (STAGE == 0) {
-        if (SWIGLU) {
-          const int wc = n / WTN, r = n % WTN;
-          const int half = r / (WTN / 2);
-          wrow = tc.n_tile * (BN / 2) + wc * (WTN / 2) + (r % (WTN / 2));
-          wb = half ? p.w_up : p.w_gate;
+    for (int i = 0; i < NDMA; ++i) {
+      const int q = wave * NDMA + i;
+      is_b[i] = q >= A_DMA;
+      if (!is_b[i]) {
+        const int row = q * 8 + lane / 8;
+        int r = m0 + row;
+        r = r < tc.rows ? r : tc.rows - 1;
+        int srow = tc.row0 + r;
+        if (p.row_index != nullptr) srow = p.row_index[srow];
+        src[i] = a_base + ((size_t)srow * K + ((lane & 7) ^ swz8(row)) * 8) * 2;
+      } else {
+        const int qb = q - A_DMA;
+        const int n = FP8 ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;
+        int wrow;
+        const void* wb;
+        if (STAGE == 0) {
+          if (SWIGLU) {
+            const int wc = n / WTN, r = n % WTN;
+            const int half = r / (WTN / 2);
+            wrow = tc.n_tile * (BN / 2) + wc * (WTN / 2) + (r % (WTN / 2));
+            wb = half ? p.w_up : p.w_gate;
+          } else {
+            wrow = tc.n_tile * BN + n;
+            wb = p.w_gate;
+          }
         } else {
           wrow = tc.n_tile * BN + n;
-          wb = p.w_gate;
+          wb = p.w_down;
         }
-      } else {
-        wrow = tc.n_tile * BN + n;
-        wb = p.w_down;
+        wrow = wrow < N ? wrow : 0;
+        const size_t e = seg_off + (size_t)wrow * p.kblock;
+        src[i] = static_cast<const unsigned char*>(wb) +
+                 (FP8 ? e + ((lane & 3) ^ swz4(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
       }
-      b_ok[i] = wrow < N;
-      const size_t esz = FP8 ? 1 : 2;
-      b_src[i] = static_cast<const unsigned char*>(wb) +
-                 ((size_t)tc.seg * wmat + (size_t)(b_ok[i] ? wrow : 0) * p.kblock) * esz + cbyte;
     }
 
+    auto issue = [&](int kt) {
+      const int k0 = kt * BK;
+      const uint32_t st = lds_base + (uint32_t)((kt % NSTAGE) * ST_BYTES);
+      const size_t aoff = (size_t)k0 * 2;
+      const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
+      const size_t boff = FP8 ? koff : koff * 2;
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int q = wave * NDMA + i;
+        dma16(st + (uint32_t)(q * 1024), src[i] + (is_b[i] ? boff : aoff));
+      }
+    };
+
     f32x16 acc[FM][FN];
-    f32x16 acc_tot[FM][FN];
 #pragma unroll
     for (int a = 0; a < FM; ++a)
 #pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        acc[a][b] = f32x16{};
-        if (FP8 && STAGE == 1) acc_tot[a][b] = f32x16{};
-      }
+      for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
+    constexpr int TFM = (FP8 && STAGE == 1) ? FM : 1, TFN = (FP8 && STAGE == 1) ? FN : 1;
+    f32x16 acc_tot[TFM][TFN];
+#pragma unroll
+    for (int a = 0; a < TFM; ++a)
+#pragma unroll
+      for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
 
-    uint4 ra[4];
-    uint4 rb[BCH];
-    auto gload = [&](int kt) {
-      const int k0 = kt * BK;
+    // prologue: slices 0 .. NSTAGE-2 in flight, slice 0 landed
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-      const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
-#pragma unroll
-      for (int i = 0; i < BCH; ++i)
-        rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + koff * (FP8 ? 1 : 2))
-                        : make_uint4(0, 0, 0, 0);
-    };
-    auto sstore = [&](int buf) {
-      unsigned char* A = lds + buf * (A_BYTES + B_BYTES);
-      unsigned char* B = A + A_BYTES;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i, c = tid & 7;
-        *reinterpret_cast<uint4*>(A + row * 128 + ((c ^ (row & 7)) << 4)) = ra[i];
-      }
-      if (!FP8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (tid >> 3) + 32 * i, c = tid & 7;
-          *reinterpret_cast<uint4*>(B + row * 128 + ((c ^ (row & 7)) << 4)) = rb[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = (tid >> 2) + 64 * i, c = (tid & 3) * 2;   // two 8-byte units
-          *reinterpret_cast<uint2*>(B + row * 64 + (((c) ^ (row & 7)) << 3)) =
-              make_uint2(rb[i].x, rb[i].y);
-          *reinterpret_cast<uint2*>(B + row * 64 + (((c + 1) ^ (row & 7)) << 3)) =
-              make_uint2(rb[i].z, rb[i].w);
-        }
-      }
-    };
-
-    const int nk = K / BK;
-    gload(0);
-    sstore(0);
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue(s);
+    {
+      const int younger = min(NSTAGE - 2, nk - 1);
+      if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
+      else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
+      else wait_vmcnt<0>();
+    }
     __syncthreads();
+
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) gload(kt + 1);
+      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
       if (FP8 && STAGE == 1 && kt > 0 && ((kt * BK) % p.kblock) == 0) {
-        // new K block (another shared expert): fold the finished block with its scales
+        // the next K block belongs to another shared expert: fold the finished block
+        // with its per-channel scales
         const int blk = (kt * BK) / p.kblock - 1;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -243,13 +290,14 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
           const float sc = col < N ? p.s_down[((size_t)tc.seg * nblk_k + blk) * N + col] : 0.f;
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
-            acc_tot[fm][fn] += sc * acc[fm][fn];
+            acc_tot[fm % TFM][fn % TFN] += sc * acc[fm][fn];
             acc[fm][fn] = f32x16{};
           }
         }
       }
-      const unsigned char* A = lds + (kt & 1) * (A_BYTES + B_BYTES);
+      const unsigned char* A = lds + (kt % NSTAGE) * ST_BYTES;
       const unsigned char* B = A + A_BYTES;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
         const int c = ks * 2 + (lane >> 5);
@@ -257,19 +305,17 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           const int row = wm * WTM + fm * 32 + (lane & 31);
-          af[fm] = *reinterpret_cast<const bf16x8*>(A + row * 128 + ((c ^ (row & 7)) << 4));
+          af[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int row = wn * WTN + fn * 32 + (lane & 31);
           if (!FP8) {
-            bfr[fn] = *reinterpret_cast<const bf16x8*>(B + row * 128 + ((c ^ (row & 7)) << 4));
+            bfr[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
           } else {
-            const uint2 q = *reinterpret_cast<const uint2*>(B + row * 64 + ((c ^ (row & 7)) << 3));
-            uint4 w;
-            e4m3x4_to_bf16x4(q.x, w.x, w.y);
-            e4m3x4_to_bf16x4(q.y, w.z, w.w);
-            bfr[fn] = __builtin_bit_cast(bf16x8, w);
+            const uint2 q = *reinterpret_cast<const uint2*>(
+                B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
+            bfr[fn] = widen_e4m3x8(q);
           }
         }
 #pragma unroll
@@ -278,7 +324,14 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
           for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
       }
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
+      __builtin_amdgcn_s_setprio(0);
+      if (kt + 1 < nk) {
+        // slice kt + 1 must have landed; younger slices may stay in flight
+        const int younger = min(NSTAGE - 2, nk - 2 - kt);
+        if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
+        else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
+        else wait_vmcnt<0>();
+      }
       __syncthreads();
     }
 
@@ -307,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
             if (SWIGLU) {
               const float g = acc[fm][fh][i] * sg;
               const float u = acc[fm][fh + FN / 2][i] * su;
-              h = silu_f(g) * u;
+              h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
             } else {
               const float g = acc[fm][fh][i] * sg;
               const float rr = fmaxf(g, 0.f);
@@ -325,26 +378,25 @@ __global__ __launch_bounds__(256, 2) void gg_mfma_kernel(GemmParams p) {
           const int col = tc.n_tile * BN + wn * WTN + fn * 32 + col_in;
           const float sc = col < N ? p.s_down[((size_t)tc.seg * nblk_k + blk) * N + col] : 0.f;
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = acc_tot[fm][fn] + sc * acc[fm][fn];
+          for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = acc_tot[fm % TFM][fn % TFN] + sc * acc[fm][fn];
         }
       }
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = tc.n_tile * BN + wn * WTN + fn * 32 + col_in;
-        if (col >= N) continue;
+      for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
+        for (int i = 0; i < 16; ++i) {
+          const int r = m0 + wm * WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (r >= tc.rows) continue;
+          const float rw = p.row_weight != nullptr ? p.row_weight[tc.row0 + r] : 1.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r >= tc.rows) continue;
-            const float rw = p.row_weight != nullptr ? p.row_weight[tc.row0 + r] : 1.f;
-            store_out(p.out, (size_t)(tc.row0 + r) * N + col, rw * acc[fm][fn][i], true);
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + col_in;
+            if (col < N) store_out(p.out, (size_t)(tc.row0 + r) * N + col, rw * acc[fm][fn][i], true);
           }
         }
       }
     }
-    __syncthreads();   // LDS of this tile is reused by the next one
+    __syncthreads();   // the next tile's prologue overwrites this tile's LDS ring
   }
 }
 
@@ -440,11 +492,38 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
   }
 }
 
+// Tile configuration per call, from what the host knows of the problem: dense segments
+// take 256 x 256 tiles when that still gives every CU at least two tiles; ragged routed
+// segments take 128 x 256 tiles.
+// Each configuration is (BM, BN, waves, LDS stages, workgroups per CU).
+#ifndef MOE_CFG_ROUTED_UP
+#define MOE_CFG_ROUTED_UP 128, 256, 8, 3, 1
+#endif
+#ifndef MOE_CFG_ROUTED_DOWN
+#define MOE_CFG_ROUTED_DOWN 128, 256, 8, 3, 1
+#endif
+#ifndef MOE_CFG_DENSE_WIDE
+#define MOE_CFG_DENSE_WIDE 256, 256, 8, 2, 1
+#endif
+
+template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
+hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8>),
+                     dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int STAGE, int ACT, bool FP8>
 hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
-  const int grid = num_cus * 2;
-  hipLaunchKernelGGL((gg_mfma_kernel<STAGE, ACT, FP8>), dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  constexpr bool kWideOk = !(FP8 && STAGE == 1);   // e4m3 down: two accumulator sets
+  const bool swiglu = STAGE == 0 && ACT == MOE_ACT_SWIGLU;
+  const long long bcols = swiglu ? 2LL * p.N : p.N;
+  const long long wide_tiles = ((p.rows + 255) / 256) * ((bcols + 255) / 256);
+  if (p.offsets == nullptr && kWideOk && wide_tiles >= 2LL * num_cus) {
+    if constexpr (kWideOk) return launch_cfg<MOE_CFG_DENSE_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
+  }
+  if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_ROUTED_UP, STAGE, ACT, FP8>(p, num_cus, s);
+  else return launch_cfg<MOE_CFG_ROUTED_DOWN, STAGE, ACT, FP8>(p, num_cus, s);
 }
 
 template <int STAGE, int ACT>
@@ -467,6 +546,7 @@ hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int ac
     return launch_f32<1, MOE_ACT_SWIGLU>(p, num_cus, s);
   }
   const bool fp8 = weight_dtype == MOE_FP8_E4M3;
+  if (decode_gemm_applies(p, act_dtype)) return launch_decode_gemm(p, stage, act, weight_dtype, s);
   if (up) {
     if (fp8) return relu2 ? launch_mfma<0, MOE_ACT_RELU2, true>(p, num_cus, s)
                           : launch_mfma<0, MOE_ACT_SWIGLU, true>(p, num_cus, s);

@@ -55,6 +55,12 @@ hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* 
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
                                int weight_dtype, int num_cus, hipStream_t s);
 
+// Weight-streaming variant of the grouped GEMM for few rows per segment.  `second`, when
+// given, is a second segment set (e.g. the shared experts) run in the same launch.
+bool decode_gemm_applies(const GemmParams& p, int act_dtype);
+hipError_t launch_decode_gemm(const GemmParams& p, Stage stage, int act, int weight_dtype,
+                              hipStream_t s, const GemmParams* second = nullptr);
+
 hipError_t launch_combine(int T, int d, int k, int act_dtype, const void* y_perm,
                           const int32_t* slot_pos, const void* y_shared, void* out,
                           hipStream_t s);

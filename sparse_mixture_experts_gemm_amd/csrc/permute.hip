@@ -4,14 +4,17 @@
 // ("大模型工程（一）：Transformer 到 MoE", sections "MoE 数学：路由、容量与平衡详解" and the
 // expert-parallel paragraph; "开源混合架构大模型技术解析", "批处理策略").  The order is
 // fixed: expert ascending, then token ascending, so the result does not depend on
-// scheduling.  Three launches:
+// scheduling.  Two launches:
 //   1. histogram: one workgroup per chunk of kChunk tokens counts its slots per expert
 //      in LDS and writes the chunk's row of a [chunks][E] table;
-//   2. scan: one workgroup turns the table into counts, offsets (exclusive scan over
-//      experts) and each chunk's starting row per expert (scan over chunks);
-//   3. scatter: one wave per chunk walks its tokens 64 at a time (lane = token); each lane
-//      sets its bit in a 64-bit LDS mask per expert it picked, and the rank of a slot
-//      among earlier tokens of the same expert is a popcount of the lower bits.
+//   2. scatter: one wave per chunk first reads the whole table (lane = expert): the column
+//      sums are the counts, their exclusive scan the offsets, and the sum over earlier
+//      chunks the chunk's starting row per expert.  It then walks its tokens 64 at a time
+//      (lane = token); each lane sets its bit in a 64-bit LDS mask per expert it picked, and
+//      the rank of a slot among earlier tokens of the same expert is a popcount of the
+//      lower bits.  Chunk 0 also writes counts and offsets.
+// Up to kFusedMaxTokens tokens, one workgroup of 16 waves does both steps in a single
+// launch (each wave owns a contiguous run of tokens; the scan runs between two barriers).
 #include "common.h"
 #include "internal.h"
 
@@ -38,47 +41,44 @@ __global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k,
   if (threadIdx.x < E) chunk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-__global__ __launch_bounds__(64) void scan_kernel(int nchunks, int E,
-                                                  const int32_t* __restrict__ chunk_hist,
-                                                  int32_t* __restrict__ chunk_base,
-                                                  int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ offsets) {
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) total += chunk_hist[(size_t)c * E + e];
-  }
-  // exclusive scan over experts (wave-wide inclusive scan, then shift)
-  int incl = total;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int v = __shfl_up(incl, o, 64);
-    if (e >= o) incl += v;
-  }
-  const int excl = incl - total;
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = excl;
-    int run = excl;
-    for (int c = 0; c < nchunks; ++c) {
-      chunk_base[(size_t)c * E + e] = run;
-      run += chunk_hist[(size_t)c * E + e];
-    }
-  }
-  if (e == E - 1) offsets[E] = incl;
-}
-
-__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k,
+__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nchunks,
                                                      const int32_t* __restrict__ idx,
                                                      const float* __restrict__ topk_w,
-                                                     const int32_t* __restrict__ chunk_base,
+                                                     const int32_t* __restrict__ chunk_hist,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm_token,
                                                      int32_t* __restrict__ slot_pos,
                                                      float* __restrict__ perm_weight) {
   __shared__ int run[64];
   __shared__ unsigned long long mask[64];
   const int lane = threadIdx.x;
-  if (lane < E) run[lane] = chunk_base[(size_t)blockIdx.x * E + lane];
+  {
+    // column sums (counts), their exclusive scan (offsets) and this chunk's start per expert
+    int total = 0, before = 0;
+    if (lane < E) {
+#pragma unroll 8
+      for (int c = 0; c < nchunks; ++c) {
+        const int v = chunk_hist[(size_t)c * E + lane];
+        total += v;
+        before += c < (int)blockIdx.x ? v : 0;
+      }
+    }
+    int incl = total;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane < E) run[lane] = incl - total + before;
+    if (blockIdx.x == 0) {
+      if (lane < E) {
+        counts[lane] = total;
+        offsets[lane] = incl - total;
+      }
+      if (lane == E - 1) offsets[E] = incl;
+    }
+  }
   const int tbeg = blockIdx.x * kChunk;
   const int tend = min(T, tbeg + kChunk);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -110,28 +110,113 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k,
   }
 }
 
+constexpr int kFusedWaves = 16;
+constexpr int kFusedMaxTokens = 1024;
+
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k,
+                                                             const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ topk_w,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm_token,
+                                                             int32_t* __restrict__ slot_pos,
+                                                             float* __restrict__ perm_weight) {
+  __shared__ int hist[kFusedWaves][64];
+  __shared__ int run[kFusedWaves][64];
+  __shared__ unsigned long long mask[kFusedWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // tokens per wave: a multiple of 64 so that every scatter step is a full wave of tokens
+  const int per = (((T + kFusedWaves - 1) / kFusedWaves) + 63) & ~63;
+  const int tbeg = min(T, wave * per);
+  const int tend = min(T, tbeg + per);
+
+  hist[wave][lane] = 0;
+  wave_lds_sync();
+  for (int t = tbeg + lane; t < tend; t += 64) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int e = lane;
+    int total = 0;
+    for (int w = 0; w < kFusedWaves; ++w) total += (e < E) ? hist[w][e] : 0;
+    int incl = total;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, 64);
+      if (e >= o) incl += v;
+    }
+    int at = incl - total;
+    if (e < E) {
+      counts[e] = total;
+      offsets[e] = at;
+      for (int w = 0; w < kFusedWaves; ++w) {
+        run[w][e] = at;
+        at += hist[w][e];
+      }
+    }
+    if (e == E - 1) offsets[E] = incl;
+  }
+  __syncthreads();
+
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t0 = tbeg; t0 < tend; t0 += 64) {
+    mask[wave][lane] = 0ull;
+    wave_lds_sync();
+    const int t = t0 + lane;
+    const bool ok = t < tend;
+    if (ok) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(size_t)t * k + j];
+        if ((unsigned)e < (unsigned)E) atomicOr(&mask[wave][e], 1ull << lane);
+      }
+    }
+    wave_lds_sync();
+    if (ok) {
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(size_t)t * k + j];
+        if ((unsigned)e >= (unsigned)E) continue;
+        const int pos = run[wave][e] + __popcll(mask[wave][e] & below);
+        perm_token[pos] = t;
+        slot_pos[(size_t)t * k + j] = pos;
+        if (perm_weight != nullptr) perm_weight[pos] = topk_w[(size_t)t * k + j];
+      }
+    }
+    wave_lds_sync();
+    if (lane < E) run[wave][lane] += __popcll(mask[wave][lane]);
+    wave_lds_sync();
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int E) {
   const size_t nchunks = (size_t)(T + kChunk - 1) / kChunk;
-  return 2 * nchunks * (size_t)E * sizeof(int32_t);
+  return nchunks * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* topk_w,
                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
                           int32_t* slot_pos, float* perm_weight, void* ws, hipStream_t s) {
+  if (T <= kFusedMaxTokens) {
+    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(1024), 0, s, T, E, k, idx, topk_w,
+                       counts, offsets, perm_token, slot_pos, perm_weight);
+    return hipGetLastError();
+  }
   const int nchunks = (T + kChunk - 1) / kChunk;
   int32_t* chunk_hist = static_cast<int32_t*>(ws);
-  int32_t* chunk_base = chunk_hist + (size_t)nchunks * E;
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, T, E, k, idx, chunk_hist);
-  }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, s, nchunks, E, chunk_hist, chunk_base,
-                     counts, offsets);
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, idx, topk_w,
-                       chunk_base, perm_token, slot_pos, perm_weight);
-  }
+  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, T, E, k, idx, chunk_hist);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, nchunks, idx, topk_w,
+                     chunk_hist, counts, offsets, perm_token, slot_pos, perm_weight);
   return hipGetLastError();
 }
 

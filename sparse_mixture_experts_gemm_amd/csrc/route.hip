@@ -5,14 +5,15 @@
 // sigmoid gating and group-limited routing as in the FusionLLM MoE ("FusionLLM：融合 MLA、
 // GDN 与 MoE 的高效混合架构大模型训练框架", section "混合专家（MoE）").
 //
-// Layout on the chip: one workgroup owns 16 tokens.  Its four waves split the dim
+// Layout on the chip: one workgroup owns 16 tokens.  Its sixteen waves split the dim
 // (K) of the 16 x E logit block between them and run bf16 MFMA 16x16x32 on operands read
 // straight from global memory (x rows are read once; the E x d router weight is shared
 // by every workgroup and stays in L2).  The partial logits are summed through LDS in a
-// fixed order, then each wave scores and selects for four tokens with lane = expert:
-// group scores by shuffles inside a group, group rank by comparing against every group,
-// and k rounds of a 64-bit wave max over (score bits, inverted expert index), which
-// picks the higher score and, on equal scores, the lower expert index.
+// fixed order, then each wave scores and selects for one token with lane = expert:
+// group maxima by DPP inside aligned groups of 8 lanes (shuffles for other group sizes),
+// group rank by comparing against every group's score (readlane), and k rounds of a DPP
+// wave max over the score bits, where the lowest lane holding the max wins (ballot), i.e.
+// the lower expert index on equal scores.
 #include "common.h"
 #include "internal.h"
 
@@ -40,45 +41,64 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
     if (scores != nullptr && valid) scores[(size_t)t * p.E + lane] = s;
   }
 
+  // fp32 bit patterns of non-negative scores order like the scores themselves
+  const uint32_t sbits = __float_as_uint(s);
   bool elig = valid;
   if (p.G > 1 && p.Gk < p.G) {
     const int gsz = p.E / p.G;
     const int g = min(lane / gsz, p.G - 1);
-    float b1 = -1.0f, b2 = -1.0f;  // scores are >= 0
-    for (int i = 0; i < gsz; ++i) {
-      float v = wave_shfl(s, g * gsz + i);
-      if (v > b1) {
-        b2 = b1;
-        b1 = v;
-      } else if (v > b2) {
-        b2 = v;
+    float gs;
+    if (gsz == 8) {
+      // groups are aligned runs of 8 lanes: DPP max inside the group
+      const uint32_t b1 = group8_max_u32(valid ? sbits : 0u);
+      gs = __uint_as_float(b1);
+      if (p.n_g == 2) {
+        // drop the first lane holding the group max, then take the max again
+        const uint64_t m = __ballot(valid && sbits == b1);
+        const uint32_t gm = (uint32_t)(m >> (8 * g)) & 0xffu;
+        const int first = 8 * g + __builtin_ctz(gm | 0x100u);
+        const uint32_t b2 = group8_max_u32((valid && lane != first) ? sbits : 0u);
+        gs = __uint_as_float(b1) + __uint_as_float(b2);
       }
+    } else {
+      float b1 = -1.0f, b2 = -1.0f;  // scores are >= 0
+      for (int i = 0; i < gsz; ++i) {
+        float v = wave_shfl(s, g * gsz + i);
+        if (v > b1) {
+          b2 = b1;
+          b1 = v;
+        } else if (v > b2) {
+          b2 = v;
+        }
+      }
+      gs = (p.n_g == 2) ? (b1 + b2) : b1;
     }
-    const float gs = (p.n_g == 2) ? (b1 + b2) : b1;
     int rank = 0;
     for (int h = 0; h < p.G; ++h) {
-      float o = wave_shfl(gs, h * gsz);
+      const float o = __uint_as_float(
+          (uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(gs), h * gsz));
       rank += (o > gs) || (o == gs && h < g);
     }
     elig = valid && rank < p.Gk;
   }
 
-  uint64_t key = elig ? ((uint64_t)__float_as_uint(s) << 32) |
-                            (uint64_t)(0xffffffffu - (uint32_t)lane)
-                      : 0ull;
+  // k rounds: wave max of (score bits + 1) over eligible lanes; the lowest lane holding the
+  // max wins, i.e. the lower expert index on equal scores
+  uint32_t key = elig ? sbits + 1u : 0u;
   float sel = 0.0f;
   int sel_e = 0;
   for (int j = 0; j < p.k; ++j) {
-    const uint64_t m = wave_max_u64(key);
-    const int win = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
-    if (lane == win) key = 0ull;
+    const uint32_t mx = wave_max_u32(key);
+    const uint64_t m = __ballot(key == mx);
+    const int win = (int)__builtin_ctzll(m);
+    if (lane == win) key = 0u;
     if (lane == j) {
-      sel = __uint_as_float((uint32_t)(m >> 32));
+      sel = __uint_as_float(mx - 1u);
       sel_e = win;
     }
   }
   float sum = 0.0f;
-  for (int j = 0; j < p.k; ++j) sum += wave_shfl(sel, j);
+  for (int j = 0; j < p.k; ++j) sum += __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sel), j));
   if (lane < p.k) {
     const float wj = (p.renormalize ? sel / sum : sel) * p.route_scale;
     idx[(size_t)t * p.k + lane] = sel_e;
@@ -86,14 +106,17 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
   }
 }
 
-// bf16 router: 16 tokens per workgroup, 4 waves split K in 32-wide MFMA steps.
-__global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p,
-                                                         const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ wr,
-                                                         const float* __restrict__ bias,
-                                                         float* scores, int32_t* idx,
-                                                         float* wout) {
-  __shared__ float part[4][kRouteTok][64];
+// bf16 router: 16 tokens per workgroup; its 16 waves split K in 32-wide MFMA steps
+// (wave w takes steps w, w+16, ...), so each wave needs a single round of loads for d = 2048.
+constexpr int kRouteWaves = 16;
+
+__global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias,
+                                                          float* scores, int32_t* idx,
+                                                          float* wout) {
+  __shared__ float part[kRouteWaves][kRouteTok][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouteTok;
@@ -107,21 +130,38 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p,
 #pragma unroll
   for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = p.d >> 5;   // 32 K elements per MFMA
-  for (int st = wave; st < nsteps; st += 4) {
-    const int kk = st * 32 + g * 8;
-    uint4 av = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
-    bf16x8 a = __builtin_bit_cast(bf16x8, av);
+  const int nsteps = p.d >> 5;
+  auto load_b = [&](int kk, int n) -> uint4 {
+    const int e = n * 16 + m;
+    return (n < ntiles && e < p.E) ? *reinterpret_cast<const uint4*>(wr + (size_t)e * p.d + kk)
+                                   : make_uint4(0, 0, 0, 0);
+  };
+  int st = wave;
+  for (; st + 3 * kRouteWaves < nsteps; st += 4 * kRouteWaves) {
+    uint4 av[4], bv[4][4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n < ntiles) {
-        const int e = n * 16 + m;
-        uint4 bv = e < p.E ? *reinterpret_cast<const uint4*>(wr + (size_t)e * p.d + kk)
-                           : make_uint4(0, 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv),
-                                                         acc[n], 0, 0, 0);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int kk = (st + kRouteWaves * u) * 32 + g * 8;
+      av[u] = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) bv[u][n] = load_b(kk, n);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                         __builtin_bit_cast(bf16x8, bv[u][n]),
+                                                         acc[n], 0, 0, 0);
+  }
+  for (; st < nsteps; st += kRouteWaves) {
+    const int kk = st * 32 + g * 8;
+    const uint4 av = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                       __builtin_bit_cast(bf16x8, load_b(kk, n)),
+                                                       acc[n], 0, 0, 0);
   }
   // 16x16 MFMA result: lane holds rows 4*(lane/16)+i of column lane%16.
 #pragma unroll
@@ -130,18 +170,17 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(RouteParams p,
     for (int i = 0; i < 4; ++i) part[wave][4 * g + i][n * 16 + m] = acc[n][i];
   }
   __syncthreads();
-  for (int r = 0; r < 4; ++r) {
-    const int row = wave * 4 + r;
-    const int t = t0 + row;
-    if (t >= p.T) break;  // uniform per wave
-    const bool valid = lane < p.E;
-    float l = 0.0f;
-    if (valid) {
-      l = ((part[0][row][lane] + part[1][row][lane]) + part[2][row][lane]) + part[3][row][lane];
-      if (bias != nullptr) l += bias[lane];
-    }
-    score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
+  const int row = wave;            // one token per wave
+  const int t = t0 + row;
+  if (t >= p.T) return;            // uniform per wave; no barrier follows
+  const bool valid = lane < p.E;
+  float l = 0.0f;
+  if (valid) {
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) l += part[w][row][lane];   // fixed order
+    if (bias != nullptr) l += bias[lane];
   }
+  score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
 }
 
 // fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.
@@ -182,7 +221,7 @@ hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, cons
   if (p.T == 0) return hipSuccess;
   if (act_dtype == MOE_BF16) {
     dim3 grid((p.T + kRouteTok - 1) / kRouteTok);
-    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(256), 0, s, p,
+    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(64 * kRouteWaves), 0, s, p,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router),
                        bias, scores, idx, w);
   } else {

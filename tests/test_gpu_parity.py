@@ -225,7 +225,8 @@ def test_permute_bit_exact_on_oracle_routing(name):
 
 @pytest.mark.parametrize("T,E,k,pattern", [(1, 64, 6, "random"), (63, 64, 6, "random"),
                                            (257, 8, 8, "random"), (1000, 64, 1, "one_expert"),
-                                           (700, 64, 6, "first_six"), (5000, 16, 3, "random")])
+                                           (700, 64, 6, "first_six"), (5000, 16, 3, "random"),
+                                           (10000, 64, 6, "random"), (8192, 64, 6, "first_six")])
 def test_permute_edge_cases(T, E, k, pattern):
     rng = np.random.default_rng(T + E + k)
     if pattern == "random":
@@ -408,3 +409,15 @@ def test_forward_error_paths_enqueue_nothing():
     assert ei.value.status == 3
     torch.cuda.synchronize()
     assert bool((out == 7).all())
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "small_swiglu"])
+def test_forward_ex_records_stage_events_and_matches_forward(name):
+    s, lay, cfg, wts, ws, x, out, _ = run_forward(name)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    out2 = torch.empty_like(out)
+    moe.forward(cfg, wts, x, out2, ws, stage_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(7)]
+    assert all(t >= 0 for t in times) and sum(times) > 0
