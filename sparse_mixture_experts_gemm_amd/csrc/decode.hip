@@ -27,7 +27,22 @@ constexpr int kRowsPerChunk = 16;
 constexpr int kChunks = 4;            // rows per pass = 64
 constexpr int kStepK = 128;           // K elements per step
 
+constexpr int kLdsMaxK = 2048;        // activation rows staged in LDS up to this K
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (no VGPR written).
+__device__ __forceinline__ void dma16_dec(uint32_t lds_base, const void* src) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
 
 __device__ __forceinline__ void widen16(uint4 q, bf16x8& lo, bf16x8& hi) {
   bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
@@ -86,19 +101,27 @@ struct DecSet {
   int nwg;       // workgroups of this set
 };
 
+constexpr int kDecWaves = 8;          // waves per workgroup
+
 template <int STAGE, int ACT, bool FP8>
-__global__ __launch_bounds__(256) void dec_gemm_kernel(DecSet first, DecSet second) {
+__global__ __launch_bounds__(kDecWaves * 64) void dec_gemm_kernel(DecSet first, DecSet second) {
   constexpr bool SWIGLU = (STAGE == 0) && (ACT == MOE_ACT_SWIGLU);
   constexpr int COLS_PER_WAVE = SWIGLU ? 8 : 16;
   constexpr int ESZ = FP8 ? 1 : 2;
-  __shared__ f32x4 red[4][kChunks][64];
+  // One LDS buffer, used either for the activation rows of a segment with at most 16 rows
+  // and K <= kLdsMaxK (16 rows x K bf16; 16-byte chunk c of row m stored at chunk
+  // c ^ (m & 15) so that the 16 rows of an MFMA operand read fall in distinct banks), or,
+  // with K split across waves, for their partial sums.
+  __shared__ __align__(16) unsigned char a_lds[kRowsPerChunk * kLdsMaxK * 2];
+  f32x4(*red)[kChunks][64] = reinterpret_cast<f32x4(*)[kChunks][64]>(a_lds);
+  static_assert(sizeof(f32x4) * kDecWaves * kChunks * 64 <= sizeof(a_lds), "reduction buffer");
   const bool in_first = (int)blockIdx.x < first.nwg;
   const DecSet& ds = in_first ? first : second;
   const GemmParams& p = ds.p;
   const int bid = in_first ? (int)blockIdx.x : (int)blockIdx.x - first.nwg;
   const int nslices = ds.nslices;
   const int KSPLIT = ds.ksplit;
-  const int GROUPS = 4 / KSPLIT;              // column groups per workgroup
+  const int GROUPS = kDecWaves / KSPLIT;      // column groups per workgroup
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int grp = wave / KSPLIT;
@@ -141,6 +164,10 @@ __global__ __launch_bounds__(256) void dec_gemm_kernel(DecSet first, DecSet seco
   const int q_end = (nsteps_all * (kpart + 1)) / KSPLIT;
   const int nblk_k = K / p.kblock;
 
+  const bool a_in_lds = nrows <= kRowsPerChunk && K <= kLdsMaxK && K % 512 == 0 && KSPLIT == 1;
+  const uint32_t a_lds_base =
+      (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)a_lds;
+
   for (int r0 = 0; r0 < nrows; r0 += kRowsPerChunk * kChunks) {
     const int nch = min(kChunks, (nrows - r0 + kRowsPerChunk - 1) / kRowsPerChunk);
     const uint16_t* arow[kChunks];
@@ -153,6 +180,18 @@ __global__ __launch_bounds__(256) void dec_gemm_kernel(DecSet first, DecSet seco
       if (p.row_index != nullptr) src = p.row_index[src];
       arow[c] = a_base + (size_t)src * K + g * 8;
     }
+    if (a_in_lds) {
+      // stage the (<= 16) rows: one 1 KB DMA per (row, 512-element block)
+      const int blocks = K / 512;
+      for (int i = wave; i < nrows * blocks; i += kDecWaves) {
+        const int m = i / blocks, blk = i % blocks;
+        int srow = row0 + m;
+        if (p.row_index != nullptr) srow = p.row_index[srow];
+        const uint16_t* src = a_base + (size_t)srow * K + (size_t)(blk * 64 + (lane ^ (m & 15))) * 8;
+        dma16_dec((uint32_t)__builtin_amdgcn_readfirstlane((int)(a_lds_base + (uint32_t)(m * K * 2 + blk * 1024))),
+                  src);
+      }
+    }
     f32x4 acc[kChunks], acc_tot[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) acc[c] = acc_tot[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -161,6 +200,11 @@ __global__ __launch_bounds__(256) void dec_gemm_kernel(DecSet first, DecSet seco
     BFrag<FP8> f0, f1, f2;
     if (q_beg < q_end) f0.load(wptr(q_beg), col_ok);
     if (q_beg + 1 < q_end) f1.load(wptr(q_beg + 1), col_ok);
+    if (a_in_lds) {
+      // every lane's staging DMAs (and the first weight loads) have landed
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+      __syncthreads();
+    }
     int fold_blk = q_beg * kStepK / p.kblock;   // K block the accumulator currently holds
     for (int q = q_beg; q < q_end; ++q) {
       if (q + 2 < q_end) f2.load(wptr(q + 2), col_ok);
@@ -181,10 +225,18 @@ __global__ __launch_bounds__(256) void dec_gemm_kernel(DecSet first, DecSet seco
       for (int c = 0; c < kChunks; ++c) {
         if (c < nch) {
           uint4 a[4];
+          if (a_in_lds) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            a[s] = aok[c] ? *reinterpret_cast<const uint4*>(arow[c] + q * kStepK + 32 * s)
-                          : make_uint4(0, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+              const int ch = q * (kStepK / 8) + 4 * s + g;   // logical 16-byte chunk of row n
+              a[s] = *reinterpret_cast<const uint4*>(a_lds + n * K * 2 + ((ch ^ n) << 4));
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              a[s] = aok[c] ? *reinterpret_cast<const uint4*>(arow[c] + q * kStepK + 32 * s)
+                            : make_uint4(0, 0, 0, 0);
+          }
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]), b[s],
@@ -277,7 +329,7 @@ DecSet make_set(const GemmParams& p) {
   DecSet d;
   d.p = p;
   d.ksplit = (groups < 2048 && steps >= 16) ? 4 : (groups < 4096 && steps >= 8) ? 2 : 1;
-  const int cols_per_wg = (4 / d.ksplit) * cols;
+  const int cols_per_wg = (kDecWaves / d.ksplit) * cols;
   d.nslices = (p.N + cols_per_wg - 1) / cols_per_wg;
   d.nwg = d.nslices * p.nseg;
   return d;
@@ -293,7 +345,8 @@ hipError_t launch_dec(const GemmParams& p, const GemmParams* p2, hipStream_t s) 
   }
   const long long grid = (long long)a.nwg + b.nwg;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((dec_gemm_kernel<STAGE, ACT, FP8>), dim3((unsigned)grid), dim3(256), 0, s, a, b);
+  hipLaunchKernelGGL((dec_gemm_kernel<STAGE, ACT, FP8>), dim3((unsigned)grid), dim3(kDecWaves * 64), 0,
+                     s, a, b);
   return hipGetLastError();
 }
 
