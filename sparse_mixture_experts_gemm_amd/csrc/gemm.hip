@@ -10,17 +10,22 @@
 //   DOWN: y = row_weight * (h W_down^T)     routing weight applied in the epilogue
 // Segments come from the device-side offsets, so the host never waits for the routing.
 //
-// gfx950 mapping (bf16 / e4m3 weights): persistent workgroups of 4 waves own a BM x BN
-// output tile; waves are laid out 2 x 2 and issue v_mfma_f32_32x32x16_bf16 on 64 x 64
-// sub-tiles.  A and B K-slices (BK = 64) are staged in LDS, double-buffered, with the 16-byte
-// chunks of each 128-byte row XOR-swizzled by (row & 7) so that the MFMA operand reads
-// (32 rows, one chunk each) spread over all banks.  For SwiGLU the B tile interleaves
-// gate and up rows per 32-column MFMA tile, so the gate and up results of an output
-// element land in the same lane and the activation runs in registers.  e4m3 weights are
-// staged as bytes and widened to bf16 (exactly) when read from LDS; their per-channel
-// scales multiply the fp32 accumulator.  Tiles are walked in XCD-contiguous order:
-// workgroup b runs on XCD b % 8, and each XCD takes a contiguous range of (expert,
-// n-tile, m-tile) tiles so that tiles sharing an expert's weights share that XCD's L2.
+// gfx950 mapping (bf16 / e4m3 weights): one persistent workgroup of 8 waves per CU walks a
+// list of BM x BN output tiles; the waves form a 2 x 4 grid over the tile and issue
+// v_mfma_f32_32x32x16_bf16 on 32 x 32 sub-tiles.  A and B K-slices (BK = 64) stream into a
+// ring of LDS stages through direct global->LDS loads; the 16-byte chunks of every 128-byte
+// LDS row are XOR-swizzled so that MFMA operand reads are free of bank conflicts.  The
+// weights are the MFMA's first operand and the token rows its second, and the weight rows
+// of each 32-row block are staged in a fixed permutation, so that every lane ends with 16
+// consecutive output features of one token and writes them with two 16-byte stores.  For
+// SwiGLU the B tile interleaves gate and up rows per 32-row MFMA block, so the gate and up
+// results of an output element land in the same lane and the activation runs in
+// registers.  e4m3 weights are staged as bytes and widened to bf16 (exactly) when read from
+// LDS; their per-channel scales multiply the fp32 accumulator.  Tiles are walked in
+// XCD-contiguous order: workgroup b runs on XCD b % 8, and each XCD takes a contiguous range
+// of (expert, n-tile, m-tile) tiles so that tiles sharing an expert's weights share that
+// XCD's L2.  The K-slices of a workgroup's consecutive tiles form one stream, so the loads
+// of the next tile are in flight while the current tile's epilogue runs.
 #include "common.h"
 #include "internal.h"
 
@@ -89,20 +94,16 @@ __device__ __forceinline__ TileCoord decode_tile(int L, int nseg, int BM, int NT
   return c;
 }
 
-__device__ __forceinline__ void store_out(void* out, size_t off, float v, bool bf16) {
-  if (bf16) static_cast<uint16_t*>(out)[off] = (uint16_t)f32_to_bf16_bits(v);
-  else static_cast<float*>(out)[off] = v;
-}
-
 // ------------------------------------------------------------------------------------
 // bf16 activations, bf16 or e4m3 weights, MFMA 32x32x16.
 //
-// Workgroup tile BM x BN (B columns), 4 waves in a 2 x 2 layout, wave tile (BM/2) x (BN/2)
-// = FM x FN MFMA tiles of 32 x 32.  K advances in slices of BK = 64 through an NSTAGE-deep
-// LDS ring filled by global_load_lds_dwordx4 (global -> LDS without VGPR staging): one
-// instruction writes 1 KB of LDS, 16 bytes per lane at M0 + 16 * lane.  Slice kt + NSTAGE - 1
-// is requested while slice kt is multiplied, and a partial vmcnt wait (loads retire in
-// order) lets the younger slices stay in flight across the barrier.
+// Workgroup tile BM x BN (B = weight rows), WAVES waves in a 2 x (WAVES/2) layout, wave
+// tile WTM x WTN = FM x FN MFMA blocks of 32 x 32.  K advances in slices of BK = 64 through
+// an NSTAGE-deep LDS ring filled by global_load_lds_dwordx4 (global -> LDS without VGPR
+// staging): one instruction writes 1 KB of LDS, 16 bytes per lane at M0 + 16 * lane.  The
+// slices of all the tiles a workgroup owns form one sequence; slice g + NSTAGE - 1 is
+// requested while slice g is multiplied, and a partial vmcnt wait (loads retire in order)
+// lets the younger slices stay in flight across the barrier.
 //
 // LDS layout: a bf16 operand row holds 64 K values in 8 chunks of 16 bytes; chunk c of row
 // r sits at position c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 8 or 16 lanes
@@ -111,8 +112,14 @@ __device__ __forceinline__ void store_out(void* out, size_t off, float v, bool b
 // its physical position.  e4m3 B slices are stored raw (64 bytes per row, 16-byte chunks
 // swizzled by (r >> 1) & 3) and widened to bf16 with v_cvt_scalef32_pk_bf16_fp8 (scale 1,
 // exact) when the operand is read.
+//
+// Output layout: D = W_blk * A_blk^T per 32 x 32 block, so element i of lane l is token
+// (column) l % 32 and MFMA row 8 * (i / 4) + 4 * (l / 32) + i % 4.  LDS row r of a 32-row
+// weight block holds weight row perm32(r) of the block, which makes that element feature
+// 16 * (l / 32) + i: a lane's 16 values are consecutive features of one token.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int perm32(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
 
 // 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  No VGPR is
 // written; the caller waits with vmcnt before reading the LDS.
@@ -145,6 +152,28 @@ __device__ __forceinline__ bf16x8 widen_e4m3x8(uint2 q) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// 16 consecutive fp32 values (scaled by the per-feature factors when given) -> 16 bf16 at
+// dst (32-byte aligned), as two 16-byte stores.
+__device__ __forceinline__ void store16_bf16(void* dst, const float (&v)[16]) {
+  uint4 lo, hi;
+  lo.x = pack_bf16x2(v[0], v[1]);   lo.y = pack_bf16x2(v[2], v[3]);
+  lo.z = pack_bf16x2(v[4], v[5]);   lo.w = pack_bf16x2(v[6], v[7]);
+  hi.x = pack_bf16x2(v[8], v[9]);   hi.y = pack_bf16x2(v[10], v[11]);
+  hi.z = pack_bf16x2(v[12], v[13]); hi.w = pack_bf16x2(v[14], v[15]);
+  uint4* d = static_cast<uint4*>(dst);
+  d[0] = lo;
+  d[1] = hi;
+}
+
+__device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 t = s4[q];
+    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+  }
+}
+
 // Tile shapes: dense segments (the shared experts: every token) use 256 x 256 tiles; the
 // routed segments (a few hundred rows per expert) use 128 x 256 tiles, which waste fewer
 // MFMA rows in each expert's last m-tile.  Eight waves (two per SIMD) per workgroup, so
@@ -166,9 +195,12 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   static_assert(!SWIGLU || FN % 2 == 0, "SwiGLU pairs gate/up MFMA tiles");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
+  static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
 
   __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
   __shared__ int s_tile0[65], s_row0[64], s_rows[64];
+  __shared__ int s_arow[2][BM];     // gathered A rows of upcoming tiles, by tile parity
+  __shared__ float s_rw[3][BM];     // row weights of upcoming tiles, by tile index mod 3
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,56 +214,93 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   __syncthreads();
   const int total = s_tile0[p.nseg];
 
+  // this workgroup's tiles: first + j * per_x, j < ntiles, inside its XCD's range
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_x = (nwg - xcd + kNumXcd - 1) / kNumXcd;
   const int lo = (int)(((long long)xcd * total) / kNumXcd);
   const int hi = (int)(((long long)(xcd + 1) * total) / kNumXcd);
+  const int first = lo + slot;
+  const int ntiles = first < hi ? (hi - first + per_x - 1) / per_x : 0;
+  if (ntiles == 0) return;   // uniform over the workgroup
+  const int nk = K / BK;
+  const int nslices = ntiles * nk;
 
   const unsigned char* a_base = static_cast<const unsigned char*>(p.a);
+  const bool gather = p.row_index != nullptr;
+  const bool has_rw = STAGE == 1 && p.row_weight != nullptr;
+  // Per-row data (gathered A rows, row weights) is staged in LDS by the epilogue two tiles
+  // before its use, which needs a tile's slices to span at least NSTAGE - 1 steps; global
+  // loads issued in the main loop would make the compiler's waits drain the DMA stream.
+  const bool prefetch = (gather || has_rw) && nk >= NSTAGE - 1;
   const int nblk_k = K / p.kblock;
-  const int nk = K / BK;
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
   const int sw = swz8(lane & 31);      // swizzle of every operand row this lane reads
 
-  for (int L = lo + slot; L < hi; L += per_x) {
-    const TileCoord tc = decode_tile(L, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
-    const int m0 = tc.m_tile * BM;
+  auto tile_at = [&](int j) {
+    return decode_tile(first + j * per_x, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
+  };
+  // row of the segment's row space that A row r of a tile reads (clamped into the segment;
+  // the results of clamped rows are never stored)
+  auto seg_row = [&](const TileCoord& tc, int r) {
+    int rr = tc.m_tile * BM + r;
+    rr = rr < tc.rows ? rr : tc.rows - 1;
+    return tc.row0 + rr;
+  };
 
-    // ---- source of every DMA this lane takes part in.  Rows past the end of the
-    // segment (or of N) are clamped to a valid row; their results are never stored.
-    const unsigned char* src[NDMA];
-    bool is_b[NDMA];
+  if (prefetch) {
+    for (int j = 0; j < 2 && j < ntiles; ++j) {
+      const TileCoord tc = tile_at(j);
+      if (tid < BM) {
+        const int sr = seg_row(tc, tid);
+        if (gather) s_arow[j][tid] = p.row_index[sr];
+        if (has_rw) s_rw[j][tid] = p.row_weight[sr];
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- sources of every DMA this lane takes part in, for the tile being loaded
+  const unsigned char* src[NDMA];
+  bool is_b[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) is_b[i] = wave * NDMA + i >= A_DMA;
+
+  auto set_sources = [&](int j) {
+    const TileCoord tc = tile_at(j);
+    if (gather && !prefetch) {
+      // short K: the rows of tile j are gathered here, at the cost of draining the loads
+      // in flight (buffer j & 1 was last read two tiles ago, before several barriers)
+      if (tid < BM) s_arow[j & 1][tid] = p.row_index[seg_row(tc, tid)];
+      __syncthreads();
+    }
     const size_t seg_off = (size_t)tc.seg * N * K;   // weight elements per segment
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
-      is_b[i] = q >= A_DMA;
       if (!is_b[i]) {
         const int row = q * 8 + lane / 8;
-        int r = m0 + row;
-        r = r < tc.rows ? r : tc.rows - 1;
-        int srow = tc.row0 + r;
-        if (p.row_index != nullptr) srow = p.row_index[srow];
+        const int srow = gather ? s_arow[j & 1][row] : seg_row(tc, row);
         src[i] = a_base + ((size_t)srow * K + ((lane & 7) ^ swz8(row)) * 8) * 2;
       } else {
         const int qb = q - A_DMA;
-        const int n = FP8 ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;
+        const int n = FP8 ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;   // LDS row
+        const int nl = (n & ~31) | perm32(n & 31);                           // weight row
         int wrow;
         const void* wb;
         if (STAGE == 0) {
           if (SWIGLU) {
-            const int wc = n / WTN, r = n % WTN;
+            const int wc = nl / WTN, r = nl % WTN;
             const int half = r / (WTN / 2);
             wrow = tc.n_tile * (BN / 2) + wc * (WTN / 2) + (r % (WTN / 2));
             wb = half ? p.w_up : p.w_gate;
           } else {
-            wrow = tc.n_tile * BN + n;
+            wrow = tc.n_tile * BN + nl;
             wb = p.w_gate;
           }
         } else {
-          wrow = tc.n_tile * BN + n;
+          wrow = tc.n_tile * BN + nl;
           wb = p.w_down;
         }
         wrow = wrow < N ? wrow : 0;
@@ -240,163 +309,236 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
                  (FP8 ? e + ((lane & 3) ^ swz4(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
       }
     }
+  };
 
-    auto issue = [&](int kt) {
-      const int k0 = kt * BK;
-      const uint32_t st = lds_base + (uint32_t)((kt % NSTAGE) * ST_BYTES);
-      const size_t aoff = (size_t)k0 * 2;
-      const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
-      const size_t boff = FP8 ? koff : koff * 2;
+  // next slice to request: tile ij, k-slice ikt, ring stage ist
+  int ij = 0, ikt = 0, ist = 0;
+  set_sources(0);
+  auto issue_next = [&]() {
+    if (ikt == nk) {
+      ikt = 0;
+      ++ij;
+      set_sources(ij);
+    }
+    const int k0 = ikt * BK;
+    const uint32_t st = lds_base + (uint32_t)(ist * ST_BYTES);
+    const size_t aoff = (size_t)k0 * 2;
+    const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
+    const size_t boff = FP8 ? koff : koff * 2;
 #pragma unroll
-      for (int i = 0; i < NDMA; ++i) {
-        const int q = wave * NDMA + i;
-        dma16(st + (uint32_t)(q * 1024), src[i] + (is_b[i] ? boff : aoff));
+    for (int i = 0; i < NDMA; ++i) {
+      const int q = wave * NDMA + i;
+      dma16(st + (uint32_t)(q * 1024), src[i] + (is_b[i] ? boff : aoff));
+    }
+    ++ikt;
+    ist = ist + 1 == NSTAGE ? 0 : ist + 1;
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
+  constexpr int TFM = (FP8 && STAGE == 1) ? FM : 1, TFN = (FP8 && STAGE == 1) ? FN : 1;
+  f32x16 acc_tot[TFM][TFN];
+#pragma unroll
+  for (int a = 0; a < TFM; ++a)
+#pragma unroll
+    for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
+
+  // prologue: slices 0 .. NSTAGE-2 in flight, slice 0 landed
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nslices) issue_next();
+  {
+    const int younger = min(NSTAGE - 2, nslices - 1);
+    if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
+    else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
+    else wait_vmcnt<0>();
+  }
+  __syncthreads();
+
+  const int col_in = lane & 31;    // token column of this lane in a 32 x 32 block
+  const int fhalf = lane >> 5;     // which 16 features of a block this lane holds
+  TileCoord tc = tile_at(0);
+  int j = 0, kt = 0, cst = 0;      // tile, k-slice and ring stage being multiplied
+  int j3 = 0;                      // j mod 3
+  for (int g = 0; g < nslices; ++g) {
+    if (g + NSTAGE - 1 < nslices) issue_next();
+    if (FP8 && STAGE == 1 && kt > 0 && ((kt * BK) % p.kblock) == 0) {
+      // the next K block belongs to another shared expert: fold the finished block
+      // with its per-channel scales
+      const int blk = (kt * BK) / p.kblock - 1;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+        float sc[16];
+        if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
+        else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc_tot[fm % TFM][fn % TFN][i] += sc[i] * acc[fm][fn][i];
+          acc[fm][fn] = f32x16{};
+        }
       }
-    };
+    }
+    const unsigned char* A = lds + cst * ST_BYTES;
+    const unsigned char* B = A + A_BYTES;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm * WTM + fm * 32 + (lane & 31);
+        af[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int row = wn * WTN + fn * 32 + (lane & 31);
+        if (!FP8) {
+          bfr[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
+        } else {
+          const uint2 q = *reinterpret_cast<const uint2*>(
+              B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
+          bfr[fn] = widen_e4m3x8(q);
+        }
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
 
-    f32x16 acc[FM][FN];
+    if (kt == nk - 1) {
+      // ---- epilogue of tile j while the next tile's first slices are in flight
+      int pf_row = 0;
+      float pf_w = 0.f;
+      const bool pf = prefetch && j + 2 < ntiles && tid < BM;
+      if (pf) {
+        const int sr = seg_row(tile_at(j + 2), tid);
+        if (gather) pf_row = p.row_index[sr];
+        if (has_rw) pf_w = p.row_weight[sr];
+      }
+      if (has_rw && !prefetch) {
+        // short K: this tile's row weights are staged here (buffer j3 was last read by the
+        // epilogue three tiles ago)
+        if (tid < BM) s_rw[j3][tid] = p.row_weight[seg_row(tc, tid)];
+        __syncthreads();
+      }
+      const int m0 = tc.m_tile * BM;
+      // every load of the epilogue is issued before its first store, so that the waits
+      // for them do not also wait for stores
+      if (STAGE == 0) {
+        constexpr int FH = SWIGLU ? FN / 2 : FN;
+        float sg[FH][16], su[FH][16];
+        if (FP8) {
 #pragma unroll
-    for (int a = 0; a < FM; ++a)
+          for (int fh = 0; fh < FH; ++fh) {
+            const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
+                                    : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
+            const int hc = hcol < N ? hcol : 0;
+            load16_f32(p.s_gate + (size_t)tc.seg * N + hc, sg[fh]);
+            if (SWIGLU) load16_f32(p.s_up + (size_t)tc.seg * N + hc, su[fh]);
+          }
+        }
 #pragma unroll
-      for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
-    constexpr int TFM = (FP8 && STAGE == 1) ? FM : 1, TFN = (FP8 && STAGE == 1) ? FN : 1;
-    f32x16 acc_tot[TFM][TFN];
+        for (int fh = 0; fh < FH; ++fh) {
+          const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
+                                  : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
+          if (hcol >= N) continue;
 #pragma unroll
-    for (int a = 0; a < TFM; ++a)
+          for (int fm = 0; fm < FM; ++fm) {
+            const int r = m0 + wm * WTM + fm * 32 + col_in;
+            if (r >= tc.rows) continue;
+            float h[16];
 #pragma unroll
-      for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
-
-    // prologue: slices 0 .. NSTAGE-2 in flight, slice 0 landed
+            for (int i = 0; i < 16; ++i) {
+              if (SWIGLU) {
+                const float gv = FP8 ? acc[fm][fh][i] * sg[fh][i] : acc[fm][fh][i];
+                const float uv = FP8 ? acc[fm][fh + FN / 2][i] * su[fh][i] : acc[fm][fh + FN / 2][i];
+                h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              } else {
+                const float gv = FP8 ? acc[fm][fh][i] * sg[fh][i] : acc[fm][fh][i];
+                const float rr = fmaxf(gv, 0.f);
+                h[i] = rr * rr;
+              }
+            }
+            store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + hcol, h);
+          }
+        }
+      } else {
+        float rw[FM];
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-      if (s < nk) issue(s);
-    {
-      const int younger = min(NSTAGE - 2, nk - 1);
+        for (int fm = 0; fm < FM; ++fm) rw[fm] = has_rw ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
+        if (FP8) {
+          const int blk = nblk_k - 1;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+            float sc[16];
+            if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
+            else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                acc[fm][fn][i] = acc_tot[fm % TFM][fn % TFN][i] + sc[i] * acc[fm][fn][i];
+          }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int r = m0 + wm * WTM + fm * 32 + col_in;
+          if (r >= tc.rows) continue;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+            if (col >= N) continue;
+            float y[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[i] = rw[fm] * acc[fm][fn][i];
+            store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + col, y);
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
+#pragma unroll
+      for (int a = 0; a < TFM; ++a)
+#pragma unroll
+        for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
+      // stores and loads may retire out of order with respect to each other: drain all
+      wait_vmcnt<0>();
+      if (pf) {
+        if (gather) s_arow[j & 1][tid] = pf_row;   // tile j + 2 has the parity of tile j
+        if (has_rw) s_rw[j3 == 0 ? 2 : j3 - 1][tid] = pf_w;   // (j + 2) mod 3
+      }
+      ++j;
+      j3 = j3 == 2 ? 0 : j3 + 1;
+      kt = 0;
+      if (j < ntiles) tc = tile_at(j);
+    } else {
+      ++kt;
+      // slice g + 1 must have landed; younger slices may stay in flight
+      const int younger = min(NSTAGE - 2, nslices - 2 - g);
       if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
       else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
       else wait_vmcnt<0>();
     }
+    cst = cst + 1 == NSTAGE ? 0 : cst + 1;
     __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
-      if (FP8 && STAGE == 1 && kt > 0 && ((kt * BK) % p.kblock) == 0) {
-        // the next K block belongs to another shared expert: fold the finished block
-        // with its per-channel scales
-        const int blk = (kt * BK) / p.kblock - 1;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = tc.n_tile * BN + wn * WTN + fn * 32 + (lane & 31);
-          const float sc = col < N ? p.s_down[((size_t)tc.seg * nblk_k + blk) * N + col] : 0.f;
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            acc_tot[fm % TFM][fn % TFN] += sc * acc[fm][fn];
-            acc[fm][fn] = f32x16{};
-          }
-        }
-      }
-      const unsigned char* A = lds + (kt % NSTAGE) * ST_BYTES;
-      const unsigned char* B = A + A_BYTES;
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int c = ks * 2 + (lane >> 5);
-        bf16x8 af[FM], bfr[FN];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int row = wm * WTM + fm * 32 + (lane & 31);
-          af[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int row = wn * WTN + fn * 32 + (lane & 31);
-          if (!FP8) {
-            bfr[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
-          } else {
-            const uint2 q = *reinterpret_cast<const uint2*>(
-                B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
-            bfr[fn] = widen_e4m3x8(q);
-          }
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bfr[fn], acc[fm][fn], 0, 0, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      if (kt + 1 < nk) {
-        // slice kt + 1 must have landed; younger slices may stay in flight
-        const int younger = min(NSTAGE - 2, nk - 2 - kt);
-        if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
-        else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
-        else wait_vmcnt<0>();
-      }
-      __syncthreads();
-    }
-
-    // ---- epilogue.  32x32 MFMA result: element i of a lane is row 8*(i/4) + 4*(lane/32)
-    // + i%4, column lane%32 of the 32x32 sub-tile.
-    const int col_in = lane & 31;
-    if (STAGE == 0) {
-      constexpr int FH = SWIGLU ? FN / 2 : FN;
-#pragma unroll
-      for (int fh = 0; fh < FH; ++fh) {
-        const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + col_in
-                                : tc.n_tile * BN + wn * WTN + fh * 32 + col_in;
-        if (hcol >= N) continue;
-        float sg = 1.f, su = 1.f;
-        if (FP8) {
-          sg = p.s_gate[(size_t)tc.seg * N + hcol];
-          if (SWIGLU) su = p.s_up[(size_t)tc.seg * N + hcol];
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r >= tc.rows) continue;
-            float h;
-            if (SWIGLU) {
-              const float g = acc[fm][fh][i] * sg;
-              const float u = acc[fm][fh + FN / 2][i] * su;
-              h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-            } else {
-              const float g = acc[fm][fh][i] * sg;
-              const float rr = fmaxf(g, 0.f);
-              h = rr * rr;
-            }
-            store_out(p.out, (size_t)(tc.row0 + r) * N + hcol, h, true);
-          }
-        }
-      }
-    } else {
-      if (FP8) {
-        const int blk = nblk_k - 1;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int col = tc.n_tile * BN + wn * WTN + fn * 32 + col_in;
-          const float sc = col < N ? p.s_down[((size_t)tc.seg * nblk_k + blk) * N + col] : 0.f;
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = acc_tot[fm % TFM][fn % TFN] + sc * acc[fm][fn];
-        }
-      }
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = m0 + wm * WTM + fm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (r >= tc.rows) continue;
-          const float rw = p.row_weight != nullptr ? p.row_weight[tc.row0 + r] : 1.f;
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + col_in;
-            if (col < N) store_out(p.out, (size_t)(tc.row0 + r) * N + col, rw * acc[fm][fn][i], true);
-          }
-        }
-      }
-    }
-    __syncthreads();   // the next tile's prologue overwrites this tile's LDS ring
   }
 }
 

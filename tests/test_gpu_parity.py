@@ -35,6 +35,12 @@ SMALL = {
     "single_token": W.small_shape(T=1, d=128, E=64, k=6, G=8, Gk=4, S=1, I=64, seed=35),
     "topk1_nogroups": W.small_shape(T=130, d=128, E=32, k=1, G=1, Gk=1, S=0, I=64, seed=36,
                                     renormalize=False, route_scale=2.5),
+    # more tiles than workgroups: each persistent workgroup streams several tiles
+    "multi_tile_swiglu": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256, seed=37),
+    "multi_tile_relu2_e4m3": W.small_shape(T=8192, d=512, E=8, k=4, G=2, Gk=1, S=1, I=256,
+                                           act="relu2", weight_dtype="e4m3", seed=38),
+    # K = 64: one K-slice per tile, several tiles per workgroup
+    "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
 }
 
 
@@ -304,8 +310,47 @@ def test_grouped_gemm_down_routed(name):
     assert err <= TOL[s.act_dtype] * np.max(np.abs(ref)), err
 
 
+@pytest.mark.parametrize("name", ["multi_tile_swiglu", "multi_tile_relu2_e4m3", "short_k"])
+def test_grouped_gemm_routed_every_row(name):
+    """Up and down routed GEMMs with several tiles per workgroup, every output row checked."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    r = O.route(lay)
+    counts, offsets, perm_token, slot_pos = O.permute(r["idx"], s.E)
+    Tk = s.T * s.k
+    pw = np.empty(Tk, np.float32)
+    pw[slot_pos] = r["w"].astype(np.float32).reshape(-1)
+    cfg = config(s)
+    wts = weights(lay)
+    h = act_empty((Tk, s.I), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, to_dev(lay.x),
+                     to_dev(perm_token), to_dev(offsets), Tk, wts, None, h)
+    h_in = W.random_act((Tk, s.I), seed=79, dtype=s.act_dtype, std=0.5)
+    y = act_empty((Tk, s.d), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, to_dev(h_in), None,
+                     to_dev(offsets), Tk, wts, to_dev(pw), y)
+    torch.cuda.synchronize()
+    got_h = act_to_f64(h, s.act_dtype)
+    got_y = act_to_f64(y, s.act_dtype)
+    x64 = r["x"]
+    h64 = O.decode_act(h_in, s.act_dtype)
+    ref_h = np.zeros((Tk, s.I))
+    ref_y = np.zeros((Tk, s.d))
+    for e in range(s.E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            ref_h[a:b] = O.expert_up(x64[perm_token[a:b]], *_dense(lay, "up", e), s.act)
+            ref_y[a:b] = pw[a:b].astype(np.float64)[:, None] * O.expert_down(h64[a:b], _dense(lay, "down", e))
+    eh = np.abs(got_h - ref_h).max(axis=1)
+    ey = np.abs(got_y - ref_y).max(axis=1)
+    bad_h = np.nonzero(eh > TOL[s.act_dtype] * np.max(np.abs(ref_h)))[0]
+    bad_y = np.nonzero(ey > TOL[s.act_dtype] * np.max(np.abs(ref_y)))[0]
+    assert bad_h.size == 0, f"up: {bad_h.size} rows off, first {bad_h[:8]}"
+    assert bad_y.size == 0, f"down: {bad_y.size} rows off, first {bad_y[:8]}"
+
+
 @pytest.mark.parametrize("name", ["small_swiglu", "small_relu2_e4m3", "small_f32", "fusionllm_bf16",
-                                  "fp8_relu2"])
+                                  "fp8_relu2", "multi_tile_swiglu", "short_k"])
 def test_grouped_gemm_shared(name):
     s = shape_of(name)
     lay = layer_of(name)
