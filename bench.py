@@ -141,7 +141,9 @@ def decode_bytes(s, counts):
     return (touched + s.S) * weight_bytes_per_expert(s) + s.E * s.d * ab + 2 * s.T * s.d * ab, touched
 
 
-def cpu_baseline(lay, n_tokens):
+def cpu_baseline(lay, n_tokens, min_seconds=10.0):
+    """The fp64 oracle on the host cores: whole forwards of the first n_tokens tokens of the
+    same layer, repeated until at least min_seconds of wall time have passed."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -149,12 +151,67 @@ def cpu_baseline(lay, n_tokens):
                     or [1])
     except Exception:
         cores = os.cpu_count() or 1
+    reps = 0
     t0 = time.perf_counter()
-    O.moe_forward(lay, tokens=np.arange(n_tokens))
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle forward of the first {n_tokens} tokens of the same layer "
-                      f"(decode of all expert weights included), {dt:.1f} s wall"}
+    while True:
+        O.moe_forward(lay, tokens=np.arange(n_tokens))
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": reps * n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} fp64 oracle forward(s) of {n_tokens} tokens of the same layer "
+                      f"(routing, all expert FFNs, combine), {dt:.1f} s wall"}
+
+
+GEMM_SOURCES = ["gemm.hip", "common.h", "internal.h", "api.cpp"]
+DECODE_SOURCES = ["decode.hip", "common.h", "internal.h", "api.cpp"]
+
+
+def kernel_source_digest(names=GEMM_SOURCES):
+    """sha256 over the sources that define a kernel and its launch."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc")
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(name, sources=GEMM_SOURCES):
+    """HBM bytes per launch recorded in profiles/<name> (from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs), or None when the file is absent or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device copy of a known size (torch's copy kernel), for scaling the TCC byte
+    counters: run it under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+    return 0
 
 
 def main(argv=None):
@@ -163,7 +220,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fusionllm_bf16")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args(argv)
@@ -171,6 +231,9 @@ def main(argv=None):
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
               "sharded across GPUs in this build.", file=sys.stderr)
         return 2
+
+    if args.copy_probe_mib > 0:
+        return copy_probe(args.copy_probe_mib)
 
     import torch
     import workloads as W
@@ -209,7 +272,8 @@ def main(argv=None):
         "stage_ms_with_events": stage_ms,
         "roofline": {"kernel": "grouped GEMM, routed up projection (SwiGLU epilogue)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": profiled_traffic(f"traffic_up_routed_{shape.name}.txt"),
                      "kernel_ms": dom_ms, "algorithmic_tflop": fl[dom] / 1e12},
     }
     if not args.no_decode:
@@ -235,10 +299,12 @@ def main(argv=None):
                                       "achieved": up_bytes / (d_up_ms * 1e-3) / 1e9,
                                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                       "frac": up_bytes / (d_up_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                                      "traffic": None, "kernel_ms": d_up_ms,
+                                      "traffic": profiled_traffic(
+                                          f"traffic_decode_up_{dshape.name}.txt", DECODE_SOURCES),
+                                      "kernel_ms": d_up_ms,
                                       "algorithmic_bytes": up_bytes}}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(lay, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_tokens, shape.T), args.cpu_seconds)
     print(json.dumps(res))
     return 0
 
