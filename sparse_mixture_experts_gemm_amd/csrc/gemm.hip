@@ -388,32 +388,38 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     }
     const unsigned char* A = lds + cst * ST_BYTES;
     const unsigned char* B = A + A_BYTES;
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    // operand fragments of K-step ks + 1 are read from LDS while the MFMAs of step ks run
+    bf16x8 af[2][FM], bfr[2][FN];
+    auto load_frags = [&](int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
       const int c = ks * 2 + (lane >> 5);
-      bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int row = wm * WTM + fm * 32 + (lane & 31);
-        af[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
+        a[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int row = wn * WTN + fn * 32 + (lane & 31);
         if (!FP8) {
-          bfr[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
+          b[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
         } else {
           const uint2 q = *reinterpret_cast<const uint2*>(
               B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
-          bfr[fn] = widen_e4m3x8(q);
+          b[fn] = widen_e4m3x8(q);
         }
       }
+    };
+    load_frags(0, af[0], bfr[0]);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[fn], af[fm], acc[fm][fn], 0, 0, 0);
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
+                                                                acc[fm][fn], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
 
