@@ -5,7 +5,7 @@
 // expert-parallel paragraph; "开源混合架构大模型技术解析", "批处理策略").  The order is
 // fixed: expert ascending, then token ascending, so the result does not depend on
 // scheduling.  Two launches:
-//   1. histogram: one workgroup per chunk of kChunk tokens counts its slots per expert
+//   1. histogram: one workgroup per chunk of tokens (at most 64 chunks) counts its slots per expert
 //      in LDS and writes the chunk's row of a [chunks][E] table;
 //   2. scatter: one wave per chunk first reads the whole table (lane = expert): the column
 //      sums are the counts, their exclusive scan the offsets, and the sum over earlier
@@ -13,8 +13,9 @@
 //      (lane = token); each lane sets its bit in a 64-bit LDS mask per expert it picked, and
 //      the rank of a slot among earlier tokens of the same expert is a popcount of the
 //      lower bits.  Chunk 0 also writes counts and offsets.
-// Up to kFusedMaxTokens tokens, one workgroup of 16 waves does both steps in a single
-// launch (each wave owns a contiguous run of tokens; the scan runs between two barriers).
+// Up to kFusedMaxTokens tokens (and kFusedMaxSlots pairs), one workgroup of 16 waves does both steps in a
+// single launch from an LDS copy of topk_idx (each wave owns a contiguous run of tokens; the
+// scan runs between two barriers).
 #include "common.h"
 #include "internal.h"
 
@@ -22,26 +23,31 @@ namespace moe {
 
 namespace {
 
-constexpr int kChunk = 256;   // tokens per histogram / scatter workgroup
+// Tokens per histogram / scatter workgroup: a multiple of 64 chosen so that there are at
+// most 64 chunks (the scatter reads one column of the chunk table per lane).
+constexpr int kMaxChunks = 64;
+inline int chunk_tokens(int T) {
+  const int per = (T + kMaxChunks - 1) / kMaxChunks;
+  return per <= 64 ? 64 : (per + 63) & ~63;
+}
 
-__global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k,
+__global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k, int chunk,
                                                    const int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ chunk_hist) {
   __shared__ int h[64];
   if (threadIdx.x < 64) h[threadIdx.x] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kChunk + threadIdx.x;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // out-of-range ids are skipped
-    }
+  const int cbeg = blockIdx.x * chunk;
+  const int cend = min(T, cbeg + chunk);
+  for (int i = cbeg * k + threadIdx.x; i < cend * k; i += 256) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // out-of-range ids are skipped
   }
   __syncthreads();
   if (threadIdx.x < E) chunk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nchunks,
+__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nchunks, int chunk,
                                                      const int32_t* __restrict__ idx,
                                                      const float* __restrict__ topk_w,
                                                      const int32_t* __restrict__ chunk_hist,
@@ -79,8 +85,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
       if (lane == E - 1) offsets[E] = incl;
     }
   }
-  const int tbeg = blockIdx.x * kChunk;
-  const int tend = min(T, tbeg + kChunk);
+  const int tbeg = blockIdx.x * chunk;
+  const int tend = min(T, tbeg + chunk);
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int t0 = tbeg; t0 < tend; t0 += 64) {
     mask[lane] = 0ull;
@@ -111,13 +117,17 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
 }
 
 constexpr int kFusedWaves = 16;
-constexpr int kFusedMaxTokens = 1024;
+constexpr int kFusedMaxTokens = 1024;   // above this, one workgroup is slower than two launches
+constexpr int kFusedMaxSlots = 28672;   // T * k staged in LDS (112 KB)
 
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
 }
 
+// Up to kFusedMaxSlots (token, slot) pairs: one workgroup of 16 waves.  The whole topk_idx
+// array is first copied into LDS with every load in flight at once; histogram, scan and
+// scatter then read it from LDS.  Each wave owns a contiguous run of tokens.
 __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k,
                                                              const int32_t* __restrict__ idx,
                                                              const float* __restrict__ topk_w,
@@ -126,23 +136,29 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k
                                                              int32_t* __restrict__ perm_token,
                                                              int32_t* __restrict__ slot_pos,
                                                              float* __restrict__ perm_weight) {
+  __shared__ __align__(16) int sidx[kFusedMaxSlots];
   __shared__ int hist[kFusedWaves][64];
   __shared__ int run[kFusedWaves][64];
   __shared__ unsigned long long mask[kFusedWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int nslot = T * k;
+
+  // stage topk_idx (16-byte loads where the array allows, then the tail)
+  const int n4 = ((reinterpret_cast<uintptr_t>(idx) & 15) == 0) ? nslot / 4 : 0;
+  for (int i = threadIdx.x; i < n4; i += 1024)
+    reinterpret_cast<int4*>(sidx)[i] = reinterpret_cast<const int4*>(idx)[i];
+  for (int i = 4 * n4 + threadIdx.x; i < nslot; i += 1024) sidx[i] = idx[i];
+  hist[wave][lane] = 0;
+  __syncthreads();
+
   // tokens per wave: a multiple of 64 so that every scatter step is a full wave of tokens
   const int per = (((T + kFusedWaves - 1) / kFusedWaves) + 63) & ~63;
   const int tbeg = min(T, wave * per);
   const int tend = min(T, tbeg + per);
-
-  hist[wave][lane] = 0;
-  wave_lds_sync();
-  for (int t = tbeg + lane; t < tend; t += 64) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
-    }
+  for (int i = tbeg * k + lane; i < tend * k; i += 64) {
+    const int e = sidx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
   }
   __syncthreads();
   if (wave == 0) {
@@ -170,25 +186,33 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k
 
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int t0 = tbeg; t0 < tend; t0 += 64) {
-    mask[wave][lane] = 0ull;
-    wave_lds_sync();
     const int t = t0 + lane;
     const bool ok = t < tend;
+    float wv[8];
+    if (perm_weight != nullptr && ok) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) wv[j] = topk_w[(size_t)t * k + j];
+    }
+    mask[wave][lane] = 0ull;
+    wave_lds_sync();
     if (ok) {
       for (int j = 0; j < k; ++j) {
-        const int e = idx[(size_t)t * k + j];
+        const int e = sidx[t * k + j];
         if ((unsigned)e < (unsigned)E) atomicOr(&mask[wave][e], 1ull << lane);
       }
     }
     wave_lds_sync();
     if (ok) {
-      for (int j = 0; j < k; ++j) {
-        const int e = idx[(size_t)t * k + j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;
+        const int e = sidx[t * k + j];
         if ((unsigned)e >= (unsigned)E) continue;
         const int pos = run[wave][e] + __popcll(mask[wave][e] & below);
         perm_token[pos] = t;
         slot_pos[(size_t)t * k + j] = pos;
-        if (perm_weight != nullptr) perm_weight[pos] = topk_w[(size_t)t * k + j];
+        if (perm_weight != nullptr) perm_weight[pos] = wv[j];
       }
     }
     wave_lds_sync();
@@ -200,23 +224,25 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k
 }  // namespace
 
 size_t permute_ws_bytes(int T, int E) {
-  const size_t nchunks = (size_t)(T + kChunk - 1) / kChunk;
+  const size_t chunk = (size_t)chunk_tokens(T);
+  const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
   return nchunks * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* topk_w,
                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
                           int32_t* slot_pos, float* perm_weight, void* ws, hipStream_t s) {
-  if (T <= kFusedMaxTokens) {
+  if (T <= kFusedMaxTokens && (long long)T * k <= kFusedMaxSlots && k <= 8) {
     hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(1024), 0, s, T, E, k, idx, topk_w,
                        counts, offsets, perm_token, slot_pos, perm_weight);
     return hipGetLastError();
   }
-  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int chunk = chunk_tokens(T);
+  const int nchunks = (T + chunk - 1) / chunk;
   int32_t* chunk_hist = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, T, E, k, idx, chunk_hist);
-  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, nchunks, idx, topk_w,
-                     chunk_hist, counts, offsets, perm_token, slot_pos, perm_weight);
+  hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, T, E, k, chunk, idx, chunk_hist);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, nchunks, chunk, idx,
+                     topk_w, chunk_hist, counts, offsets, perm_token, slot_pos, perm_weight);
   return hipGetLastError();
 }
 
