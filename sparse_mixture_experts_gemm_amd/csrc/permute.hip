@@ -18,6 +18,7 @@
 // scan runs between two barriers).
 #include "common.h"
 #include "internal.h"
+#include "permute_core.h"
 
 namespace moe {
 
@@ -116,18 +117,12 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
   }
 }
 
-constexpr int kFusedWaves = 16;
 constexpr int kFusedMaxTokens = 1024;   // above this, one workgroup is slower than two launches
 constexpr int kFusedMaxSlots = 28672;   // T * k staged in LDS (112 KB)
 
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Up to kFusedMaxSlots (token, slot) pairs: one workgroup of 16 waves.  The whole topk_idx
-// array is first copied into LDS with every load in flight at once; histogram, scan and
-// scatter then read it from LDS.  Each wave owns a contiguous run of tokens.
+// Up to kFusedMaxTokens tokens: one workgroup of 16 waves.  The whole topk_idx array is
+// first copied into LDS with every load in flight at once; histogram, scan and scatter
+// then read it from LDS.  Each wave owns a contiguous run of tokens.
 __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k,
                                                              const int32_t* __restrict__ idx,
                                                              const float* __restrict__ topk_w,
@@ -137,88 +132,15 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k
                                                              int32_t* __restrict__ slot_pos,
                                                              float* __restrict__ perm_weight) {
   __shared__ __align__(16) int sidx[kFusedMaxSlots];
-  __shared__ int hist[kFusedWaves][64];
-  __shared__ int run[kFusedWaves][64];
-  __shared__ unsigned long long mask[kFusedWaves][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ PermuteLds pl;
   const int nslot = T * k;
-
   // stage topk_idx (16-byte loads where the array allows, then the tail)
   const int n4 = ((reinterpret_cast<uintptr_t>(idx) & 15) == 0) ? nslot / 4 : 0;
   for (int i = threadIdx.x; i < n4; i += 1024)
     reinterpret_cast<int4*>(sidx)[i] = reinterpret_cast<const int4*>(idx)[i];
   for (int i = 4 * n4 + threadIdx.x; i < nslot; i += 1024) sidx[i] = idx[i];
-  hist[wave][lane] = 0;
   __syncthreads();
-
-  // tokens per wave: a multiple of 64 so that every scatter step is a full wave of tokens
-  const int per = (((T + kFusedWaves - 1) / kFusedWaves) + 63) & ~63;
-  const int tbeg = min(T, wave * per);
-  const int tend = min(T, tbeg + per);
-  for (int i = tbeg * k + lane; i < tend * k; i += 64) {
-    const int e = sidx[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int e = lane;
-    int total = 0;
-    for (int w = 0; w < kFusedWaves; ++w) total += (e < E) ? hist[w][e] : 0;
-    int incl = total;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int v = __shfl_up(incl, o, 64);
-      if (e >= o) incl += v;
-    }
-    int at = incl - total;
-    if (e < E) {
-      counts[e] = total;
-      offsets[e] = at;
-      for (int w = 0; w < kFusedWaves; ++w) {
-        run[w][e] = at;
-        at += hist[w][e];
-      }
-    }
-    if (e == E - 1) offsets[E] = incl;
-  }
-  __syncthreads();
-
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int t0 = tbeg; t0 < tend; t0 += 64) {
-    const int t = t0 + lane;
-    const bool ok = t < tend;
-    float wv[8];
-    if (perm_weight != nullptr && ok) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) wv[j] = topk_w[(size_t)t * k + j];
-    }
-    mask[wave][lane] = 0ull;
-    wave_lds_sync();
-    if (ok) {
-      for (int j = 0; j < k; ++j) {
-        const int e = sidx[t * k + j];
-        if ((unsigned)e < (unsigned)E) atomicOr(&mask[wave][e], 1ull << lane);
-      }
-    }
-    wave_lds_sync();
-    if (ok) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        const int e = sidx[t * k + j];
-        if ((unsigned)e >= (unsigned)E) continue;
-        const int pos = run[wave][e] + __popcll(mask[wave][e] & below);
-        perm_token[pos] = t;
-        slot_pos[(size_t)t * k + j] = pos;
-        if (perm_weight != nullptr) perm_weight[pos] = wv[j];
-      }
-    }
-    wave_lds_sync();
-    if (lane < E) run[wave][lane] += __popcll(mask[wave][lane]);
-    wave_lds_sync();
-  }
+  permute_lds(T, E, k, sidx, topk_w, pl, counts, offsets, perm_token, slot_pos, perm_weight);
 }
 
 }  // namespace

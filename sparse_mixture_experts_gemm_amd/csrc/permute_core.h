@@ -1,0 +1,106 @@
+// Single-workgroup permutation of (token, slot) pairs whose expert ids are already in LDS.
+// Used by the small-batch permutation and by the small-batch route kernel, which selects
+// the experts itself and permutes in the same launch.  Order: expert ascending, then token
+// ascending (see permute.hip).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+constexpr int kPermWaves = 16;   // the workgroup is 16 waves (1024 threads)
+
+struct PermuteLds {
+  int hist[kPermWaves][64];
+  int run[kPermWaves][64];
+  unsigned long long mask[kPermWaves][64];
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// sidx: [T * k] expert ids in LDS; wsrc: [T * k] routing weights (LDS or global) or null.
+// Every thread of the workgroup must call it.  k <= 8, E <= 64.
+__device__ __forceinline__ void permute_lds(int T, int E, int k, const int* sidx,
+                                            const float* wsrc, PermuteLds& pl,
+                                            int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ perm_token,
+                                            int32_t* __restrict__ slot_pos,
+                                            float* __restrict__ perm_weight) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // tokens per wave: a multiple of 64 so that every scatter step is a full wave of tokens
+  const int per = (((T + kPermWaves - 1) / kPermWaves) + 63) & ~63;
+  const int tbeg = min(T, wave * per);
+  const int tend = min(T, tbeg + per);
+
+  pl.hist[wave][lane] = 0;
+  wave_lds_sync();
+  for (int i = tbeg * k + lane; i < tend * k; i += 64) {
+    const int e = sidx[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&pl.hist[wave][e], 1);   // out-of-range ids are skipped
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int e = lane;
+    int total = 0;
+    for (int w = 0; w < kPermWaves; ++w) total += (e < E) ? pl.hist[w][e] : 0;
+    int incl = total;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int v = __shfl_up(incl, o, 64);
+      if (e >= o) incl += v;
+    }
+    int at = incl - total;
+    if (e < E) {
+      counts[e] = total;
+      offsets[e] = at;
+      for (int w = 0; w < kPermWaves; ++w) {
+        pl.run[w][e] = at;
+        at += pl.hist[w][e];
+      }
+    }
+    if (e == E - 1) offsets[E] = incl;
+  }
+  __syncthreads();
+
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t0 = tbeg; t0 < tend; t0 += 64) {
+    const int t = t0 + lane;
+    const bool ok = t < tend;
+    float wv[8];
+    if (perm_weight != nullptr && ok) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) wv[j] = wsrc[(size_t)t * k + j];
+    }
+    pl.mask[wave][lane] = 0ull;
+    wave_lds_sync();
+    if (ok) {
+      for (int j = 0; j < k; ++j) {
+        const int e = sidx[t * k + j];
+        if ((unsigned)e < (unsigned)E) atomicOr(&pl.mask[wave][e], 1ull << lane);
+      }
+    }
+    wave_lds_sync();
+    if (ok) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;
+        const int e = sidx[t * k + j];
+        if ((unsigned)e >= (unsigned)E) continue;
+        const int pos = pl.run[wave][e] + __popcll(pl.mask[wave][e] & below);
+        perm_token[pos] = t;
+        slot_pos[(size_t)t * k + j] = pos;
+        if (perm_weight != nullptr) perm_weight[pos] = wv[j];
+      }
+    }
+    wave_lds_sync();
+    if (lane < E) pl.run[wave][lane] += __popcll(pl.mask[wave][lane]);
+    wave_lds_sync();
+  }
+}
+
+}  // namespace moe
