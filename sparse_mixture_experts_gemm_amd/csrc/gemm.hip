@@ -174,10 +174,9 @@ __device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
   }
 }
 
-// Tile shapes: dense segments (the shared experts: every token) use 256 x 256 tiles; the
-// routed segments (a few hundred rows per expert) use 128 x 256 tiles, which waste fewer
-// MFMA rows in each expert's last m-tile.  Eight waves (two per SIMD) per workgroup, so
-// one wave's LDS and barrier waits are covered by its partner's MFMAs.
+// Tile shapes: 256 x 256 when the problem gives every CU at least two such tiles, else
+// 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
+// are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
@@ -640,18 +639,19 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
   }
 }
 
-// Tile configuration per call, from what the host knows of the problem: dense segments
-// take 256 x 256 tiles when that still gives every CU at least two tiles; ragged routed
-// segments take 128 x 256 tiles.
+// Tile configuration per call, from what the host knows of the problem: 256 x 256 tiles
+// whenever that still gives every CU at least two tiles (measured faster than 128 x 256
+// tiles even for routed segments of ~400 rows, where a third of the last m-tile is
+// padding: the larger tile halves the L2 and LDS traffic per MFMA), else 128 x 256.
 // Each configuration is (BM, BN, waves, LDS stages, workgroups per CU).
-#ifndef MOE_CFG_ROUTED_UP
-#define MOE_CFG_ROUTED_UP 128, 256, 8, 3, 1
+#ifndef MOE_CFG_NARROW_UP
+#define MOE_CFG_NARROW_UP 128, 256, 8, 3, 1
 #endif
-#ifndef MOE_CFG_ROUTED_DOWN
-#define MOE_CFG_ROUTED_DOWN 128, 256, 8, 3, 1
+#ifndef MOE_CFG_NARROW_DOWN
+#define MOE_CFG_NARROW_DOWN 128, 256, 8, 3, 1
 #endif
-#ifndef MOE_CFG_DENSE_WIDE
-#define MOE_CFG_DENSE_WIDE 256, 256, 8, 2, 1
+#ifndef MOE_CFG_WIDE
+#define MOE_CFG_WIDE 256, 256, 8, 2, 1
 #endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
@@ -667,11 +667,11 @@ hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
   const bool swiglu = STAGE == 0 && ACT == MOE_ACT_SWIGLU;
   const long long bcols = swiglu ? 2LL * p.N : p.N;
   const long long wide_tiles = ((p.rows + 255) / 256) * ((bcols + 255) / 256);
-  if (p.offsets == nullptr && kWideOk && wide_tiles >= 2LL * num_cus) {
-    if constexpr (kWideOk) return launch_cfg<MOE_CFG_DENSE_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
+  if (kWideOk && wide_tiles >= 2LL * num_cus) {
+    if constexpr (kWideOk) return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
   }
-  if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_ROUTED_UP, STAGE, ACT, FP8>(p, num_cus, s);
-  else return launch_cfg<MOE_CFG_ROUTED_DOWN, STAGE, ACT, FP8>(p, num_cus, s);
+  if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_NARROW_UP, STAGE, ACT, FP8>(p, num_cus, s);
+  else return launch_cfg<MOE_CFG_NARROW_DOWN, STAGE, ACT, FP8>(p, num_cus, s);
 }
 
 template <int STAGE, int ACT>

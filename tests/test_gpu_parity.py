@@ -39,6 +39,8 @@ SMALL = {
     "multi_tile_swiglu": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256, seed=37),
     "multi_tile_relu2_e4m3": W.small_shape(T=8192, d=512, E=8, k=4, G=2, Gk=1, S=1, I=256,
                                            act="relu2", weight_dtype="e4m3", seed=38),
+    # enough rows for 256 x 256 tiles in the routed GEMMs
+    "multi_tile_wide": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512, seed=40),
     # K = 64: one K-slice per tile, several tiles per workgroup
     "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
 }
@@ -310,7 +312,8 @@ def test_grouped_gemm_down_routed(name):
     assert err <= TOL[s.act_dtype] * np.max(np.abs(ref)), err
 
 
-@pytest.mark.parametrize("name", ["multi_tile_swiglu", "multi_tile_relu2_e4m3", "short_k"])
+@pytest.mark.parametrize("name", ["multi_tile_swiglu", "multi_tile_relu2_e4m3", "short_k",
+                                  "multi_tile_wide"])
 def test_grouped_gemm_routed_every_row(name):
     """Up and down routed GEMMs with several tiles per workgroup, every output row checked."""
     s = shape_of(name)
