@@ -360,6 +360,11 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   const int col_in = lane & 31;    // token column of this lane in a 32 x 32 block
   const int fhalf = lane >> 5;     // which 16 features of a block this lane holds
   TileCoord tc = tile_at(0);
+  // rows of the segment left from this wave's first tile row (<= 0: all padding)
+  auto rows_of_wave = [&](const TileCoord& t) {
+    return __builtin_amdgcn_readfirstlane(t.rows - t.m_tile * BM - wm * WTM);
+  };
+  int wave_rows = rows_of_wave(tc);
   int j = 0, kt = 0, cst = 0;      // tile, k-slice and ring stage being multiplied
   int j3 = 0;                      // j mod 3
   for (int g = 0; g < nslices; ++g) {
@@ -408,17 +413,21 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         }
       }
     };
-    load_frags(0, af[0], bfr[0]);
-    __builtin_amdgcn_s_setprio(1);
+    // a wave whose rows of the tile are all past the end of the segment (the upper half
+    // of an expert's last 256-row tile) skips its LDS reads and MFMAs
+    if (wave_rows > 0) {
+      load_frags(0, af[0], bfr[0]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
-                                                                acc[fm][fn], 0, 0, 0);
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
+                                                                  acc[fm][fn], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -533,7 +542,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       ++j;
       j3 = j3 == 2 ? 0 : j3 + 1;
       kt = 0;
-      if (j < ntiles) tc = tile_at(j);
+      if (j < ntiles) {
+        tc = tile_at(j);
+        wave_rows = rows_of_wave(tc);
+      }
     } else {
       ++kt;
       // slice g + 1 must have landed; younger slices may stay in flight
