@@ -46,6 +46,13 @@ design notes):
 * ReLU^2 expert: W2 (max(W1 x, 0))^2, no gate/up pair.
 * e4m3 expert weights: W[n, :] = scale[n] * e4m3(code[n, :]) (OCP e4m3, bias 7, max 448,
   0x7F/0xFF NaN); activations stay bf16.
+* Selection-only expert bias b_e (the aux-loss-free balancing of [MoE-Eng] "负载均衡"):
+  the selection compares the scores of l + b (sigmoid or softmax of the biased logits);
+  the weights are the unbiased scores of the selected experts, renormalised.
+* Load statistics: f_e counts routed (token, slot) assignments before any capacity drop,
+  divided by T k; p_e averages each token's scores normalised to sum 1 over the E experts.
+* Capacity: floor(c T k / E) rows per expert; each expert keeps its rows in token order
+  and drops the rest (dropped slots contribute zero; weights are not renormalised).
 """
 from __future__ import annotations
 
@@ -58,6 +65,7 @@ __all__ = [
     "group_scores", "select_experts", "routing_weights", "route", "silu", "expert_ffn",
     "expert_up", "expert_down", "combine",
     "moe_forward", "permute", "expert_weights", "shared_weights", "decode_act",
+    "selection_keys", "load_stats", "expert_capacity",
 ]
 
 
@@ -166,18 +174,50 @@ def routing_weights(scores64, idx, renormalize: bool = True, route_scale: float 
     return sel * route_scale
 
 
-def route(layer, tokens=None):
-    """Router of a stored layer: returns dict(logits, scores, idx, w) in fp64 (idx int32).
+def selection_keys(logits, fn: str, select_bias=None) -> np.ndarray:
+    """The values the expert selection compares.  Without a selection bias these are the
+    gate scores; with one, the scores of the biased logits l + b_e.  [MoE-Eng] section
+    "MoE 数学：路由、容量与平衡详解" (and "负载均衡"): the per-expert bias b_e enters the
+    gate logits for the assignment only; the weights keep coming from the unbiased
+    scores."""
+    l = np.asarray(logits, np.float64)
+    if select_bias is not None:
+        l = l + np.asarray(select_bias, np.float64)[None, :]
+    return gate_scores(l, fn)
 
-    The selection is decided on the fp32-rounded scores (group sums in fp32)."""
+
+def route(layer, tokens=None):
+    """Router of a stored layer: returns dict(logits, scores, keys, idx, w) in fp64 (idx
+    int32).  The selection is decided on the fp32-rounded selection keys (group sums in
+    fp32); the weights use the unbiased fp64 scores."""
     s = layer.shape
     x = decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
     w_r = decode_act(layer.router, s.act_dtype)
     l = router_logits(x, w_r, layer.logit_bias)
     sc = gate_scores(l, s.score)
-    idx = select_experts(sc.astype(np.float32), s.k, s.G, s.Gk, s.n_g)
+    sb = getattr(layer, "select_bias", None)
+    keys = sc if sb is None else selection_keys(l, s.score, sb)
+    idx = select_experts(keys.astype(np.float32), s.k, s.G, s.Gk, s.n_g)
     w = routing_weights(sc, idx, s.renormalize, s.route_scale)
-    return {"x": x, "logits": l, "scores": sc, "idx": idx, "w": w}
+    return {"x": x, "logits": l, "scores": sc, "keys": keys, "idx": idx, "w": w}
+
+
+# ----------------------------------------------------------------------------- load statistics
+def load_stats(scores, idx, E: int, alpha: float = 1.0):
+    """Per-batch load statistics of the router and the Switch auxiliary-loss value.
+
+    [MoE-Eng] section "负载均衡": loss = alpha * E * sum_e f_e p_e, with f_e the fraction of
+    the routed (token, slot) assignments that went to expert e and p_e its mean routing
+    probability.  The probability of expert e for token t is its gate score divided by the
+    token's sum over all E experts (the softmax itself for softmax gating; the normalised
+    sigmoid scores otherwise).  Returns (f [E], p [E], loss)."""
+    sc = np.asarray(scores, np.float64)
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    f = np.bincount(idx.reshape(-1), minlength=E).astype(np.float64) / float(T * k)
+    prob = sc / sc.sum(axis=1, keepdims=True)
+    p = prob.mean(axis=0)
+    return f, p, float(alpha * E * np.sum(f * p))
 
 
 # ----------------------------------------------------------------------------- experts
@@ -210,10 +250,11 @@ def expert_ffn(x, w1, w3, w2, act: str):
 
 def combine(y_perm, slot_pos, y_shared, k: int):
     """out[t] = sum_j y_perm[slot_pos[t*k + j]] (+ y_shared[t]): the merge of the k weighted
-    expert outputs of every token back into token order."""
+    expert outputs of every token back into token order (slots dropped by a capacity limit,
+    slot_pos -1, contribute nothing)."""
     y = np.asarray(y_perm, np.float64)
     sp = np.asarray(slot_pos, np.int64).reshape(-1, k)
-    out = y[sp].sum(axis=1)
+    out = np.where((sp >= 0)[..., None], y[np.maximum(sp, 0)], 0.0).sum(axis=1)
     if y_shared is not None:
         out = out + np.asarray(y_shared, np.float64)
     return out
@@ -244,13 +285,24 @@ def moe_forward(layer, tokens=None):
 
     The masked per-(slot, expert) loop of the MoEBlock listing, with the slot loop folded
     into the mask: for each expert, the tokens that picked it in any slot.  ``tokens``
-    restricts the computation to a subset of rows (every step is per token)."""
+    restricts the computation to a subset of rows (every step is per token).  With a
+    capacity factor, slots dropped by the capacity limit contribute nothing; which slots
+    are dropped depends on the whole batch, so the routing of all tokens decides it."""
     s = layer.shape
     r = route(layer, tokens)
     x, idx, w = r["x"], r["idx"], r["w"]
+    kept = np.ones(idx.shape, dtype=bool)
+    cf = getattr(s, "capacity_factor", None)
+    if cf is not None:
+        full = r if tokens is None else route(layer)
+        cap = expert_capacity(s.T, s.k, s.E, cf)
+        _, _, _, slot_pos = permute(full["idx"], s.E, cap)
+        kept_all = slot_pos.reshape(s.T, s.k) >= 0
+        kept = kept_all if tokens is None else kept_all[np.asarray(tokens)]
+    r["kept"] = kept
     out = np.zeros_like(x)
     for e in range(s.E):
-        rows, slots = np.nonzero(idx == e)
+        rows, slots = np.nonzero((idx == e) & kept)
         if rows.size == 0:
             continue
         w1, w3, w2 = expert_weights(layer, e)
@@ -263,19 +315,34 @@ def moe_forward(layer, tokens=None):
 
 
 # ----------------------------------------------------------------------------- permutation
-def permute(idx, E: int):
+def expert_capacity(T: int, k: int, E: int, factor: float) -> int:
+    """Rows an expert may take in one batch: floor(c * T * k / E).  [MoE-Eng] section
+    "MoE 数学：路由、容量与平衡详解" gives the capacity c |T| k / E; a row count is an
+    integer, and the reading taken is to round down."""
+    return int(math.floor(factor * T * k / E))
+
+
+def permute(idx, E: int, capacity=None):
     """Rows grouped by expert: order of (expert asc, token asc) over all (t, j) slots.
 
-    Returns counts [E], offsets [E+1] (exclusive scan of counts), perm_token [T*k]
-    (token of permuted row p) and slot_pos [T*k] (permuted row of slot t*k + j)."""
+    Returns counts [E], offsets [E+1] (exclusive scan of counts), perm_token [rows]
+    (token of permuted row p) and slot_pos [T*k] (permuted row of slot t*k + j).  With a
+    capacity, each expert keeps its first ``capacity`` slots in that order (the tokens
+    beyond it are dropped: they bypass the expert and contribute nothing, [MoE-Eng]
+    section "MoE 数学：路由、容量与平衡详解"); counts are the kept rows and dropped slots
+    have slot_pos -1."""
     idx = np.asarray(idx, dtype=np.int64)
     T, k = idx.shape
     e_flat = idx.reshape(-1)
     t_flat = np.repeat(np.arange(T), k)
     order = np.lexsort((t_flat, e_flat))            # stable: expert, then token
-    counts = np.bincount(e_flat, minlength=E).astype(np.int32)
+    routed = np.bincount(e_flat, minlength=E)
+    start = np.concatenate([[0], np.cumsum(routed)])
+    rank = np.arange(T * k) - start[e_flat[order]]    # position inside the expert's run
+    keep = np.ones(T * k, dtype=bool) if capacity is None else rank < capacity
+    counts = np.minimum(routed, capacity if capacity is not None else routed).astype(np.int32)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    perm_token = t_flat[order].astype(np.int32)
-    slot_pos = np.empty(T * k, dtype=np.int32)
-    slot_pos[order] = np.arange(T * k, dtype=np.int32)
+    perm_token = t_flat[order][keep].astype(np.int32)
+    slot_pos = np.full(T * k, -1, dtype=np.int32)
+    slot_pos[order[keep]] = np.arange(int(keep.sum()), dtype=np.int32)
     return counts, offsets, perm_token, slot_pos

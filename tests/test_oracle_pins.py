@@ -386,6 +386,176 @@ def test_permute_empty_experts_and_single_token():
     assert perm_token.tolist() == [0, 0] and slot_pos.tolist() == [1, 0]
 
 
+# ----------------------------------------------------------------------------- selection bias
+def _with_bias(lay, b):
+    lay.select_bias = None if b is None else np.asarray(b, np.float32)
+    return lay
+
+
+def test_zero_selection_bias_is_the_unbiased_router():
+    lay = f32layer(E=8, k=3, G=4, Gk=2, T=40, d=6, score="sigmoid")
+    ref = O.route(lay)
+    got = O.route(_with_bias(lay, np.zeros(8)))
+    assert np.array_equal(ref["idx"], got["idx"]) and np.array_equal(ref["w"], got["w"])
+
+
+@pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+def test_large_selection_bias_forces_the_biased_experts(score):
+    """A bias far above every logit makes those experts the selection of every token, while
+    the weights stay the renormalised UNBIASED scores of the selected experts."""
+    lay = f32layer(E=8, k=3, T=30, d=6, score=score)
+    b = np.zeros(8)
+    chosen = [1, 4, 6]
+    b[chosen] = 60.0
+    r = O.route(_with_bias(lay, b))
+    for t in range(30):
+        assert sorted(r["idx"][t].tolist()) == chosen
+        xr = lay.x[t].astype(np.float64).tolist()
+        logits = [math.fsum(xr[c] * float(lay.router[e, c]) for c in range(6)) for e in range(8)]
+        if score == "sigmoid":
+            sc = [1.0 / (1.0 + math.exp(-v)) for v in logits]
+        else:
+            m = max(logits)
+            z = [math.exp(v - m) for v in logits]
+            sc = [v / math.fsum(z) for v in z]
+        tot = math.fsum(sc[e] for e in chosen)
+        for j in range(3):
+            assert abs(r["w"][t, j] - sc[int(r["idx"][t, j])] / tot) < 1e-12
+
+
+def test_selection_bias_brute_force_with_groups():
+    """Selection on sigma(l + b) from the definition (brute force over group and expert
+    subsets), weights from sigma(l)."""
+    lay = f32layer(E=8, k=3, G=4, Gk=2, n_g=2, T=12, d=5, score="sigmoid")
+    rng = np.random.default_rng(41)
+    b = rng.standard_normal(8)
+    r = O.route(_with_bias(lay, b))
+    b32 = np.asarray(b, np.float32).astype(np.float64)
+    for t in range(12):
+        xr = lay.x[t].astype(np.float64).tolist()
+        logits = [math.fsum(xr[c] * float(lay.router[e, c]) for c in range(5)) for e in range(8)]
+        keys = np.array([1.0 / (1.0 + math.exp(-(logits[e] + b32[e]))) for e in range(8)], np.float32)
+        if len(set(keys.tolist())) < 8:
+            continue
+        sel = _bf_select(keys, 3, 4, 2, 2)
+        assert r["idx"][t].tolist() == sel
+        sc = [1.0 / (1.0 + math.exp(-v)) for v in logits]
+        tot = math.fsum(sc[e] for e in sel)
+        assert np.allclose(r["w"][t], [sc[e] / tot for e in sel], rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+def test_common_shift_of_the_selection_bias_changes_nothing(score):
+    """Without groups the selection is a ranking of l + b: adding one constant to every b_e
+    leaves it unchanged (sigmoid and softmax are monotone in each logit)."""
+    lay = f32layer(E=8, k=2, T=50, d=6, score=score)
+    rng = np.random.default_rng(42)
+    b = rng.standard_normal(8) * 0.5
+    a = O.route(_with_bias(lay, b))["idx"]
+    c = O.route(_with_bias(lay, b + 0.75))["idx"]
+    assert np.array_equal(a, c)
+
+
+# ----------------------------------------------------------------------------- load statistics
+def test_load_stats_uniform_routing_gives_alpha():
+    """[MoE-Eng] "负载均衡": the loss is minimal, alpha * E * E * (1/E)^2 = alpha, when every
+    f_e = p_e = 1/E."""
+    E = 4
+    idx = np.arange(E, dtype=np.int32)[:, None]
+    scores = np.full((E, E), 0.3)
+    f, p, loss = O.load_stats(scores, idx, E, alpha=0.01)
+    assert np.allclose(f, 0.25) and np.allclose(p, 0.25)
+    assert abs(loss - 0.01) < 1e-15
+
+
+def test_load_stats_hand_examples():
+    # softmax probabilities, both tokens to expert 0: f = [1, 0], p = [0.75, 0.25]
+    f, p, loss = O.load_stats(np.array([[0.9, 0.1], [0.6, 0.4]]), np.array([[0], [0]]), 2, 1.0)
+    assert f.tolist() == [1.0, 0.0] and np.allclose(p, [0.75, 0.25]) and abs(loss - 1.5) < 1e-15
+    # sigmoid scores are normalised per token: [0.75, 0.25] and [0.5, 0.5]
+    f, p, loss = O.load_stats(np.array([[0.9, 0.3], [0.2, 0.2]]), np.array([[0], [1]]), 2, 2.0)
+    assert f.tolist() == [0.5, 0.5] and np.allclose(p, [0.625, 0.375]) and abs(loss - 2.0) < 1e-15
+    # top-2 of 3 experts: f counts assignments over T * k
+    f, _, _ = O.load_stats(np.ones((2, 3)), np.array([[0, 1], [0, 2]]), 3, 1.0)
+    assert f.tolist() == [0.5, 0.25, 0.25]
+
+
+def test_load_stats_fractions_sum_to_one():
+    lay = f32layer(E=8, k=3, G=4, Gk=2, T=60, d=6, score="sigmoid")
+    r = O.route(lay)
+    f, p, loss = O.load_stats(r["scores"], r["idx"], 8, 0.5)
+    assert abs(f.sum() - 1.0) < 1e-14 and abs(p.sum() - 1.0) < 1e-14 and loss > 0
+
+
+# ----------------------------------------------------------------------------- capacity
+def test_expert_capacity_values():
+    assert O.expert_capacity(4096, 6, 64, 1.25) == 480
+    assert O.expert_capacity(10, 1, 3, 1.0) == 3         # 3.33 rounds down
+    assert O.expert_capacity(4, 1, 2, 1.0) == 2
+
+
+def test_capacity_hand_example():
+    idx = np.array([[0], [0], [0], [1]], dtype=np.int32)
+    counts, offsets, perm_token, slot_pos = O.permute(idx, 2, capacity=2)
+    assert counts.tolist() == [2, 1] and offsets.tolist() == [0, 2, 3]
+    assert perm_token.tolist() == [0, 1, 3] and slot_pos.tolist() == [0, 1, -1, 2]
+
+
+def test_capacity_keeps_each_experts_first_tokens_python_sorted():
+    rng = np.random.default_rng(43)
+    s = rng.random((53, 8)).astype(np.float32)
+    idx = O.select_experts(s, 3, 1, 1, 1)
+    for cap in (0, 1, 7, 19, 1000):
+        counts, offsets, perm_token, slot_pos = O.permute(idx, 8, capacity=cap)
+        pairs = sorted((int(idx[t, j]), t, j) for t in range(53) for j in range(3))
+        kept, seen = [], {}
+        for e, t, j in pairs:
+            seen[e] = seen.get(e, 0) + 1
+            if seen[e] <= cap:
+                kept.append((e, t, j))
+        assert perm_token.tolist() == [t for (_, t, _) in kept]
+        assert [slot_pos[t * 3 + j] for (_, t, j) in kept] == list(range(len(kept)))
+        dropped = set((t, j) for (_, t, j) in pairs) - set((t, j) for (_, t, j) in kept)
+        assert all(slot_pos[t * 3 + j] == -1 for (t, j) in dropped)
+        assert counts.tolist() == [min(cap, sum(1 for p in pairs if p[0] == e)) for e in range(8)]
+    unlimited = O.permute(idx, 8)
+    large = O.permute(idx, 8, capacity=10 ** 6)
+    assert all(np.array_equal(a, b) for a, b in zip(unlimited, large))
+
+
+def test_forward_with_capacity_brute_force():
+    """Dropped slots contribute nothing: brute force per token over the kept slots."""
+    shape = W.small_shape(act_dtype="f32", weight_dtype="f32", T=6, d=5, E=4, k=2, S=1, I=3,
+                          G=1, Gk=1, score="softmax", capacity_factor=0.5)
+    lay = W.make_layer(shape, cache=False)
+    r = O.moe_forward(lay)
+    cap = O.expert_capacity(6, 2, 4, 0.5)
+    assert cap == 1
+    pairs = sorted((int(r["idx"][t, j]), t, j) for t in range(6) for j in range(2))
+    kept, seen = set(), {}
+    for e, t, j in pairs:
+        seen[e] = seen.get(e, 0) + 1
+        if seen[e] <= cap:
+            kept.add((t, j))
+    assert r["kept"].sum() == len(kept)
+    for t in range(6):
+        xr = lay.x[t].astype(np.float64).tolist()
+        ref = np.array(_bf_ffn(xr, lay.sh_gate[0].astype(np.float64).tolist(),
+                               lay.sh_up[0].astype(np.float64).tolist(),
+                               lay.sh_down[0].astype(np.float64).tolist(), "swiglu"))
+        for j in range(2):
+            if (t, j) not in kept:
+                continue
+            e = int(r["idx"][t, j])
+            ref = ref + r["w"][t, j] * np.array(_bf_ffn(xr, lay.w_gate[e].astype(np.float64).tolist(),
+                                                        lay.w_up[e].astype(np.float64).tolist(),
+                                                        lay.w_down[e].astype(np.float64).tolist(), "swiglu"))
+        assert np.allclose(r["out"][t], ref, rtol=1e-11, atol=1e-12)
+    # a subset of tokens sees the same drops as the whole batch
+    sub = O.moe_forward(lay, tokens=np.array([4, 1]))
+    assert np.allclose(sub["out"], r["out"][[4, 1]], rtol=1e-13, atol=0)
+
+
 # ----------------------------------------------------------------------------- workloads
 def test_fusionllm_shapes_match_the_yaml():
     y = json.load(open(os.path.join(GOLDEN, "fusionllm_moe_yaml.json")))
@@ -421,7 +591,8 @@ def _swapped_ffn(x, w1, w3, w2, act):
 
 
 @pytest.mark.parametrize("mutation", ["swap_gate_up", "no_renorm", "tie_high_index",
-                                      "token_desc_perm", "drop_shared", "transpose_down"])
+                                      "token_desc_perm", "drop_shared", "transpose_down",
+                                      "biased_weights", "keep_last_at_capacity"])
 def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
     """Each mutation is a plausible slip in the oracle; the named pin must then fail."""
     if mutation == "swap_gate_up":
@@ -455,6 +626,28 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
             return c, o, pt, sp
         monkeypatch.setattr(O, "permute", bad)
         check = test_permute_matches_python_sorted
+    elif mutation == "biased_weights":
+        # weights taken from the biased selection keys instead of the unbiased scores
+        orig_route = O.moe_oracle.route
+        def bad_route(layer, tokens=None):
+            r = orig_route(layer, tokens)
+            s = layer.shape
+            r["w"] = O.moe_oracle.routing_weights(r["keys"], r["idx"], s.renormalize, s.route_scale)
+            return r
+        monkeypatch.setattr(O, "route", bad_route)
+        check = lambda: test_large_selection_bias_forces_the_biased_experts("sigmoid")
+    elif mutation == "keep_last_at_capacity":
+        orig_perm = O.permute
+        def bad(idx, E, capacity=None):
+            if capacity is None:
+                return orig_perm(idx, E)
+            idx = np.asarray(idx)
+            T, k = idx.shape
+            rev = orig_perm(idx[::-1], E, capacity)     # keeps the LAST tokens of each expert
+            sp = rev[3].reshape(T, k)[::-1].reshape(-1)
+            return rev[0], rev[1], (T - 1 - rev[2]).astype(np.int32), sp
+        monkeypatch.setattr(O, "permute", bad)
+        check = test_capacity_keeps_each_experts_first_tokens_python_sorted
     elif mutation == "drop_shared":
         monkeypatch.setattr(O.moe_oracle, "shared_weights",
                             lambda lay, i: tuple(np.zeros_like(a) if a is not None else None

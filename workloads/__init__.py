@@ -56,6 +56,8 @@ class MoeShape:
     renormalize: bool = True
     route_scale: float = 1.0
     x_from: Optional[str] = None     # take x rows (and weights) of another shape
+    capacity_factor: Optional[float] = None   # expert capacity c*T*k/E (None: unlimited)
+    select_bias_std: Optional[float] = None   # selection-only per-expert bias ~ N(0, std^2)
 
     @property
     def flops_per_token(self) -> int:
@@ -84,8 +86,13 @@ SHAPES = {
     "fp8_relu2": MoeShape("fp8_relu2", T=16384, d=2048, E=64, k=6, score="sigmoid", G=8,
                           Gk=4, S=4, I=1536, act="relu2", act_dtype="bf16",
                           weight_dtype="e4m3", seed=4),
+    # the prefill layer with a selection-only expert bias and capacity factor 1.25
+    "balance_bf16": MoeShape("balance_bf16", T=4096, d=2048, E=64, k=6, score="sigmoid", G=8,
+                             Gk=4, S=4, I=1536, act="swiglu", act_dtype="bf16",
+                             weight_dtype="bf16", seed=1, x_from="fusionllm_bf16",
+                             capacity_factor=1.25, select_bias_std=0.5),
 }
-ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2"]
+ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2", "balance_bf16"]
 
 
 def shape_by_name(name: str) -> MoeShape:
@@ -155,6 +162,7 @@ class Layer:
     sh_s_gate: Optional[np.ndarray] = None
     sh_s_up: Optional[np.ndarray] = None
     sh_s_down: Optional[np.ndarray] = None
+    select_bias: Optional[np.ndarray] = None   # [E] fp32, selection only
     extra: dict = field(default_factory=dict)
 
 
@@ -179,6 +187,15 @@ def _normal(seed_seq, shape, std):
 _CACHE: dict = {}
 
 
+def _select_bias(s: MoeShape):
+    """Selection-only expert bias of a shape: its own seeded stream (independent of the
+    weight streams, so shapes that share weights can differ in bias)."""
+    if s.select_bias_std is None:
+        return None
+    st = np.random.SeedSequence([s.seed, 0x5E1EC7])
+    return _normal(st, (s.E,), s.select_bias_std).astype(np.float32)
+
+
 def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> Layer:
     """Build the seeded layer (inputs + weights) of a shape."""
     if isinstance(shape, str):
@@ -188,6 +205,7 @@ def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> L
         lay = Layer(**{**base.__dict__})
         lay.shape = shape
         lay.x = base.x[: shape.T].copy()
+        lay.select_bias = _select_bias(shape)
         return lay
     if cache and shape.name in _CACHE:
         return _CACHE[shape.name]
@@ -265,7 +283,8 @@ def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> L
                 sh_up=mats[("shared", "up")], sh_down=mats[("shared", "down")],
                 s_gate=scales[("routed", "gate")], s_up=scales[("routed", "up")],
                 s_down=scales[("routed", "down")], sh_s_gate=scales[("shared", "gate")],
-                sh_s_up=scales[("shared", "up")], sh_s_down=scales[("shared", "down")])
+                sh_s_up=scales[("shared", "up")], sh_s_down=scales[("shared", "down")],
+                select_bias=_select_bias(s))
     if cache:
         _CACHE[shape.name] = lay
     return lay
