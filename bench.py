@@ -71,11 +71,17 @@ class Runner:
         self.cfg = moe.make_config(s.T, s.d, s.E, s.k, G=s.G, Gk=s.Gk, n_g=s.n_g, S=s.S, I=s.I,
                                    score=s.score, renormalize=s.renormalize,
                                    route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
-                                   weight_dtype=s.weight_dtype)
+                                   weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor)
+        names = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                 "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]
         if weights is None:
-            t = {n: to_dev(getattr(lay, n)) for n in
-                 ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-                  "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]}
+            t = {n: to_dev(getattr(lay, n)) for n in names}
+            t["select_bias"] = to_dev(lay.select_bias)
+            weights = moe.Weights(**t)
+        elif lay.select_bias is not None:
+            # the same device weights with this layer's selection bias
+            t = dict(weights.tensors)
+            t["select_bias"] = to_dev(lay.select_bias)
             weights = moe.Weights(**t)
         self.w = weights
         self.x = to_dev(lay.x)
@@ -92,17 +98,17 @@ class Runner:
         off = al(s.T * s.k * 4) * 2
         return self.ws[off: off + 4 * s.E].view(self.torch.int32).cpu().numpy()
 
-    def timed(self, steps, warmup):
+    def timed(self, steps, warmup, load_stats=None):
         """K plain forwards bracketed by one event pair (the headline step time)."""
         torch = self.torch
         for _ in range(warmup):
-            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws, load_stats=load_stats)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record()
         for _ in range(steps):
-            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws, load_stats=load_stats)
         b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -226,6 +232,7 @@ def main(argv=None):
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-balance", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
@@ -303,6 +310,22 @@ def main(argv=None):
                                           f"traffic_decode_up_{dshape.name}.txt", DECODE_SOURCES),
                                       "kernel_ms": d_up_ms,
                                       "algorithmic_bytes": up_bytes}}
+    if not args.no_balance and shape.name == "fusionllm_bf16":
+        # the same layer with a selection-only expert bias, capacity factor 1.25 and the
+        # load statistics written by every step
+        bshape = W.SHAPES["balance_bf16"]
+        blay = W.make_layer(bshape)
+        brun = Runner(bshape, blay, weights=run.w)
+        st = torch.empty(2 * bshape.E + 1, dtype=torch.float32, device="cuda")
+        b_ms, _ = brun.timed(args.steps, args.warmup, load_stats=st)
+        counts = brun.counts()
+        stv = st.cpu().numpy()
+        res["balance"] = {"workload": bshape.name, "capacity_factor": bshape.capacity_factor,
+                          "select_bias": f"N(0, {bshape.select_bias_std}^2) per expert",
+                          "ms_per_step": b_ms, "tokens_per_s": bshape.T / (b_ms * 1e-3),
+                          "rows_kept_frac": float(counts.sum()) / (bshape.T * bshape.k),
+                          "aux_loss_alpha1": float(stv[2 * bshape.E]),
+                          "max_f_over_mean": float(stv[:bshape.E].max() * bshape.E)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_tokens, shape.T), args.cpu_seconds)
     print(json.dumps(res))

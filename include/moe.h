@@ -73,6 +73,11 @@ typedef struct {
   moe_act act;               /* SwiGLU (gate, up, down) or ReLU^2 (gate, down)           */
   moe_dtype act_dtype;       /* MOE_F32 or MOE_BF16                                      */
   moe_dtype weight_dtype;    /* MOE_F32, MOE_BF16 or MOE_FP8_E4M3                        */
+  float capacity_factor;     /* c > 0: each expert takes at most floor(c*T*k/E) rows per
+                                batch, in token order, and drops the rest (the dropped slots
+                                contribute nothing); c <= 0: unlimited (no dropping).
+                                Source: expert capacity c|T|k/E and token dropping, section
+                                "MoE 数学：路由、容量与平衡详解" of "大模型工程（一）"   */
 } moe_config;
 
 /* Expert weights.  [out, in] per expert, stacked on dim 0.  e4m3 weights carry one fp32
@@ -92,39 +97,61 @@ typedef struct {
   const float* sh_s_gate;    /* [S, I]                                                     */
   const float* sh_s_up;      /* [S, I]                                                     */
   const float* sh_s_down;    /* [S, d]                                                     */
+  const float* select_bias;  /* [E] selection-only expert bias, or NULL (see moe_route)     */
 } moe_weights;
 
 /* Bytes of device workspace moe_forward needs for this config (host only, no HIP call).
- * moe_permute and moe_grouped_gemm need at most the same amount. */
+ * moe_permute, moe_load_stats and moe_grouped_gemm need at most the same amount. */
 moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Router, scoring and group-limited top-k for T tokens.
  *   l[t,e] = sum_c x[t,c] router[e,c] (+ logit_bias[e]), fp32 accumulation;
  *   s = sigmoid(l) or softmax over e;
- *   groups g = experts [g*E/G, (g+1)*E/G); group score = sum of its n_g largest s;
+ *   selection keys: s, or with a selection bias the scores of l + select_bias (sigmoid,
+ *   or softmax over e, of the biased logits);
+ *   groups g = experts [g*E/G, (g+1)*E/G); group score = sum of its n_g largest keys;
  *   keep the Gk best groups (ties: lower group index), then the k best experts of the
- *   kept groups (ties: lower expert index), slot order score-descending;
- *   w_j = route_scale * s_j / sum_i s_i (or route_scale * s_j without renormalisation).
- * x [T, d] act_dtype; router [E, d] act_dtype; scores [T, E] fp32 (optional, NULL = not
- * written); topk_idx [T, k] int32; topk_w [T, k] fp32.
+ *   kept groups by key (ties: lower expert index), slot order key-descending;
+ *   w_j = route_scale * s_j / sum_i s_i (or route_scale * s_j without renormalisation),
+ *   always from the unbiased scores s.
+ * x [T, d] act_dtype; router [E, d] act_dtype; logit_bias, select_bias [E] fp32 or NULL;
+ * scores [T, E] fp32 (optional, NULL = not written; the unbiased s); topk_idx [T, k]
+ * int32; topk_w [T, k] fp32.
  * Source: the MoEBlock listing and section "MoE 数学：路由、容量与平衡详解" of
- * "大模型工程（一）：Transformer 到 MoE"; group-limited sigmoid gating in section
- * "混合专家（MoE）" of the FusionLLM training-framework page. */
+ * "大模型工程（一）：Transformer 到 MoE" (the selection-only bias b_e: its sections
+ * "负载均衡" and "MoE 数学"); group-limited sigmoid gating in section "混合专家（MoE）" of
+ * the FusionLLM training-framework page. */
 moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
-                     const float* logit_bias, float* scores, int32_t* topk_idx,
-                     float* topk_w, hipStream_t stream);
+                     const float* logit_bias, const float* select_bias, float* scores,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
-/* The selection step of moe_route alone, on given fp32 scores [T, E] (every score must be
- * finite and >= 0, as sigmoid and softmax values are).  Same outputs and tie rules. */
-moe_status moe_select(const moe_config* cfg, const float* scores, int32_t* topk_idx,
-                      float* topk_w, hipStream_t stream);
+/* The selection step of moe_route alone, on given fp32 scores [T, E] and optional
+ * selection keys [T, E] (NULL: the scores are the keys).  Every value must be finite and
+ * >= 0, as sigmoid and softmax values are.  Same outputs and tie rules. */
+moe_status moe_select(const moe_config* cfg, const float* scores, const float* keys,
+                      int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Load statistics of one batch and the Switch auxiliary-loss value:
+ *   f[e] = (number of (t, j) with topk_idx[t, j] = e) / (T*k)   (routed, before capacity)
+ *   p[e] = (1/T) sum_t scores[t, e] / sum_e' scores[t, e']     (mean routing probability)
+ *   loss[0] = alpha * E * sum_e f[e] p[e]
+ * scores [T, E] fp32 (the unbiased scores, as moe_route writes them), topk_idx [T, k];
+ * f, p [E] and loss [1] fp32.  Sums are taken in a fixed order (deterministic).  ws: at
+ * least moe_workspace_size bytes (per-chunk partial sums).
+ * Source: the auxiliary loss alpha E sum f_e p_e and its terms, sections "负载均衡" and
+ * "MoE 数学：路由、容量与平衡详解" of "大模型工程（一）：Transformer 到 MoE". */
+moe_status moe_load_stats(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                          float alpha, float* f, float* p, float* loss, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 /* Expert-sorted permutation of the T*k (token, slot) pairs: rows ordered by
- * (expert ascending, token ascending); deterministic.
- *   counts[e]      number of slots routed to expert e                    [E]
- *   offsets[e]     exclusive prefix sum of counts; offsets[E] = T*k       [E+1]
+ * (expert ascending, token ascending); deterministic.  With cfg->capacity_factor > 0 each
+ * expert keeps only its first floor(c*T*k/E) slots in that order (computed in double
+ * from the fp32 factor) and the others are dropped.
+ *   counts[e]      number of rows of expert e (slots kept)               [E]
+ *   offsets[e]     exclusive prefix sum of counts (offsets[E] = rows)    [E+1]
  *   perm_token[p]  token of permuted row p                               [T*k]
- *   slot_pos[t*k+j] permuted row of slot j of token t                    [T*k]
+ *   slot_pos[t*k+j] permuted row of slot j of token t, -1 when dropped   [T*k]
  *   perm_weight[p] topk_w of permuted row p (optional: both topk_w and perm_weight
  *                  NULL, or both set)                                    [T*k]
  * All int32/fp32 device buffers.  ws: at least moe_workspace_size bytes.  Every row of
@@ -161,7 +188,8 @@ moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_s
                             void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* out[t] = sum_{j<k} y_perm[slot_pos[t*k+j]] + y_shared[t], summed in that fixed order in
- * fp32, rounded to act_dtype.  y_perm [T*k, d], y_shared [T, d] or NULL, out [T, d].
+ * fp32, rounded to act_dtype; slots with slot_pos < 0 (dropped) are skipped.
+ * y_perm [T*k, d], y_shared [T, d] or NULL, out [T, d].
  * Source: the weighted merge of the selected experts' outputs (MoEBlock listing;
  * "四、工作原理" of "开源混合架构大模型技术解析") plus the always-on shared experts. */
 moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_pos,
@@ -183,6 +211,11 @@ typedef struct {
    * routed and shared experts run in one launch (few rows per expert), [3] and [4] (and
    * [5] and [6]) are recorded back to back after that launch.  Caller-owned events. */
   hipEvent_t stage_events[8];
+  /* Device buffer [2E + 1] fp32, or NULL: when given, the forward also writes the load
+   * statistics of moe_load_stats for its routing (f, then p, then the loss) with
+   * aux_alpha as alpha; they are computed between events [1] and [2]. */
+  float* load_stats;
+  float aux_alpha;
 } moe_forward_opts;
 
 /* moe_forward with options (opts may be NULL, which is moe_forward). */

@@ -280,29 +280,40 @@ def shared_weights(layer, i: int):
     return w1, w3, w2
 
 
-def moe_forward(layer, tokens=None):
+def moe_forward(layer, tokens=None, idx=None):
     """out[t] = sum_j w_j FFN_{e_j}(x_t) + sum_s FFN^shared_s(x_t)  (fp64).
 
     The masked per-(slot, expert) loop of the MoEBlock listing, with the slot loop folded
     into the mask: for each expert, the tokens that picked it in any slot.  ``tokens``
     restricts the computation to a subset of rows (every step is per token).  With a
     capacity factor, slots dropped by the capacity limit contribute nothing; which slots
-    are dropped depends on the whole batch, so the routing of all tokens decides it."""
+    are dropped depends on the whole batch, so the routing of all tokens decides it
+    (computed from the fp32 capacity factor, as stored).  ``idx`` [T, k] replaces the
+    selection with a given one for the whole batch (the weights stay the renormalised
+    fp64 scores of those experts), for comparing outputs under a routing that was checked
+    separately."""
     s = layer.shape
     r = route(layer, tokens)
-    x, idx, w = r["x"], r["idx"], r["w"]
-    kept = np.ones(idx.shape, dtype=bool)
+    if idx is not None:
+        idx_all = np.asarray(idx, np.int32)
+        r["idx"] = idx_all if tokens is None else idx_all[np.asarray(tokens)]
+        r["w"] = routing_weights(r["scores"], r["idx"], s.renormalize, s.route_scale)
+    x, idx_t, w = r["x"], r["idx"], r["w"]
+    kept = np.ones(idx_t.shape, dtype=bool)
     cf = getattr(s, "capacity_factor", None)
     if cf is not None:
-        full = r if tokens is None else route(layer)
-        cap = expert_capacity(s.T, s.k, s.E, cf)
-        _, _, _, slot_pos = permute(full["idx"], s.E, cap)
+        if idx is not None:
+            full_idx = np.asarray(idx, np.int32)
+        else:
+            full_idx = (r if tokens is None else route(layer))["idx"]
+        cap = expert_capacity(s.T, s.k, s.E, float(np.float32(cf)))
+        _, _, _, slot_pos = permute(full_idx, s.E, cap)
         kept_all = slot_pos.reshape(s.T, s.k) >= 0
         kept = kept_all if tokens is None else kept_all[np.asarray(tokens)]
     r["kept"] = kept
     out = np.zeros_like(x)
     for e in range(s.E):
-        rows, slots = np.nonzero((idx == e) & kept)
+        rows, slots = np.nonzero((idx_t == e) & kept)
         if rows.size == 0:
             continue
         w1, w3, w2 = expert_weights(layer, e)

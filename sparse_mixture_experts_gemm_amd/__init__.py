@@ -14,7 +14,8 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
-    "workspace_size", "route", "select", "permute", "grouped_gemm", "combine", "forward",
+    "workspace_size", "route", "select", "load_stats", "permute", "grouped_gemm", "combine",
+    "forward",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
     "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
@@ -27,9 +28,9 @@ MOE_ACT_SWIGLU, MOE_ACT_RELU2 = 0, 1
 MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 
-EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_permute",
-                    "moe_grouped_gemm", "moe_combine", "moe_forward", "moe_forward_ex",
-                    "moe_status_string", "moe_last_hip_error"]
+EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_load_stats",
+                    "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
+                    "moe_forward_ex", "moe_status_string", "moe_last_hip_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -57,11 +58,12 @@ class Config(ctypes.Structure):
         ("inter_dim", ctypes.c_int32), ("score_fn", ctypes.c_int32),
         ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float),
         ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
     ]
 
 
 _W_FIELDS = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-             "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]
+             "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down", "select_bias"]
 
 
 class _WeightsC(ctypes.Structure):
@@ -80,7 +82,8 @@ class Weights:
 
 
 class _OptsC(ctypes.Structure):
-    _fields_ = [("stage_events", ctypes.c_void_p * 8)]
+    _fields_ = [("stage_events", ctypes.c_void_p * 8), ("load_stats", ctypes.c_void_p),
+                ("aux_alpha", ctypes.c_float)]
 
 
 _LIB = None
@@ -99,8 +102,9 @@ def lib():
         wp = ctypes.POINTER(_WeightsC)
         sig = {
             "moe_workspace_size": [cfgp, ctypes.POINTER(sz)],
-            "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp],
-            "moe_select": [cfgp, vp, vp, vp, vp],
+            "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_select": [cfgp, vp, vp, vp, vp, vp],
+            "moe_load_stats": [cfgp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_grouped_gemm": [cfgp, i32, i32, vp, vp, vp, i32, wp, vp, vp, vp, sz, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
@@ -146,14 +150,16 @@ def _check(status: int, what: str):
 
 
 def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renormalize=True,
-                route_scale=1.0, act="swiglu", act_dtype="bf16", weight_dtype="bf16") -> Config:
+                route_scale=1.0, act="swiglu", act_dtype="bf16", weight_dtype="bf16",
+                capacity_factor=0.0) -> Config:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3}
     return Config(num_tokens=T, dim=d, num_experts=E, top_k=k, num_groups=G, topk_groups=Gk,
                   group_score_topn=n_g, num_shared=S, inter_dim=I,
                   score_fn={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score],
                   renormalize=int(bool(renormalize)), route_scale=float(route_scale),
                   act={"swiglu": MOE_ACT_SWIGLU, "relu2": MOE_ACT_RELU2}[act],
-                  act_dtype=dt[act_dtype], weight_dtype=dt[weight_dtype])
+                  act_dtype=dt[act_dtype], weight_dtype=dt[weight_dtype],
+                  capacity_factor=float(capacity_factor or 0.0))
 
 
 def workspace_size(cfg: Config) -> int:
@@ -162,15 +168,22 @@ def workspace_size(cfg: Config) -> int:
     return n.value
 
 
-def route(cfg, x, router, logit_bias, scores, topk_idx, topk_w, stream=None):
+def route(cfg, x, router, logit_bias, select_bias, scores, topk_idx, topk_w, stream=None):
     _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(router), _ptr(logit_bias),
-                           _ptr(scores), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
-           "moe_route")
+                           _ptr(select_bias), _ptr(scores), _ptr(topk_idx), _ptr(topk_w),
+                           _stream(stream)), "moe_route")
 
 
-def select(cfg, scores, topk_idx, topk_w, stream=None):
-    _check(lib().moe_select(ctypes.byref(cfg), _ptr(scores), _ptr(topk_idx), _ptr(topk_w),
-                            _stream(stream)), "moe_select")
+def select(cfg, scores, keys, topk_idx, topk_w, stream=None):
+    _check(lib().moe_select(ctypes.byref(cfg), _ptr(scores), _ptr(keys), _ptr(topk_idx),
+                            _ptr(topk_w), _stream(stream)), "moe_select")
+
+
+def load_stats(cfg, scores, topk_idx, alpha, f, p, loss, ws, ws_bytes=None, stream=None):
+    nb = ws_bytes if ws_bytes is not None else (0 if ws is None else ws.numel() * ws.element_size())
+    _check(lib().moe_load_stats(ctypes.byref(cfg), _ptr(scores), _ptr(topk_idx), float(alpha),
+                                _ptr(f), _ptr(p), _ptr(loss), _ptr(ws), nb, _stream(stream)),
+           "moe_load_stats")
 
 
 def permute(cfg, topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, ws,
@@ -195,19 +208,23 @@ def combine(cfg, y_perm, slot_pos, y_shared, out, stream=None):
                              _ptr(out), _stream(stream)), "moe_combine")
 
 
-def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None, stage_events=None):
+def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None, stage_events=None,
+            load_stats=None, aux_alpha=1.0):
     """The whole layer.  stage_events: optional list of 8 torch.cuda.Event (or None) recorded
-    at the stage boundaries (see moe_forward_opts in include/moe.h)."""
+    at the stage boundaries; load_stats: optional device fp32 buffer [2E + 1] for the load
+    statistics (see moe_forward_opts in include/moe.h)."""
     nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
-    if stage_events is None:
+    if stage_events is None and load_stats is None:
         _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
                                  _ptr(ws), nb, _stream(stream)), "moe_forward")
         return
     opts = _OptsC()
-    for i, ev in enumerate(stage_events):
+    for i, ev in enumerate(stage_events or []):
         if ev is not None and not ev.cuda_event:
             ev.record()          # torch creates its events lazily; the library re-records it
         opts.stage_events[i] = None if ev is None else ev.cuda_event
+    opts.load_stats = _ptr(load_stats)
+    opts.aux_alpha = float(aux_alpha)
     _check(lib().moe_forward_ex(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
                                 _ptr(ws), nb, _stream(stream), ctypes.byref(opts)),
            "moe_forward_ex")

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdint>
 
 #include "internal.h"
@@ -54,6 +55,7 @@ moe_status check_config(const moe_config* c) {
   if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
@@ -89,7 +91,17 @@ moe::RouteParams route_params(const moe_config* c) {
   p.score_fn = c->score_fn;
   p.renormalize = c->renormalize;
   p.route_scale = c->route_scale;
+  p.select_bias = nullptr;
   return p;
+}
+
+// Rows an expert may keep: floor(c * T * k / E) in double from the fp32 factor, or
+// INT_MAX (unlimited) for c <= 0.
+int expert_capacity(const moe_config* c) {
+  if (!(c->capacity_factor > 0.0f)) return INT_MAX;
+  const double cap = std::floor((double)c->capacity_factor * (double)c->num_tokens *
+                                (double)c->top_k / (double)c->num_experts);
+  return cap >= (double)INT_MAX ? INT_MAX : (int)cap;
 }
 
 size_t act_size(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
@@ -100,6 +112,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Workspace of moe_forward, in carve order.
 struct Carve {
   size_t topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, perm_ws;
+  size_t scores, stats_ws;
   size_t h_routed, h_shared, y_routed, y_shared, total;
 };
 
@@ -118,6 +131,8 @@ Carve carve(const moe_config* c) {
   w.slot_pos = take(T * k * 4);
   w.perm_weight = take(T * k * 4);
   w.perm_ws = take(moe::permute_ws_bytes((int)T, (int)E));
+  w.scores = take(T * E * 4);                    // only written when statistics are asked
+  w.stats_ws = take(moe::stats_ws_bytes((int)T, (int)E));
   w.h_routed = take(T * k * I * as);
   w.h_shared = take(T * S * I * as);
   w.y_routed = take(T * k * d * as);
@@ -206,8 +221,8 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
 }
 
 moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
-                     const float* logit_bias, float* scores, int32_t* topk_idx, float* topk_w,
-                     hipStream_t stream) {
+                     const float* logit_bias, const float* select_bias, float* scores,
+                     int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   try {
     moe_status st = check_config(cfg);
     if (st != MOE_OK) return st;
@@ -215,21 +230,44 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
     if (x == nullptr || router == nullptr || topk_idx == nullptr || topk_w == nullptr)
       return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(router)) return MOE_ERR_UNSUPPORTED;
-    return hip_status(moe::launch_route(route_params(cfg), cfg->act_dtype, x, router, logit_bias,
-                                        scores, topk_idx, topk_w, stream));
+    moe::RouteParams rp = route_params(cfg);
+    rp.select_bias = select_bias;
+    return hip_status(moe::launch_route(rp, cfg->act_dtype, x, router, logit_bias, scores,
+                                        topk_idx, topk_w, stream));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
 }
 
-moe_status moe_select(const moe_config* cfg, const float* scores, int32_t* topk_idx,
-                      float* topk_w, hipStream_t stream) {
+moe_status moe_select(const moe_config* cfg, const float* scores, const float* keys,
+                      int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   try {
     moe_status st = check_config(cfg);
     if (st != MOE_OK) return st;
     if (cfg->num_tokens == 0) return MOE_OK;
     if (scores == nullptr || topk_idx == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
-    return hip_status(moe::launch_select(route_params(cfg), scores, topk_idx, topk_w, stream));
+    return hip_status(moe::launch_select(route_params(cfg), scores, keys, topk_idx, topk_w,
+                                         stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_load_stats(const moe_config* cfg, const float* scores, const int32_t* topk_idx,
+                          float alpha, float* f, float* p, float* loss, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (scores == nullptr || topk_idx == nullptr || f == nullptr || p == nullptr ||
+        loss == nullptr)
+      return MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(alpha)) return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::stats_ws_bytes(cfg->num_tokens, cfg->num_experts);
+    if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_load_stats(cfg->num_tokens, cfg->num_experts, cfg->top_k,
+                                             scores, topk_idx, alpha, f, p, loss, ws, stream));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -247,9 +285,10 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
     if ((topk_w == nullptr) != (perm_weight == nullptr)) return MOE_ERR_INVALID_ARG;
     const size_t need = moe::permute_ws_bytes(cfg->num_tokens, cfg->num_experts);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_permute(cfg->num_tokens, cfg->num_experts, cfg->top_k, topk_idx,
-                                          topk_w, counts, offsets, perm_token, slot_pos,
-                                          perm_weight, ws, stream));
+    return hip_status(moe::launch_permute(cfg->num_tokens, cfg->num_experts, cfg->top_k,
+                                          expert_capacity(cfg), topk_idx, topk_w, counts,
+                                          offsets, perm_token, slot_pos, perm_weight, ws,
+                                          stream));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -345,13 +384,24 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
       if (opts != nullptr && opts->stage_events[i] != nullptr && e == hipSuccess)
         e = hipEventRecord(opts->stage_events[i], stream);
     };
+    const bool stats = opts != nullptr && opts->load_stats != nullptr;
+    if (stats && !std::isfinite(opts->aux_alpha)) return MOE_ERR_INVALID_ARG;
+    moe::RouteParams rp = route_params(cfg);
+    rp.select_bias = w->select_bias;
+    float* scores = stats ? static_cast<float*>(at(cv.scores)) : nullptr;
     mark(0);
-    e = moe::launch_route(route_params(cfg), cfg->act_dtype, x, w->router, w->logit_bias,
-                          nullptr, idx, tw, stream);
+    e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw, stream);
     mark(1);
     if (e == hipSuccess)
-      e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, idx, tw, counts, offsets,
-                              perm_token, slot_pos, perm_weight, at(cv.perm_ws), stream);
+      e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, expert_capacity(cfg), idx, tw,
+                              counts, offsets, perm_token, slot_pos, perm_weight,
+                              at(cv.perm_ws), stream);
+    if (stats && e == hipSuccess) {
+      const int E = cfg->num_experts;
+      e = moe::launch_load_stats(T, E, cfg->top_k, scores, idx, opts->aux_alpha,
+                                 opts->load_stats, opts->load_stats + E,
+                                 opts->load_stats + 2 * E, at(cv.stats_ws), stream);
+    }
     mark(2);
     // few rows per expert: the routed and shared experts stream their weights in one
     // launch per stage

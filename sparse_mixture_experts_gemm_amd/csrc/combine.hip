@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(int d, int k,
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int p = slot_pos[(size_t)t * k + j];
+      if (p < 0) continue;   // dropped by the expert capacity
       const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)p * d + c);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(int d, int k, const fl
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int p = slot_pos[(size_t)t * k + j];
+      if (p < 0) continue;   // dropped by the expert capacity
       const float4 v = *reinterpret_cast<const float4*>(y + (size_t)p * d + c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }

@@ -14,6 +14,7 @@ struct RouteParams {
   int score_fn;       // moe_score_fn
   int renormalize;
   float route_scale;
+  const float* select_bias;   // [E] selection-only bias or null
 };
 
 // Segments of a grouped GEMM.  Routed: segment e = rows [offsets[e], offsets[e+1]).
@@ -44,13 +45,21 @@ enum class Stage { Up = 0, Down = 1 };
 hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, const void* router,
                         const float* bias, float* scores, int32_t* idx, float* w,
                         hipStream_t s);
-hipError_t launch_select(const RouteParams& p, const float* scores, int32_t* idx, float* w,
-                         hipStream_t s);
+hipError_t launch_select(const RouteParams& p, const float* scores, const float* keys,
+                         int32_t* idx, float* w, hipStream_t s);
 
+// Load statistics: per-chunk partial sums in ws (stats_ws_bytes), then one reduction.
+size_t stats_ws_bytes(int T, int E);
+hipError_t launch_load_stats(int T, int E, int k, const float* scores, const int32_t* idx,
+                             float alpha, float* f, float* p, float* loss, void* ws,
+                             hipStream_t s);
+
+// capacity: rows an expert may keep (INT_MAX: unlimited); dropped slots get slot_pos -1.
 size_t permute_ws_bytes(int T, int E);
-hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* topk_w,
-                          int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                          int32_t* slot_pos, float* perm_weight, void* ws, hipStream_t s);
+hipError_t launch_permute(int T, int E, int k, int capacity, const int32_t* idx,
+                          const float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* slot_pos, float* perm_weight, void* ws,
+                          hipStream_t s);
 
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
                                int weight_dtype, int num_cus, hipStream_t s);

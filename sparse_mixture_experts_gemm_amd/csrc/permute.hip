@@ -13,6 +13,9 @@
 //      (lane = token); each lane sets its bit in a 64-bit LDS mask per expert it picked, and
 //      the rank of a slot among earlier tokens of the same expert is a popcount of the
 //      lower bits.  Chunk 0 also writes counts and offsets.
+// With an expert capacity ("MoE 数学：路由、容量与平衡详解" of "大模型工程（一）": tokens beyond an
+// expert's capacity are dropped), a slot whose rank inside its expert reaches the
+// capacity gets slot_pos -1 and no row; counts and offsets count the kept rows.
 // Up to kFusedMaxTokens tokens (and kFusedMaxSlots pairs), one workgroup of 16 waves does both steps in a
 // single launch from an LDS copy of topk_idx (each wave owns a contiguous run of tokens; the
 // scan runs between two barriers).
@@ -48,7 +51,8 @@ __global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k, int chun
   if (threadIdx.x < E) chunk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nchunks, int chunk,
+__global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int capacity,
+                                                     int nchunks, int chunk,
                                                      const int32_t* __restrict__ idx,
                                                      const float* __restrict__ topk_w,
                                                      const int32_t* __restrict__ chunk_hist,
@@ -57,11 +61,13 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
                                                      int32_t* __restrict__ perm_token,
                                                      int32_t* __restrict__ slot_pos,
                                                      float* __restrict__ perm_weight) {
-  __shared__ int run[64];
+  __shared__ int run[64];        // rank inside its expert of the chunk's next slot
+  __shared__ int koff[64];       // first permuted row of each expert
   __shared__ unsigned long long mask[64];
   const int lane = threadIdx.x;
   {
-    // column sums (counts), their exclusive scan (offsets) and this chunk's start per expert
+    // column sums (slots per expert), the kept rows min(sum, capacity), their exclusive
+    // scan (offsets) and the number of this expert's slots in earlier chunks
     int total = 0, before = 0;
     if (lane < E) {
 #pragma unroll 8
@@ -71,17 +77,21 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
         before += c < (int)blockIdx.x ? v : 0;
       }
     }
-    int incl = total;
+    const int kept = min(total, capacity);
+    int incl = kept;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    if (lane < E) run[lane] = incl - total + before;
+    if (lane < E) {
+      run[lane] = before;
+      koff[lane] = incl - kept;
+    }
     if (blockIdx.x == 0) {
       if (lane < E) {
-        counts[lane] = total;
-        offsets[lane] = incl - total;
+        counts[lane] = kept;
+        offsets[lane] = incl - kept;
       }
       if (lane == E - 1) offsets[E] = incl;
     }
@@ -105,10 +115,15 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int nc
       for (int j = 0; j < k; ++j) {
         const int e = idx[(size_t)t * k + j];
         if ((unsigned)e >= (unsigned)E) continue;
-        const int pos = run[e] + __popcll(mask[e] & below);
-        perm_token[pos] = t;
-        slot_pos[(size_t)t * k + j] = pos;
-        if (perm_weight != nullptr) perm_weight[pos] = topk_w[(size_t)t * k + j];
+        const int rank = run[e] + __popcll(mask[e] & below);
+        if (rank < capacity) {
+          const int pos = koff[e] + rank;
+          perm_token[pos] = t;
+          slot_pos[(size_t)t * k + j] = pos;
+          if (perm_weight != nullptr) perm_weight[pos] = topk_w[(size_t)t * k + j];
+        } else {
+          slot_pos[(size_t)t * k + j] = -1;
+        }
       }
     }
     __syncthreads();
@@ -123,7 +138,7 @@ constexpr int kFusedMaxSlots = 28672;   // T * k staged in LDS (112 KB)
 // Up to kFusedMaxTokens tokens: one workgroup of 16 waves.  The whole topk_idx array is
 // first copied into LDS with every load in flight at once; histogram, scan and scatter
 // then read it from LDS.  Each wave owns a contiguous run of tokens.
-__global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k,
+__global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k, int capacity,
                                                              const int32_t* __restrict__ idx,
                                                              const float* __restrict__ topk_w,
                                                              int32_t* __restrict__ counts,
@@ -140,7 +155,8 @@ __global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k
     reinterpret_cast<int4*>(sidx)[i] = reinterpret_cast<const int4*>(idx)[i];
   for (int i = 4 * n4 + threadIdx.x; i < nslot; i += 1024) sidx[i] = idx[i];
   __syncthreads();
-  permute_lds(T, E, k, sidx, topk_w, pl, counts, offsets, perm_token, slot_pos, perm_weight);
+  permute_lds(T, E, k, capacity, sidx, topk_w, pl, counts, offsets, perm_token, slot_pos,
+              perm_weight);
 }
 
 }  // namespace
@@ -151,20 +167,22 @@ size_t permute_ws_bytes(int T, int E) {
   return nchunks * (size_t)E * sizeof(int32_t);
 }
 
-hipError_t launch_permute(int T, int E, int k, const int32_t* idx, const float* topk_w,
-                          int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                          int32_t* slot_pos, float* perm_weight, void* ws, hipStream_t s) {
+hipError_t launch_permute(int T, int E, int k, int capacity, const int32_t* idx,
+                          const float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* slot_pos, float* perm_weight, void* ws,
+                          hipStream_t s) {
   if (T <= kFusedMaxTokens && (long long)T * k <= kFusedMaxSlots && k <= 8) {
-    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(1024), 0, s, T, E, k, idx, topk_w,
-                       counts, offsets, perm_token, slot_pos, perm_weight);
+    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(1024), 0, s, T, E, k, capacity, idx,
+                       topk_w, counts, offsets, perm_token, slot_pos, perm_weight);
     return hipGetLastError();
   }
   const int chunk = chunk_tokens(T);
   const int nchunks = (T + chunk - 1) / chunk;
   int32_t* chunk_hist = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, s, T, E, k, chunk, idx, chunk_hist);
-  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, nchunks, chunk, idx,
-                     topk_w, chunk_hist, counts, offsets, perm_token, slot_pos, perm_weight);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, s, T, E, k, capacity, nchunks,
+                     chunk, idx, topk_w, chunk_hist, counts, offsets, perm_token, slot_pos,
+                     perm_weight);
   return hipGetLastError();
 }
 

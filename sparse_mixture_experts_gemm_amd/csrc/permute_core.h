@@ -11,7 +11,8 @@ constexpr int kPermWaves = 16;   // the workgroup is 16 waves (1024 threads)
 
 struct PermuteLds {
   int hist[kPermWaves][64];
-  int run[kPermWaves][64];
+  int run[kPermWaves][64];       // rank inside its expert of the wave's next slot
+  int koff[64];                  // first permuted row of each expert
   unsigned long long mask[kPermWaves][64];
 };
 
@@ -21,8 +22,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // sidx: [T * k] expert ids in LDS; wsrc: [T * k] routing weights (LDS or global) or null.
+// Each expert keeps its first `capacity` slots (token order); the others get slot_pos -1.
 // Every thread of the workgroup must call it.  k <= 8, E <= 64.
-__device__ __forceinline__ void permute_lds(int T, int E, int k, const int* sidx,
+__device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, const int* sidx,
                                             const float* wsrc, PermuteLds& pl,
                                             int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets,
@@ -47,19 +49,21 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, const int* sidx
     const int e = lane;
     int total = 0;
     for (int w = 0; w < kPermWaves; ++w) total += (e < E) ? pl.hist[w][e] : 0;
-    int incl = total;
+    const int kept = min(total, capacity);
+    int incl = kept;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       int v = __shfl_up(incl, o, 64);
       if (e >= o) incl += v;
     }
-    int at = incl - total;
     if (e < E) {
-      counts[e] = total;
-      offsets[e] = at;
+      counts[e] = kept;
+      offsets[e] = incl - kept;
+      pl.koff[e] = incl - kept;
+      int rank = 0;
       for (int w = 0; w < kPermWaves; ++w) {
-        pl.run[w][e] = at;
-        at += pl.hist[w][e];
+        pl.run[w][e] = rank;
+        rank += pl.hist[w][e];
       }
     }
     if (e == E - 1) offsets[E] = incl;
@@ -91,10 +95,15 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, const int* sidx
         if (j >= k) break;
         const int e = sidx[t * k + j];
         if ((unsigned)e >= (unsigned)E) continue;
-        const int pos = pl.run[wave][e] + __popcll(pl.mask[wave][e] & below);
-        perm_token[pos] = t;
-        slot_pos[(size_t)t * k + j] = pos;
-        if (perm_weight != nullptr) perm_weight[pos] = wv[j];
+        const int rank = pl.run[wave][e] + __popcll(pl.mask[wave][e] & below);
+        if (rank < capacity) {
+          const int pos = pl.koff[e] + rank;
+          perm_token[pos] = t;
+          slot_pos[(size_t)t * k + j] = pos;
+          if (perm_weight != nullptr) perm_weight[pos] = wv[j];
+        } else {
+          slot_pos[(size_t)t * k + j] = -1;
+        }
       }
     }
     wave_lds_sync();

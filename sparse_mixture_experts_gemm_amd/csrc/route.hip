@@ -23,26 +23,21 @@ namespace {
 
 constexpr int kRouteTok = 16;   // tokens per workgroup (bf16 path)
 
-// Score of one expert lane, then selection for token t.  `valid` marks lanes < E.
-__device__ __forceinline__ void score_select_write(float logit, bool valid, int lane,
-                                                   const RouteParams& p, int t, float* scores,
-                                                   int32_t* idx, float* wout,
-                                                   bool from_logit) {
-  float s = logit;
-  if (from_logit) {
-    if (p.score_fn == MOE_SCORE_SIGMOID) {
-      s = 1.0f / (1.0f + expf(-logit));
-    } else {
-      float mx = wave_max_f(valid ? logit : -INFINITY);
-      float e = valid ? expf(logit - mx) : 0.0f;
-      float sum = wave_sum_f(e);
-      s = e / sum;
-    }
-    if (scores != nullptr && valid) scores[(size_t)t * p.E + lane] = s;
-  }
+// Gate score of one expert lane: sigmoid, or softmax over the wave's valid lanes.
+__device__ __forceinline__ float gate_score(float logit, bool valid, const RouteParams& p) {
+  if (p.score_fn == MOE_SCORE_SIGMOID) return 1.0f / (1.0f + expf(-logit));
+  const float mx = wave_max_f(valid ? logit : -INFINITY);
+  const float e = valid ? expf(logit - mx) : 0.0f;
+  const float sum = wave_sum_f(e);
+  return e / sum;
+}
 
-  // fp32 bit patterns of non-negative scores order like the scores themselves
-  const uint32_t sbits = __float_as_uint(s);
+// Selection for token t on per-lane selection keys (>= 0) with weights from the scores s.
+__device__ __forceinline__ void select_write(float s, float key, bool valid, int lane,
+                                             const RouteParams& p, int t, int32_t* idx,
+                                             float* wout) {
+  // fp32 bit patterns of non-negative keys order like the keys themselves
+  const uint32_t sbits = __float_as_uint(key);
   bool elig = valid;
   if (p.G > 1 && p.Gk < p.G) {
     const int gsz = p.E / p.G;
@@ -63,7 +58,7 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
     } else {
       float b1 = -1.0f, b2 = -1.0f;  // scores are >= 0
       for (int i = 0; i < gsz; ++i) {
-        float v = wave_shfl(s, g * gsz + i);
+        float v = wave_shfl(key, g * gsz + i);
         if (v > b1) {
           b2 = b1;
           b1 = v;
@@ -84,16 +79,17 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
 
   // k rounds: wave max of (score bits + 1) over eligible lanes; the lowest lane holding the
   // max wins, i.e. the lower expert index on equal scores
-  uint32_t key = elig ? sbits + 1u : 0u;
+  uint32_t kb = elig ? sbits + 1u : 0u;
   float sel = 0.0f;
   int sel_e = 0;
   for (int j = 0; j < p.k; ++j) {
-    const uint32_t mx = wave_max_u32(key);
-    const uint64_t m = __ballot(key == mx);
+    const uint32_t mx = wave_max_u32(kb);
+    const uint64_t m = __ballot(kb == mx);
     const int win = (int)__builtin_ctzll(m);
-    if (lane == win) key = 0u;
+    const float s_win = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(s), win));
+    if (lane == win) kb = 0u;
     if (lane == j) {
-      sel = __uint_as_float(mx - 1u);
+      sel = s_win;
       sel_e = win;
     }
   }
@@ -104,6 +100,19 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
     idx[(size_t)t * p.k + lane] = sel_e;
     wout[(size_t)t * p.k + lane] = wj;
   }
+}
+
+// Scores of one expert lane from its logit, then selection for token t.  The selection
+// compares the scores of the logits plus the selection-only bias when one is given; the
+// weights use the unbiased scores.  `valid` marks lanes < E.
+__device__ __forceinline__ void score_select_write(float logit, bool valid, int lane,
+                                                   const RouteParams& p, int t, float* scores,
+                                                   int32_t* idx, float* wout) {
+  const float s = gate_score(logit, valid, p);
+  if (scores != nullptr && valid) scores[(size_t)t * p.E + lane] = s;
+  float key = s;
+  if (p.select_bias != nullptr) key = gate_score(logit + (valid ? p.select_bias[lane] : 0.0f), valid, p);
+  select_write(s, key, valid, lane, p, t, idx, wout);
 }
 
 // bf16 router: 16 tokens per workgroup; its 16 waves split K in 32-wide MFMA steps
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
     for (int w = 0; w < kRouteWaves; ++w) l += part[w][row][lane];   // fixed order
     if (bias != nullptr) l += bias[lane];
   }
-  score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
+  score_select_write(l, valid, lane, p, t, scores, idx, wout);
 }
 
 // fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.
@@ -200,17 +209,19 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p, const flo
     for (int c = 0; c < p.d; ++c) l = fmaf(xr[c], wrow[c], l);
     if (bias != nullptr) l += bias[lane];
   }
-  score_select_write(l, valid, lane, p, t, scores, idx, wout, true);
+  score_select_write(l, valid, lane, p, t, scores, idx, wout);
 }
 
 __global__ __launch_bounds__(256) void select_kernel(RouteParams p, const float* __restrict__ scores,
+                                                     const float* __restrict__ keys,
                                                      int32_t* idx, float* wout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const bool valid = lane < p.E;
   const float s = valid ? scores[(size_t)t * p.E + lane] : 0.0f;
-  score_select_write(s, valid, lane, p, t, nullptr, idx, wout, false);
+  const float key = (keys == nullptr) ? s : (valid ? keys[(size_t)t * p.E + lane] : 0.0f);
+  select_write(s, key, valid, lane, p, t, idx, wout);
 }
 
 }  // namespace
@@ -232,11 +243,11 @@ hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, cons
   return hipGetLastError();
 }
 
-hipError_t launch_select(const RouteParams& p, const float* scores, int32_t* idx, float* w,
-                         hipStream_t s) {
+hipError_t launch_select(const RouteParams& p, const float* scores, const float* keys,
+                         int32_t* idx, float* w, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((p.T + 3) / 4);
-  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, p, scores, idx, w);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, p, scores, keys, idx, w);
   return hipGetLastError();
 }
 

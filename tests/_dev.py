@@ -27,7 +27,7 @@ def config(shape, T=None):
     return moe.make_config(s.T if T is None else T, s.d, s.E, s.k, G=s.G, Gk=s.Gk, n_g=s.n_g,
                            S=s.S, I=s.I, score=s.score, renormalize=s.renormalize,
                            route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
-                           weight_dtype=s.weight_dtype)
+                           weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor)
 
 
 def weights(lay):
@@ -36,6 +36,7 @@ def weights(lay):
     t = {n: to_dev(getattr(lay, n)) for n in names}
     t["router"] = to_dev(lay.router)
     t["logit_bias"] = to_dev(lay.logit_bias)
+    t["select_bias"] = to_dev(lay.select_bias)
     return moe.Weights(**t)
 
 

@@ -75,14 +75,17 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
     (dict(T=-1), 1), (dict(d=0), 1), (dict(E=128, G=8, k=6), 2), (dict(d=2000), 2),
     (dict(I=1000), 2), (dict(act_dtype="f32", weight_dtype="bf16"), 2),
     (dict(act_dtype="bf16", weight_dtype="f32"), 2),
+    (dict(capacity_factor=float("nan")), 1),
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
     c = cfg(**bad)
     n = ctypes.c_size_t(0)
     assert lib.moe_workspace_size(ctypes.byref(c), ctypes.byref(n)) == status
     fake = 4096   # never dereferenced: validation fails first
-    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, fake, fake, None) == status
-    assert lib.moe_select(ctypes.byref(c), fake, fake, fake, None) == status
+    assert lib.moe_route(ctypes.byref(c), fake, fake, None, None, None, fake, fake, None) == status
+    assert lib.moe_select(ctypes.byref(c), fake, None, fake, fake, None) == status
+    assert lib.moe_load_stats(ctypes.byref(c), fake, fake, 1.0, fake, fake, fake, fake, 1 << 20,
+                              None) == status
     with pytest.raises(moe.MoeError):
         moe.workspace_size(c)
 
@@ -119,6 +122,12 @@ def test_null_and_workspace_errors_are_reported_before_launch(lib):
                                 fake, None, 0, None) == 1
     # combine: null y
     assert lib.moe_combine(ctypes.byref(c), None, fake, None, fake, None) == 1
+    # load statistics: null outputs, missing workspace, non-finite alpha
+    assert lib.moe_load_stats(ctypes.byref(c), fake, fake, 1.0, None, fake, fake, fake, 1 << 20,
+                              None) == 1
+    assert lib.moe_load_stats(ctypes.byref(c), fake, fake, 1.0, fake, fake, fake, None, 0, None) == 3
+    assert lib.moe_load_stats(ctypes.byref(c), fake, fake, float("inf"), fake, fake, fake, fake,
+                              1 << 20, None) == 1
 
 
 def test_zero_tokens_is_a_no_op(lib):
@@ -126,7 +135,8 @@ def test_zero_tokens_is_a_no_op(lib):
     fake = 4096
     w = moe.Weights(router=fake, w_gate=fake, w_up=fake, w_down=fake, sh_gate=fake, sh_up=fake,
                     sh_down=fake)
-    assert lib.moe_route(ctypes.byref(c), None, None, None, None, None, None, None) == 0
+    assert lib.moe_route(ctypes.byref(c), None, None, None, None, None, None, None, None) == 0
+    assert lib.moe_load_stats(ctypes.byref(c), None, None, 1.0, None, None, None, None, 0, None) == 0
     assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), None, None, None, 0, None) == 0
     assert lib.moe_combine(ctypes.byref(c), None, None, None, None, None) == 0
     assert lib.moe_grouped_gemm(ctypes.byref(c), 0, 0, None, None, None, 0, ctypes.byref(w.c), None,

@@ -41,6 +41,12 @@ SMALL = {
                                            act="relu2", weight_dtype="e4m3", seed=38),
     # enough rows for 256 x 256 tiles in the routed GEMMs
     "multi_tile_wide": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512, seed=40),
+    # selection-only expert bias: softmax gating (fp32) and n_g = 2 groups (bf16)
+    "biased_softmax_f32": W.small_shape(T=257, d=128, E=16, k=3, score="softmax", G=1, Gk=1,
+                                        S=0, I=64, act_dtype="f32", weight_dtype="f32",
+                                        select_bias_std=1.0, seed=41),
+    "biased_groups_n2": W.small_shape(T=333, d=256, E=32, k=4, G=8, Gk=3, n_g=2, S=1, I=128,
+                                      select_bias_std=0.7, capacity_factor=1.0, seed=42),
     # K = 64: one K-slice per tile, several tiles per workgroup
     "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
 }
@@ -129,9 +135,29 @@ def test_select_bit_exact_on_oracle_scores(name):
     cfg = config(s, T=T)
     idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
-    moe.select(cfg, to_dev(sc32), idx, w)
+    moe.select(cfg, to_dev(sc32), None, idx, w)
     torch.cuda.synchronize()
     ref_idx = O.select_experts(sc32, s.k, s.G, s.Gk, s.n_g)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    ref_w = O.routing_weights(sc32.astype(np.float64), ref_idx, s.renormalize, s.route_scale)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["balance_bf16", "biased_softmax_f32", "biased_groups_n2"])
+def test_select_on_keys_bit_exact(name):
+    """Selection on given fp32 keys (the scores of the biased logits), weights from the
+    unbiased scores: indices bit-exact against the oracle's selection on the same keys."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    r = O.route(lay)
+    sc32 = r["scores"].astype(np.float32)
+    k32 = r["keys"].astype(np.float32)
+    cfg = config(s)
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    moe.select(cfg, to_dev(sc32), to_dev(k32), idx, w)
+    torch.cuda.synchronize()
+    ref_idx = O.select_experts(k32, s.k, s.G, s.Gk, s.n_g)
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
     ref_w = O.routing_weights(sc32.astype(np.float64), ref_idx, s.renormalize, s.route_scale)
     assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=1e-7)
@@ -159,7 +185,7 @@ def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
     cfg = moe.make_config(T, 64, E, k, G=G, Gk=Gk, n_g=n_g, I=64)
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    moe.select(cfg, to_dev(sc), idx, w)
+    moe.select(cfg, to_dev(sc), None, idx, w)
     torch.cuda.synchronize()
     ref = O.select_experts(sc, k, G, Gk, n_g)
     assert np.array_equal(idx.cpu().numpy(), ref)
@@ -173,7 +199,8 @@ def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
 
 # ----------------------------------------------------------------------------- route
 ROUTE_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
-               "small_swiglu", "small_f32", "single_token", "topk1_nogroups"]
+               "small_swiglu", "small_f32", "single_token", "topk1_nogroups", "balance_bf16",
+               "biased_softmax_f32", "biased_groups_n2"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -185,26 +212,49 @@ def test_route_matches_oracle(name):
     scores = torch.empty((T, s.E), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
-    moe.route(cfg, to_dev(lay.x), to_dev(lay.router), to_dev(lay.logit_bias), scores, idx, w)
+    moe.route(cfg, to_dev(lay.x), to_dev(lay.router), to_dev(lay.logit_bias),
+              to_dev(lay.select_bias), scores, idx, w)
     torch.cuda.synchronize()
     r = O.route(lay)
     g_sc = scores.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(g_sc - r["scores"])) <= 1e-5
     g_idx = idx.cpu().numpy()
-    mar = margins(r["scores"], s)
+    mar = margins(r["keys"], s)
     clear = mar > MARGIN
     assert np.array_equal(g_idx[clear], r["idx"][clear])
     # near-tie tokens: the GPU's pick must still be a valid top-k within the margin
     for t in np.nonzero(~clear)[0]:
-        assert valid_within_margin(g_idx[t], r["scores"][t], s), (t, g_idx[t], r["idx"][t])
+        assert valid_within_margin(g_idx[t], r["keys"][t], s), (t, g_idx[t], r["idx"][t])
     assert (~clear).sum() <= max(4, T // 200)
     same = (g_idx == r["idx"]).all(axis=1)
     assert np.allclose(w.cpu().numpy()[same], r["w"][same], rtol=1e-5, atol=1e-6)
 
 
+# ----------------------------------------------------------------------------- load statistics
+@pytest.mark.parametrize("name", ["fusionllm_bf16", "skewed_bf16", "decode_bf16", "tiny_fp32",
+                                  "biased_softmax_f32", "small_relu2_e4m3"])
+def test_load_stats_match_oracle(name):
+    s = shape_of(name)
+    r = O.route(layer_of(name))
+    sc32 = r["scores"].astype(np.float32)
+    cfg = config(s)
+    ws = workspace(cfg)
+    f = torch.empty(s.E, dtype=torch.float32, device="cuda")
+    p = torch.empty(s.E, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    moe.load_stats(cfg, to_dev(sc32), to_dev(r["idx"]), 0.01, f, p, loss, ws)
+    torch.cuda.synchronize()
+    rf, rp, rl = O.load_stats(sc32.astype(np.float64), r["idx"], s.E, 0.01)
+    # f: an integer count over T*k, rounded once to fp32
+    assert np.array_equal(f.cpu().numpy(), rf.astype(np.float32))
+    # p, loss: fp32 sums of T normalised scores
+    assert np.allclose(p.cpu().numpy(), rp, rtol=1e-5, atol=1e-7)
+    assert abs(loss.cpu().item() - rl) <= 1e-5 * abs(rl)
+
+
 # ----------------------------------------------------------------------------- permute
-def _check_permute(T, E, k, idx_np, topk_w_np):
-    cfg = moe.make_config(T, 64, E, k, I=64)
+def _check_permute(T, E, k, idx_np, topk_w_np, capacity_factor=0.0):
+    cfg = moe.make_config(T, 64, E, k, I=64, capacity_factor=capacity_factor)
     ws = workspace(cfg)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
@@ -213,14 +263,19 @@ def _check_permute(T, E, k, idx_np, topk_w_np):
     pw = torch.empty(max(T * k, 1), dtype=torch.float32, device="cuda")
     moe.permute(cfg, to_dev(idx_np), to_dev(topk_w_np), counts, offsets, pt, sp, pw, ws)
     torch.cuda.synchronize()
-    rc, ro, rpt, rsp = O.permute(idx_np, E)
+    cap = None
+    if capacity_factor > 0:
+        cap = O.expert_capacity(T, k, E, float(np.float32(capacity_factor)))
+    rc, ro, rpt, rsp = O.permute(idx_np, E, cap)
+    rows = int(ro[-1])
     assert np.array_equal(counts.cpu().numpy(), rc)
     assert np.array_equal(offsets.cpu().numpy(), ro)
-    assert np.array_equal(pt.cpu().numpy()[:T * k], rpt)
+    assert np.array_equal(pt.cpu().numpy()[:rows], rpt)
     assert np.array_equal(sp.cpu().numpy()[:T * k], rsp)
-    ref_pw = np.empty(T * k, np.float32)
-    ref_pw[rsp] = topk_w_np.reshape(-1)
-    assert np.array_equal(pw.cpu().numpy()[:T * k], ref_pw)
+    kept = rsp >= 0
+    ref_pw = np.empty(rows, np.float32)
+    ref_pw[rsp[kept]] = topk_w_np.reshape(-1)[kept]
+    assert np.array_equal(pw.cpu().numpy()[:rows], ref_pw)
 
 
 @pytest.mark.parametrize("name", ["fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
@@ -229,6 +284,16 @@ def test_permute_bit_exact_on_oracle_routing(name):
     s = shape_of(name)
     r = O.route(layer_of(name))
     _check_permute(s.T, s.E, s.k, r["idx"], r["w"].astype(np.float32))
+
+
+@pytest.mark.parametrize("name,cf", [("fusionllm_bf16", 1.25), ("fusionllm_bf16", 0.5),
+                                     ("decode_bf16", 1.0), ("skewed_bf16", 1.25),
+                                     ("small_swiglu", 0.3), ("single_token", 0.01),
+                                     ("tiny_fp32", 1.1)])
+def test_permute_with_capacity_bit_exact(name, cf):
+    s = shape_of(name)
+    r = O.route(layer_of(name))
+    _check_permute(s.T, s.E, s.k, r["idx"], r["w"].astype(np.float32), capacity_factor=cf)
 
 
 @pytest.mark.parametrize("T,E,k,pattern", [(1, 64, 6, "random"), (63, 64, 6, "random"),
@@ -381,12 +446,18 @@ def test_grouped_gemm_shared(name):
 
 
 # ----------------------------------------------------------------------------- combine
-@pytest.mark.parametrize("name,with_shared", [("small_swiglu", True), ("small_f32", True),
-                                              ("fusionllm_bf16", True), ("topk1_nogroups", False)])
-def test_combine(name, with_shared):
+@pytest.mark.parametrize("name,with_shared,cf", [("small_swiglu", True, None), ("small_f32", True, None),
+                                                 ("fusionllm_bf16", True, None),
+                                                 ("topk1_nogroups", False, None),
+                                                 ("fusionllm_bf16", True, 0.8),
+                                                 ("small_f32", False, 0.5)])
+def test_combine(name, with_shared, cf):
     s = shape_of(name)
     r = O.route(layer_of(name))
-    _, _, _, slot_pos = O.permute(r["idx"], s.E)
+    cap = None if cf is None else O.expert_capacity(s.T, s.k, s.E, cf)
+    _, _, _, slot_pos = O.permute(r["idx"], s.E, cap)
+    if cap is not None:
+        assert (slot_pos < 0).any()
     y = W.random_act((s.T * s.k, s.d), seed=79, dtype=s.act_dtype)
     ysh = W.random_act((s.T, s.d), seed=80, dtype=s.act_dtype) if with_shared else None
     out = act_empty((s.T, s.d), s.act_dtype)
@@ -403,7 +474,8 @@ def test_combine(name, with_shared):
 # ----------------------------------------------------------------------------- forward
 FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                  "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
-                 "single_token", "topk1_nogroups"]
+                 "single_token", "topk1_nogroups", "balance_bf16", "biased_softmax_f32",
+                 "biased_groups_n2"]
 
 
 def run_forward(name):
@@ -424,15 +496,55 @@ def run_forward(name):
 def test_forward_matches_oracle(name):
     s, lay, cfg, wts, ws, x, out, gpu_idx = run_forward(name)
     rows = sample_tokens(s.T, n=128, seed=4)
-    ref = O.moe_forward(lay, tokens=rows)
-    same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
-    mar = margins(ref["scores"], s)
-    assert np.all(same | (mar <= MARGIN)), "routing differs away from a near tie"
+    if s.capacity_factor is not None:
+        # which slots a capacity drops depends on the whole batch's routing: check the GPU
+        # routing of every token against the oracle, then compare the outputs under it
+        full = O.route(lay)
+        mar_all = margins(full["keys"], s)
+        same_all = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, full["idx"])])
+        assert np.all(same_all | (mar_all <= MARGIN)), "routing differs away from a near tie"
+        for t in np.nonzero(~same_all)[0]:
+            assert valid_within_margin(gpu_idx[t], full["keys"][t], s)
+        ref = O.moe_forward(lay, tokens=rows, idx=gpu_idx)
+        same = np.ones(len(rows), dtype=bool)
+        assert (~ref["kept"]).any() or s.capacity_factor >= 1.0
+    else:
+        ref = O.moe_forward(lay, tokens=rows)
+        same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
+        mar = margins(ref["keys"], s)
+        assert np.all(same | (mar <= MARGIN)), "routing differs away from a near tie"
     got = act_to_f64(out, s.act_dtype)[rows]
     diff = np.max(np.abs(got[same] - ref["out"][same]))
     scale = np.max(np.abs(ref["out"][same]))
     print(f"{name}: max|d|/max|ref| = {diff / scale:.3e} over {same.sum()} rows")
     assert diff <= TOL[s.act_dtype] * scale
+
+
+@pytest.mark.parametrize("name", ["balance_bf16", "small_f32"])
+def test_forward_load_stats_match_oracle(name):
+    """The statistics moe_forward_ex writes for its own routing: f from the GPU routing
+    exactly, p and the loss against the oracle's fp64 scores."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    cfg = config(s)
+    wts = weights(lay)
+    ws = workspace(cfg)
+    out = act_empty((s.T, s.d), s.act_dtype)
+    st = torch.empty(2 * s.E + 1, dtype=torch.float32, device="cuda")
+    moe.forward(cfg, wts, to_dev(lay.x), out, ws, load_stats=st, aux_alpha=0.5)
+    torch.cuda.synchronize()
+    gpu_idx = ws[: s.T * s.k * 4].view(torch.int32).cpu().numpy().reshape(s.T, s.k)
+    r = O.route(lay)
+    rf, rp, rl = O.load_stats(r["scores"], gpu_idx, s.E, 0.5)
+    got = st.cpu().numpy()
+    assert np.array_equal(got[: s.E], rf.astype(np.float32))
+    assert np.allclose(got[s.E: 2 * s.E], rp, rtol=1e-4, atol=1e-6)
+    assert abs(got[2 * s.E] - rl) <= 1e-4 * abs(rl)
+    # the forward's output does not depend on whether statistics were asked for
+    out2 = torch.empty_like(out)
+    moe.forward(cfg, wts, to_dev(lay.x), out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
 
 
 @pytest.mark.parametrize("name", ["fusionllm_bf16", "small_swiglu_e4m3", "tiny_fp32"])

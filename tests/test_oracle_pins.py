@@ -556,6 +556,17 @@ def test_forward_with_capacity_brute_force():
     assert np.allclose(sub["out"], r["out"][[4, 1]], rtol=1e-13, atol=0)
 
 
+def test_forward_with_its_own_routing_given_is_unchanged():
+    shape = W.small_shape(act_dtype="f32", weight_dtype="f32", T=9, d=6, E=4, k=2, S=1, I=3,
+                          G=2, Gk=1, score="sigmoid", capacity_factor=0.75, select_bias_std=0.5)
+    lay = W.make_layer(shape, cache=False)
+    a = O.moe_forward(lay)
+    b = O.moe_forward(lay, idx=a["idx"])
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["kept"], b["kept"])
+    c = O.moe_forward(lay, tokens=np.array([2, 7]), idx=a["idx"])
+    assert np.allclose(c["out"], a["out"][[2, 7]], rtol=1e-13, atol=0)
+
+
 # ----------------------------------------------------------------------------- workloads
 def test_fusionllm_shapes_match_the_yaml():
     y = json.load(open(os.path.join(GOLDEN, "fusionllm_moe_yaml.json")))
