@@ -53,6 +53,9 @@ design notes):
   divided by T k; p_e averages each token's scores normalised to sum 1 over the E experts.
 * Capacity: floor(c T k / E) rows per expert; each expert keeps its rows in token order
   and drops the rest (dropped slots contribute zero; weights are not renormalised).
+* e4m3 activations (optional, with e4m3 weights): each token's x row is quantised with
+  its own scale max|x|/448 in fp32 steps (RNE, saturating) before the up projections;
+  the router and the down projections are unchanged.
 """
 from __future__ import annotations
 
@@ -65,7 +68,8 @@ __all__ = [
     "group_scores", "select_experts", "routing_weights", "route", "silu", "expert_ffn",
     "expert_up", "expert_down", "combine",
     "moe_forward", "permute", "expert_weights", "shared_weights", "decode_act",
-    "selection_keys", "load_stats", "expert_capacity",
+    "selection_keys", "load_stats", "expert_capacity", "quantize_rows_e4m3",
+    "dequantize_rows_e4m3",
 ]
 
 
@@ -202,6 +206,52 @@ def route(layer, tokens=None):
     return {"x": x, "logits": l, "scores": sc, "keys": keys, "idx": idx, "w": w}
 
 
+# ----------------------------------------------------------------------------- e4m3 activations
+def _e4m3_rne_magnitude(v32):
+    """|v| (fp32, <= 448) to the nearest e4m3 magnitude code, ties to even.  Normal codes
+    (|v| >= 2^-6) keep 3 mantissa bits of the fp32 value; subnormals are multiples of
+    2^-9.  Returns codes 0..126."""
+    a = np.abs(np.asarray(v32, np.float64))
+    codes = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    m_sub = np.rint(a[sub] * 512.0).astype(np.int64)        # exact scaling; rint = RNE
+    codes[sub] = m_sub                                      # m = 8 is the smallest normal
+    nrm = ~sub
+    e = np.floor(np.log2(a[nrm])).astype(np.int64)          # exact for fp32 inputs
+    frac = a[nrm] / np.ldexp(1.0, e) - 1.0                  # in [0, 1), exact
+    m = np.rint(frac * 8.0).astype(np.int64)                # RNE on the 3-bit mantissa
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    codes[nrm] = (e + 7) * 8 + m
+    return codes
+
+
+def quantize_rows_e4m3(a):
+    """Per-row e4m3 quantisation of activations, in the kernel's fp32 steps: scale =
+    fp32(max|a_row|) / 448 (fp32 division), v = a / scale (fp32 division), clamp |v| to
+    448, round to the nearest e4m3 value with ties to even, keep the sign.  A row of zeros
+    has scale 0 and codes 0.  Returns (codes uint8 [rows, cols], scales float32 [rows]).
+    [MoE-Eng] section "生产现实：前沿实验室真正交付的内容", FP8 item (E4M3 products with FP32
+    accumulation); the per-token
+    scale is the reading taken for activations."""
+    a32 = np.asarray(a, np.float32)
+    amax = np.max(np.abs(a32), axis=1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    v = (a32 / safe[:, None]).astype(np.float32)
+    mag = np.minimum(np.abs(v), np.float32(448.0))
+    codes = _e4m3_rne_magnitude(mag)
+    codes = np.where(scale[:, None] > 0, codes, 0)
+    sign = (v < 0) & (codes > 0)
+    out = (codes | np.where(sign, 0x80, 0)).astype(np.uint8)
+    return out, scale
+
+
+def dequantize_rows_e4m3(codes, scale):
+    return decode_e4m3(codes) * np.asarray(scale, np.float64)[:, None]
+
+
 # ----------------------------------------------------------------------------- load statistics
 def load_stats(scores, idx, E: int, alpha: float = 1.0):
     """Per-batch load statistics of the router and the Switch auxiliary-loss value.
@@ -311,16 +361,21 @@ def moe_forward(layer, tokens=None, idx=None):
         kept_all = slot_pos.reshape(s.T, s.k) >= 0
         kept = kept_all if tokens is None else kept_all[np.asarray(tokens)]
     r["kept"] = kept
+    # with e4m3 activations the up projections see each token's quantised row (the router
+    # keeps the unquantised x)
+    xa = x
+    if getattr(s, "fp8_act", False):
+        xa = dequantize_rows_e4m3(*quantize_rows_e4m3(x))
     out = np.zeros_like(x)
     for e in range(s.E):
         rows, slots = np.nonzero((idx_t == e) & kept)
         if rows.size == 0:
             continue
         w1, w3, w2 = expert_weights(layer, e)
-        out[rows] += w[rows, slots][:, None] * expert_ffn(x[rows], w1, w3, w2, s.act)
+        out[rows] += w[rows, slots][:, None] * expert_ffn(xa[rows], w1, w3, w2, s.act)
     for i in range(s.S):
         w1, w3, w2 = shared_weights(layer, i)
-        out += expert_ffn(x, w1, w3, w2, s.act)
+        out += expert_ffn(xa, w1, w3, w2, s.act)
     r["out"] = out
     return r
 

@@ -567,6 +567,75 @@ def test_forward_with_its_own_routing_given_is_unchanged():
     assert np.allclose(c["out"], a["out"][[2, 7]], rtol=1e-13, atol=0)
 
 
+# ----------------------------------------------------------------------------- e4m3 activations
+def _quant_inputs():
+    rng = np.random.default_rng(44)
+    a = (rng.standard_normal((40, 256)) * rng.random((40, 1)) * 20).astype(np.float32)
+    a[0] = 0.0                                                   # zero row
+    a[1] = np.float32(1e-3) * rng.standard_normal(256).astype(np.float32)
+    a[2, :] = 0.0
+    a[2, 0] = 7.0                                                # a single non-zero
+    a[3] = np.linspace(-448 * 2.0 ** -9, 448 * 2.0 ** -9, 256, dtype=np.float32)   # subnormals
+    return a
+
+
+def test_activation_quantiser_matches_torch_e4m3():
+    """Codes: torch's float8_e4m3fn conversion (round to nearest even) of the same fp32
+    quotients a / scale, each computed with one fp32 division."""
+    a = _quant_inputs()
+    codes, scale = O.quantize_rows_e4m3(a)
+    amax = np.abs(a).max(axis=1)
+    assert np.array_equal(scale, (amax / np.float32(448.0)).astype(np.float32))
+    safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+    v = np.clip((a / safe[:, None]).astype(np.float32), -448, 448)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ref = np.where(scale[:, None] > 0, ref, 0)
+    ref = np.where(ref == 0x80, 0, ref)                          # -0 is stored as +0
+    assert np.array_equal(codes, ref)
+    assert codes[0].max() == 0 and scale[0] == 0
+    assert codes[2, 0] == 0x7E                                   # the row max maps to 448
+
+
+def test_activation_quantiser_error_bound():
+    """Half an e4m3 ulp: 2^-4 relative for normals, 2^-10 * scale absolute below 2^-6."""
+    a = _quant_inputs()
+    codes, scale = O.quantize_rows_e4m3(a)
+    dq = O.dequantize_rows_e4m3(codes, scale)
+    a64 = a.astype(np.float64)
+    for r in range(a.shape[0]):
+        if scale[r] == 0:
+            assert np.all(dq[r] == 0)
+            continue
+        v = np.abs(a64[r]) / float(scale[r])
+        err = np.abs(dq[r] - a64[r])
+        normal = v >= 2.0 ** -6
+        assert np.all(err[normal] <= 2.0 ** -4 * np.abs(a64[r][normal]) * (1 + 1e-6))
+        assert np.all(err[~normal] <= 2.0 ** -10 * float(scale[r]) * (1 + 1e-6))
+
+
+def test_forward_with_e4m3_activations_is_the_forward_of_the_dequantised_rows():
+    shape = W.small_shape(act_dtype="bf16", weight_dtype="e4m3", T=7, d=64, E=4, k=2, S=1, I=64,
+                          G=1, Gk=1, act="relu2", fp8_act=True)
+    lay = W.make_layer(shape, cache=False)
+    r = O.moe_forward(lay)
+    x = O.decode_bf16(lay.x)
+    xq = O.dequantize_rows_e4m3(*O.quantize_rows_e4m3(x))
+    assert not np.array_equal(xq, x)
+    for t in range(7):
+        ref = np.zeros(64)
+        for j in range(2):
+            e = int(r["idx"][t, j])
+            w1, _, w2 = O.expert_weights(lay, e)
+            ref += r["w"][t, j] * np.array(_bf_ffn(xq[t].tolist(), w1.tolist(), None, w2.tolist(), "relu2"))
+        w1, _, w2 = O.shared_weights(lay, 0)
+        ref += np.array(_bf_ffn(xq[t].tolist(), w1.tolist(), None, w2.tolist(), "relu2"))
+        assert np.allclose(r["out"][t], ref, rtol=1e-10, atol=1e-12)
+    # routing uses the unquantised x: same selection as the layer without e4m3 activations
+    plain = W.make_layer(W.small_shape(act_dtype="bf16", weight_dtype="e4m3", T=7, d=64, E=4, k=2,
+                                       S=1, I=64, G=1, Gk=1, act="relu2"), cache=False)
+    assert np.array_equal(O.route(plain)["idx"], r["idx"])
+
+
 # ----------------------------------------------------------------------------- workloads
 def test_fusionllm_shapes_match_the_yaml():
     y = json.load(open(os.path.join(GOLDEN, "fusionllm_moe_yaml.json")))
@@ -603,7 +672,8 @@ def _swapped_ffn(x, w1, w3, w2, act):
 
 @pytest.mark.parametrize("mutation", ["swap_gate_up", "no_renorm", "tie_high_index",
                                       "token_desc_perm", "drop_shared", "transpose_down",
-                                      "biased_weights", "keep_last_at_capacity"])
+                                      "biased_weights", "keep_last_at_capacity",
+                                      "truncating_quantiser"])
 def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
     """Each mutation is a plausible slip in the oracle; the named pin must then fail."""
     if mutation == "swap_gate_up":
@@ -659,6 +729,15 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
             return rev[0], rev[1], (T - 1 - rev[2]).astype(np.int32), sp
         monkeypatch.setattr(O, "permute", bad)
         check = test_capacity_keeps_each_experts_first_tokens_python_sorted
+    elif mutation == "truncating_quantiser":
+        orig = O.moe_oracle._e4m3_rne_magnitude
+        def trunc(v32):
+            a = np.abs(np.asarray(v32, np.float64))
+            c = orig(a)
+            up = O.decode_e4m3(c.astype(np.uint8)) > a           # rounded up: step back
+            return np.where(up, c - 1, c)
+        monkeypatch.setattr(O.moe_oracle, "_e4m3_rne_magnitude", trunc)
+        check = test_activation_quantiser_matches_torch_e4m3
     elif mutation == "drop_shared":
         monkeypatch.setattr(O.moe_oracle, "shared_weights",
                             lambda lay, i: tuple(np.zeros_like(a) if a is not None else None

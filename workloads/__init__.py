@@ -58,6 +58,7 @@ class MoeShape:
     x_from: Optional[str] = None     # take x rows (and weights) of another shape
     capacity_factor: Optional[float] = None   # expert capacity c*T*k/E (None: unlimited)
     select_bias_std: Optional[float] = None   # selection-only per-expert bias ~ N(0, std^2)
+    fp8_act: bool = False  # up projections take e4m3 activations with per-token scales
 
     @property
     def flops_per_token(self) -> int:
@@ -86,13 +87,18 @@ SHAPES = {
     "fp8_relu2": MoeShape("fp8_relu2", T=16384, d=2048, E=64, k=6, score="sigmoid", G=8,
                           Gk=4, S=4, I=1536, act="relu2", act_dtype="bf16",
                           weight_dtype="e4m3", seed=4),
+    # the e4m3 layer with the up projections on e4m3 x e4m3 products (per-token scales)
+    "fp8a_relu2": MoeShape("fp8a_relu2", T=16384, d=2048, E=64, k=6, score="sigmoid", G=8,
+                           Gk=4, S=4, I=1536, act="relu2", act_dtype="bf16",
+                           weight_dtype="e4m3", seed=4, x_from="fp8_relu2", fp8_act=True),
     # the prefill layer with a selection-only expert bias and capacity factor 1.25
     "balance_bf16": MoeShape("balance_bf16", T=4096, d=2048, E=64, k=6, score="sigmoid", G=8,
                              Gk=4, S=4, I=1536, act="swiglu", act_dtype="bf16",
                              weight_dtype="bf16", seed=1, x_from="fusionllm_bf16",
                              capacity_factor=1.25, select_bias_std=0.5),
 }
-ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2", "balance_bf16"]
+ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2", "balance_bf16",
+         "fp8a_relu2"]
 
 
 def shape_by_name(name: str) -> MoeShape:
