@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
@@ -71,7 +72,8 @@ class Runner:
         self.cfg = moe.make_config(s.T, s.d, s.E, s.k, G=s.G, Gk=s.Gk, n_g=s.n_g, S=s.S, I=s.I,
                                    score=s.score, renormalize=s.renormalize,
                                    route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
-                                   weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor)
+                                   weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor,
+                                   fp8_act=s.fp8_act)
         names = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                  "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]
         if weights is None:
@@ -233,6 +235,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
@@ -326,6 +329,25 @@ def main(argv=None):
                           "rows_kept_frac": float(counts.sum()) / (bshape.T * bshape.k),
                           "aux_loss_alpha1": float(stv[2 * bshape.E]),
                           "max_f_over_mean": float(stv[:bshape.E].max() * bshape.E)}
+    if not args.no_fp8 and shape.name == "fusionllm_bf16":
+        # the e4m3-weight layer (T = 16384, ReLU^2): bf16 activations, then e4m3 activations
+        # in the up projections (same device weights)
+        f8 = {}
+        base = None
+        for name in ("fp8_relu2", "fp8a_relu2"):
+            fshape = W.SHAPES[name]
+            frun = Runner(fshape, W.make_layer(fshape), weights=base)
+            base = frun.w
+            f_ms, _ = frun.timed(max(5, args.steps // 4), args.warmup)
+            up_ms = frun.staged(max(5, args.steps // 4), args.warmup, stages=[2, 3])["up_routed"]
+            ffl = stage_flops(fshape, fshape.T)
+            f8[name] = {"ms_per_step": f_ms, "tokens_per_s": fshape.T / (f_ms * 1e-3),
+                        "up_routed_ms": up_ms,
+                        "up_routed_tflops": ffl["up_routed"] / (up_ms * 1e-3) / 1e12}
+        up_a8 = f8["fp8a_relu2"]["up_routed_tflops"]
+        f8["fp8a_relu2"]["up_routed_frac_of_fp8_peak"] = up_a8 / PEAK_FP8_TFLOPS
+        f8["fp8_relu2"]["up_routed_frac_of_bf16_peak"] = f8["fp8_relu2"]["up_routed_tflops"] / PEAK_BF16_TFLOPS
+        res["fp8"] = f8
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(lay, min(args.cpu_tokens, shape.T), args.cpu_seconds)
     print(json.dumps(res))

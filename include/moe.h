@@ -78,6 +78,12 @@ typedef struct {
                                 contribute nothing); c <= 0: unlimited (no dropping).
                                 Source: expert capacity c|T|k/E and token dropping, section
                                 "MoE 数学：路由、容量与平衡详解" of "大模型工程（一）"   */
+  int32_t fp8_act;           /* 1: the up projections multiply e4m3 activations (each token
+                                row quantised with scale max|x|/448, moe_quantize_rows) by the
+                                e4m3 weights, fp32 accumulation; needs act_dtype MOE_BF16 and
+                                weight_dtype MOE_FP8_E4M3.  0: bf16 activations.
+                                Source: FP8 E4M3 products with FP32 accumulation, section
+                                "生产现实：前沿实验室真正交付的内容" of "大模型工程（一）"  */
 } moe_config;
 
 /* Expert weights.  [out, in] per expert, stacked on dim 0.  e4m3 weights carry one fp32
@@ -164,6 +170,16 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
                        int32_t* slot_pos, float* perm_weight, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Per-row e4m3 quantisation of bf16 rows a [rows, cols] (cols a multiple of 8):
+ *   scale[r] = max_c |a[r, c]| / 448                    (fp32 division)
+ *   q[r, c]  = e4m3(clamp(a[r, c] / scale[r], +-448))   (fp32 division, nearest even)
+ * A row of zeros gets scale 0 and codes 0.  q [rows, cols] uint8 (8-byte aligned),
+ * scale [rows] fp32.  Needs cfg->act_dtype MOE_BF16.
+ * Source: FP8 E4M3 with FP32 accumulation, section "生产现实：前沿实验室真正交付的内容" of
+ * "大模型工程（一）：Transformer 到 MoE"; the per-token scale is this library's reading. */
+moe_status moe_quantize_rows(const moe_config* cfg, const void* a, int32_t rows, int32_t cols,
+                             uint8_t* q, float* scale, hipStream_t stream);
+
 /* One stage of the expert FFNs as a grouped GEMM over expert segments.
  *   set = MOE_EXPERTS_ROUTED: segment e is rows [offsets[e], offsets[e+1]) of a row space
  *         of `rows` rows (offsets: device [E+1], from moe_permute); routed weights.
@@ -178,6 +194,8 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const flo
  *               row_weight[r] * (a_r W_down^T) (row_weight NULL = 1), [rows, d], act_dtype;
  *               for the shared set the S experts' outputs are summed.
  * e4m3 weights are multiplied by their per-output-channel scales.  fp32 accumulation.
+ * With cfg->fp8_act the UP stage takes a = e4m3 codes (moe_quantize_rows) and row_weight
+ * = the per-row scales of a (indexed like a, i.e. through row_index); it is required.
  * ws / ws_bytes: reserved, may be NULL / 0.
  * Source: grouped GEMM after routing and the fused Linear+ReLU^2 kernel, section
  * "融合内核" of the FusionLLM training-framework page; SwiGLU in item 3 of section

@@ -14,8 +14,8 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
-    "workspace_size", "route", "select", "load_stats", "permute", "grouped_gemm", "combine",
-    "forward",
+    "workspace_size", "route", "select", "load_stats", "permute", "quantize_rows",
+    "grouped_gemm", "combine", "forward",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
     "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
@@ -29,8 +29,8 @@ MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 
 EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_load_stats",
-                    "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_forward",
-                    "moe_forward_ex", "moe_status_string", "moe_last_hip_error"]
+                    "moe_permute", "moe_quantize_rows", "moe_grouped_gemm", "moe_combine",
+                    "moe_forward", "moe_forward_ex", "moe_status_string", "moe_last_hip_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -58,7 +58,7 @@ class Config(ctypes.Structure):
         ("inter_dim", ctypes.c_int32), ("score_fn", ctypes.c_int32),
         ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float),
         ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_float),
+        ("capacity_factor", ctypes.c_float), ("fp8_act", ctypes.c_int32),
     ]
 
 
@@ -108,6 +108,7 @@ def lib():
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_grouped_gemm": [cfgp, i32, i32, vp, vp, vp, i32, wp, vp, vp, vp, sz, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
+            "moe_quantize_rows": [cfgp, vp, i32, i32, vp, vp, vp],
             "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
             "moe_forward_ex": [cfgp, wp, vp, vp, vp, sz, vp, ctypes.POINTER(_OptsC)],
             "moe_last_hip_error": [],
@@ -151,7 +152,7 @@ def _check(status: int, what: str):
 
 def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renormalize=True,
                 route_scale=1.0, act="swiglu", act_dtype="bf16", weight_dtype="bf16",
-                capacity_factor=0.0) -> Config:
+                capacity_factor=0.0, fp8_act=False) -> Config:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3}
     return Config(num_tokens=T, dim=d, num_experts=E, top_k=k, num_groups=G, topk_groups=Gk,
                   group_score_topn=n_g, num_shared=S, inter_dim=I,
@@ -159,7 +160,7 @@ def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renorm
                   renormalize=int(bool(renormalize)), route_scale=float(route_scale),
                   act={"swiglu": MOE_ACT_SWIGLU, "relu2": MOE_ACT_RELU2}[act],
                   act_dtype=dt[act_dtype], weight_dtype=dt[weight_dtype],
-                  capacity_factor=float(capacity_factor or 0.0))
+                  capacity_factor=float(capacity_factor or 0.0), fp8_act=int(bool(fp8_act)))
 
 
 def workspace_size(cfg: Config) -> int:
@@ -201,6 +202,11 @@ def grouped_gemm(cfg, stage, expert_set, a, row_index, offsets, rows, weights: W
                                   _ptr(row_index), _ptr(offsets), int(rows),
                                   ctypes.byref(weights.c), _ptr(row_weight), _ptr(out), _ptr(ws),
                                   nb, _stream(stream)), "moe_grouped_gemm")
+
+
+def quantize_rows(cfg, a, rows, cols, q, scale, stream=None):
+    _check(lib().moe_quantize_rows(ctypes.byref(cfg), _ptr(a), int(rows), int(cols), _ptr(q),
+                                   _ptr(scale), _stream(stream)), "moe_quantize_rows")
 
 
 def combine(cfg, y_perm, slot_pos, y_shared, out, stream=None):

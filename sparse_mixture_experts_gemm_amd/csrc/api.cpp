@@ -56,11 +56,14 @@ moe_status check_config(const moe_config* c) {
   if (c->act != MOE_ACT_SWIGLU && c->act != MOE_ACT_RELU2) return MOE_ERR_INVALID_ARG;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  if (c->fp8_act != 0 && c->fp8_act != 1) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
   // implemented combinations and shapes
   if (E > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->fp8_act && (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_FP8_E4M3))
+    return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_F32) {
     if (c->weight_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (c->dim % 16 != 0 || c->inter_dim % 16 != 0) return MOE_ERR_UNSUPPORTED;
@@ -112,7 +115,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Workspace of moe_forward, in carve order.
 struct Carve {
   size_t topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, perm_ws;
-  size_t scores, stats_ws;
+  size_t scores, stats_ws, x_q, x_scale;
   size_t h_routed, h_shared, y_routed, y_shared, total;
 };
 
@@ -133,6 +136,8 @@ Carve carve(const moe_config* c) {
   w.perm_ws = take(moe::permute_ws_bytes((int)T, (int)E));
   w.scores = take(T * E * 4);                    // only written when statistics are asked
   w.stats_ws = take(moe::stats_ws_bytes((int)T, (int)E));
+  w.x_q = take(c->fp8_act ? T * d : 0);          // e4m3 activations of the up projections
+  w.x_scale = take(c->fp8_act ? T * 4 : 0);
   w.h_routed = take(T * k * I * as);
   w.h_shared = take(T * S * I * as);
   w.y_routed = take(T * k * d * as);
@@ -304,6 +309,8 @@ moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_s
     moe_status st = check_config(cfg);
     if (st != MOE_OK) return st;
     if (rows == 0) return MOE_OK;
+    const bool a8 = cfg->fp8_act && stage == MOE_STAGE_UP;
+    if (a8 && row_weight == nullptr) return MOE_ERR_INVALID_ARG;   // the A-row scales
     moe::GemmParams p;
     st = gemm_params(cfg, stage, set, a, row_index, offsets, rows, w, row_weight, out, &p);
     if (st != MOE_OK) return st;
@@ -312,7 +319,7 @@ moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_s
     if (st != MOE_OK) return st;
     return hip_status(moe::launch_grouped_gemm(
         p, stage == MOE_STAGE_UP ? moe::Stage::Up : moe::Stage::Down, cfg->act, cfg->act_dtype,
-        cfg->weight_dtype, cus, stream));
+        cfg->weight_dtype, cus, stream, a8));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -329,6 +336,23 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
       return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_combine(cfg->num_tokens, cfg->dim, cfg->top_k, cfg->act_dtype,
                                           y_perm, slot_pos, y_shared, out, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_quantize_rows(const moe_config* cfg, const void* a, int32_t rows, int32_t cols,
+                             uint8_t* q, float* scale, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (a == nullptr || q == nullptr || scale == nullptr) return MOE_ERR_INVALID_ARG;
+    if (cfg->act_dtype != MOE_BF16 || cols % 8 != 0) return MOE_ERR_UNSUPPORTED;
+    if ((long long)rows * cols > INT_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(a) || (reinterpret_cast<uintptr_t>(q) & 7u) != 0) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_quant_rows(rows, cols, a, q, scale, stream));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -359,16 +383,19 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     const bool shared = cfg->num_shared > 0;
 
     // validate every grouped-GEMM argument before the first launch
+    const bool a8 = cfg->fp8_act != 0;
+    const void* x_up = a8 ? at(cv.x_q) : x;                   // rows of the up projections
+    const float* x_up_scale = a8 ? static_cast<const float*>(at(cv.x_scale)) : nullptr;
     moe::GemmParams up_r, up_s{}, dn_r, dn_s{};
-    st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_ROUTED, x, perm_token, offsets, Tk, w,
-                     nullptr, at(cv.h_routed), &up_r);
+    st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_ROUTED, x_up, perm_token, offsets, Tk, w,
+                     x_up_scale, at(cv.h_routed), &up_r);
     if (st != MOE_OK) return st;
     st = gemm_params(cfg, MOE_STAGE_DOWN, MOE_EXPERTS_ROUTED, at(cv.h_routed), nullptr, offsets,
                      Tk, w, perm_weight, at(cv.y_routed), &dn_r);
     if (st != MOE_OK) return st;
     if (shared) {
-      st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_SHARED, x, nullptr, nullptr, T, w, nullptr,
-                       at(cv.h_shared), &up_s);
+      st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_SHARED, x_up, nullptr, nullptr, T, w,
+                       x_up_scale, at(cv.h_shared), &up_s);
       if (st != MOE_OK) return st;
       st = gemm_params(cfg, MOE_STAGE_DOWN, MOE_EXPERTS_SHARED, at(cv.h_shared), nullptr, nullptr,
                        T, w, nullptr, at(cv.y_shared), &dn_s);
@@ -402,11 +429,14 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                                  opts->load_stats, opts->load_stats + E,
                                  opts->load_stats + 2 * E, at(cv.stats_ws), stream);
     }
+    if (a8 && e == hipSuccess)
+      e = moe::launch_quant_rows(T, cfg->dim, x, static_cast<uint8_t*>(at(cv.x_q)),
+                                 static_cast<float*>(at(cv.x_scale)), stream);
     mark(2);
     // few rows per expert: the routed and shared experts stream their weights in one
-    // launch per stage
+    // launch per stage (bf16 activations only)
     const int adt = cfg->act_dtype;
-    const bool decode = moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
+    const bool decode = !a8 && moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
                         (!shared || (moe::decode_gemm_applies(up_s, adt) &&
                                      moe::decode_gemm_applies(dn_s, adt)));
     if (decode) {
@@ -423,11 +453,11 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     } else {
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
-                                     stream);
+                                     stream, a8);
       mark(3);
       if (shared && e == hipSuccess)
         e = moe::launch_grouped_gemm(up_s, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
-                                     stream);
+                                     stream, a8);
       mark(4);
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,

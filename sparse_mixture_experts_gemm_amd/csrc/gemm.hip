@@ -177,14 +177,21 @@ __device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
 // Tile shapes: 256 x 256 when the problem gives every CU at least two such tiles, else
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
-template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
+template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
+          bool A8 = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   constexpr int BK = 64;
   constexpr int WM = 2, WN = WAVES / 2;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   constexpr bool SWIGLU = (STAGE == 0) && (ACT == MOE_ACT_SWIGLU);
-  constexpr int AROW = BK * 2;                      // bytes per A row in LDS
+  // A8: e4m3 activations and weights, v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) on
+  // 64-byte LDS rows; every lane reads 32 bytes of a row as two 16-byte chunks, swizzled
+  // by (row >> 2) & 3 so that 16 consecutive rows hit distinct 16-byte bank groups
+  static_assert(!A8 || (FP8 && STAGE == 0), "e4m3 activations: up projection, e4m3 weights");
+  constexpr int ESZ_A = A8 ? 1 : 2;                 // bytes per A element
+  constexpr int AROW = BK * ESZ_A;                  // bytes per A row in LDS
+  constexpr int CPR_A = AROW / 16;                  // 16-byte chunks per A row
   constexpr int BROW = FP8 ? BK : BK * 2;           // bytes per B row in LDS
   constexpr int A_BYTES = BM * AROW, B_BYTES = BN * BROW, ST_BYTES = A_BYTES + B_BYTES;
   constexpr int A_DMA = A_BYTES / 1024, B_DMA = B_BYTES / 1024;   // 1 KB per DMA instruction
@@ -193,6 +200,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   static_assert((A_DMA + B_DMA) % WAVES == 0, "DMA split");
   static_assert(!SWIGLU || FN % 2 == 0, "SwiGLU pairs gate/up MFMA tiles");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
+  auto swz_a = [](int r) { return A8 ? ((r >> 2) & 3) : swz8(r); };   // A rows
+  auto swz_b8 = [](int r) { return A8 ? ((r >> 2) & 3) : swz4(r); };  // e4m3 B rows
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
 
@@ -228,14 +237,16 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
 
   const unsigned char* a_base = static_cast<const unsigned char*>(p.a);
   const bool gather = p.row_index != nullptr;
-  const bool has_rw = STAGE == 1 && p.row_weight != nullptr;
+  // per-row factor staged with the tile: the routing weight (DOWN) or, for e4m3
+  // activations, the scale of the A row (UP; indexed like A, through row_index)
+  const bool has_rw = (STAGE == 1 || A8) && p.row_weight != nullptr;
   // Per-row data (gathered A rows, row weights) is staged in LDS by the epilogue two tiles
   // before its use, which needs a tile's slices to span at least NSTAGE - 1 steps; global
   // loads issued in the main loop would make the compiler's waits drain the DMA stream.
   const bool prefetch = (gather || has_rw) && nk >= NSTAGE - 1;
   const int nblk_k = K / p.kblock;
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
-  const int sw = swz8(lane & 31);      // swizzle of every operand row this lane reads
+  const int sw = swz_a(lane & 31);     // swizzle of every A operand row this lane reads
 
   auto tile_at = [&](int j) {
     return decode_tile(first + j * per_x, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       if (tid < BM) {
         const int sr = seg_row(tc, tid);
         if (gather) s_arow[j][tid] = p.row_index[sr];
-        if (has_rw) s_rw[j][tid] = p.row_weight[sr];
+        if (has_rw) s_rw[j][tid] = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
       }
     }
     __syncthreads();
@@ -279,9 +290,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
       if (!is_b[i]) {
-        const int row = q * 8 + lane / 8;
+        const int row = q * (1024 / AROW) + lane / CPR_A;
         const int srow = gather ? s_arow[j & 1][row] : seg_row(tc, row);
-        src[i] = a_base + ((size_t)srow * K + ((lane & 7) ^ swz8(row)) * 8) * 2;
+        src[i] = a_base + (size_t)srow * K * ESZ_A + (size_t)(((lane % CPR_A) ^ swz_a(row)) * 16);
       } else {
         const int qb = q - A_DMA;
         const int n = FP8 ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;   // LDS row
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         wrow = wrow < N ? wrow : 0;
         const size_t e = seg_off + (size_t)wrow * p.kblock;
         src[i] = static_cast<const unsigned char*>(wb) +
-                 (FP8 ? e + ((lane & 3) ^ swz4(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
+                 (FP8 ? e + ((lane & 3) ^ swz_b8(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
       }
     }
   };
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     }
     const int k0 = ikt * BK;
     const uint32_t st = lds_base + (uint32_t)(ist * ST_BYTES);
-    const size_t aoff = (size_t)k0 * 2;
+    const size_t aoff = (size_t)k0 * ESZ_A;
     const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
     const size_t boff = FP8 ? koff : koff * 2;
 #pragma unroll
@@ -415,7 +426,32 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     };
     // a wave whose rows of the tile are all past the end of the segment (the upper half
     // of an expert's last 256-row tile) skips its LDS reads and MFMAs
-    if (wave_rows > 0) {
+    if (A8) {
+      if (wave_rows > 0) {
+        // one 32x32x64 e4m3 MFMA per block and K-slice: lane half h holds K bytes
+        // [32 h, 32 h + 32) of its row in both operands
+        typedef int v8i __attribute__((ext_vector_type(8)));
+        const int h = lane >> 5;
+        auto frag8 = [&](const unsigned char* base, int row) {
+          const int z = (row >> 2) & 3;
+          const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 64 + (((2 * h) ^ z) << 4));
+          const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 64 + (((2 * h + 1) ^ z) << 4));
+          return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        v8i a8[FM], b8[FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) b8[fn] = frag8(B, wn * WTN + fn * 32 + (lane & 31));
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                b8[fn], a8[fm], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+      }
+    } else if (wave_rows > 0) {
       load_frags(0, af[0], bfr[0]);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -439,12 +475,15 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       if (pf) {
         const int sr = seg_row(tile_at(j + 2), tid);
         if (gather) pf_row = p.row_index[sr];
-        if (has_rw) pf_w = p.row_weight[sr];
+        if (has_rw) pf_w = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
       }
       if (has_rw && !prefetch) {
         // short K: this tile's row weights are staged here (buffer j3 was last read by the
         // epilogue three tiles ago)
-        if (tid < BM) s_rw[j3][tid] = p.row_weight[seg_row(tc, tid)];
+        if (tid < BM) {
+          const int sr = seg_row(tc, tid);
+          s_rw[j3][tid] = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
+        }
         __syncthreads();
       }
       const int m0 = tc.m_tile * BM;
@@ -452,6 +491,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       // for them do not also wait for stores
       if (STAGE == 0) {
         constexpr int FH = SWIGLU ? FN / 2 : FN;
+        float ra[FM];   // e4m3 activations: the scale of each lane's A row
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) ra[fm] = (A8 && has_rw) ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
         float sg[FH][16], su[FH][16];
         if (FP8) {
 #pragma unroll
@@ -476,11 +518,11 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               if (SWIGLU) {
-                const float gv = FP8 ? acc[fm][fh][i] * sg[fh][i] : acc[fm][fh][i];
-                const float uv = FP8 ? acc[fm][fh + FN / 2][i] * su[fh][i] : acc[fm][fh + FN / 2][i];
+                const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
+                const float uv = FP8 ? acc[fm][fh + FN / 2][i] * (su[fh][i] * ra[fm]) : acc[fm][fh + FN / 2][i];
                 h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
               } else {
-                const float gv = FP8 ? acc[fm][fh][i] * sg[fh][i] : acc[fm][fh][i];
+                const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
                 const float rr = fmaxf(gv, 0.f);
                 h[i] = rr * rr;
               }
@@ -666,11 +708,28 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #define MOE_CFG_WIDE 256, 256, 8, 2, 1
 #endif
 
-template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8>
+// e4m3 activations: a K-slice is half the bytes, so the ring holds four slices
+#ifndef MOE_CFG_NARROW_A8
+#define MOE_CFG_NARROW_A8 128, 256, 8, 4, 1
+#endif
+#ifndef MOE_CFG_WIDE_A8
+#define MOE_CFG_WIDE_A8 256, 256, 8, 4, 1
+#endif
+
+template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
+          bool A8 = false>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_mfma_a8(const GemmParams& p, int num_cus, hipStream_t s) {
+  const long long bcols = ACT == MOE_ACT_SWIGLU ? 2LL * p.N : p.N;
+  const long long wide_tiles = ((p.rows + 255) / 256) * ((bcols + 255) / 256);
+  if (wide_tiles >= 2LL * num_cus) return launch_cfg<MOE_CFG_WIDE_A8, 0, ACT, true, true>(p, num_cus, s);
+  return launch_cfg<MOE_CFG_NARROW_A8, 0, ACT, true, true>(p, num_cus, s);
 }
 
 template <int STAGE, int ACT, bool FP8>
@@ -696,8 +755,13 @@ hipError_t launch_f32(const GemmParams& p, int num_cus, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
-                               int weight_dtype, int num_cus, hipStream_t s) {
+                               int weight_dtype, int num_cus, hipStream_t s, bool fp8_act) {
   if (p.rows == 0) return hipSuccess;
+  if (fp8_act) {
+    // e4m3 x e4m3 up projection (the caller checked stage, dtypes and the scales)
+    return act == MOE_ACT_RELU2 ? launch_mfma_a8<MOE_ACT_RELU2>(p, num_cus, s)
+                                : launch_mfma_a8<MOE_ACT_SWIGLU>(p, num_cus, s);
+  }
   const bool up = stage == Stage::Up;
   const bool relu2 = act == MOE_ACT_RELU2;
   if (act_dtype == MOE_F32) {

@@ -61,8 +61,15 @@ hipError_t launch_permute(int T, int E, int k, int capacity, const int32_t* idx,
                           int32_t* perm_token, int32_t* slot_pos, float* perm_weight, void* ws,
                           hipStream_t s);
 
+// Per-row e4m3 quantisation of bf16 rows [rows, cols] (cols a multiple of 8): codes
+// [rows, cols] and one fp32 scale per row.
+hipError_t launch_quant_rows(int rows, int cols, const void* a, uint8_t* q, float* scale,
+                             hipStream_t s);
+
+// fp8_act: UP stage on e4m3 activations (a = codes, row_weight = per-a-row scales) with
+// e4m3 weights.
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
-                               int weight_dtype, int num_cus, hipStream_t s);
+                               int weight_dtype, int num_cus, hipStream_t s, bool fp8_act = false);
 
 // Weight-streaming variant of the grouped GEMM for few rows per segment.  `second`, when
 // given, is a second segment set (e.g. the shared experts) run in the same launch.

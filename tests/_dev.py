@@ -27,7 +27,8 @@ def config(shape, T=None):
     return moe.make_config(s.T if T is None else T, s.d, s.E, s.k, G=s.G, Gk=s.Gk, n_g=s.n_g,
                            S=s.S, I=s.I, score=s.score, renormalize=s.renormalize,
                            route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
-                           weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor)
+                           weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor,
+                           fp8_act=s.fp8_act)
 
 
 def weights(lay):

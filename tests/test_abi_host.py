@@ -76,6 +76,7 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
     (dict(I=1000), 2), (dict(act_dtype="f32", weight_dtype="bf16"), 2),
     (dict(act_dtype="bf16", weight_dtype="f32"), 2),
     (dict(capacity_factor=float("nan")), 1),
+    (dict(fp8_act=True), 2),                       # e4m3 activations need e4m3 weights
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
     c = cfg(**bad)
@@ -122,6 +123,15 @@ def test_null_and_workspace_errors_are_reported_before_launch(lib):
                                 fake, None, 0, None) == 1
     # combine: null y
     assert lib.moe_combine(ctypes.byref(c), None, fake, None, fake, None) == 1
+    # quantize: null output, columns not a multiple of 8, fp32 activations
+    assert lib.moe_quantize_rows(ctypes.byref(c), fake, 4, 64, None, fake, None) == 1
+    assert lib.moe_quantize_rows(ctypes.byref(c), fake, 4, 60, fake, fake, None) == 2
+    c32 = moe.make_config(64, 64, 8, 2, I=64, act_dtype="f32", weight_dtype="f32")
+    assert lib.moe_quantize_rows(ctypes.byref(c32), fake, 4, 64, fake, fake, None) == 2
+    # grouped gemm with e4m3 activations: the up stage needs the row scales
+    ca8 = cfg(T=64, weight_dtype="e4m3", fp8_act=True)
+    assert lib.moe_grouped_gemm(ctypes.byref(ca8), 0, 1, fake, None, None, 10, ctypes.byref(w.c),
+                                None, fake, None, 0, None) == 1
     # load statistics: null outputs, missing workspace, non-finite alpha
     assert lib.moe_load_stats(ctypes.byref(c), fake, fake, 1.0, None, fake, fake, fake, 1 << 20,
                               None) == 1

@@ -47,6 +47,11 @@ SMALL = {
                                         select_bias_std=1.0, seed=41),
     "biased_groups_n2": W.small_shape(T=333, d=256, E=32, k=4, G=8, Gk=3, n_g=2, S=1, I=128,
                                       select_bias_std=0.7, capacity_factor=1.0, seed=42),
+    # e4m3 activations in the up projections (with e4m3 weights)
+    "small_a8_swiglu": W.small_shape(T=300, d=256, E=16, k=4, G=4, Gk=2, S=2, I=192,
+                                     weight_dtype="e4m3", fp8_act=True, seed=43),
+    "multi_tile_a8_relu2": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256,
+                                         act="relu2", weight_dtype="e4m3", fp8_act=True, seed=44),
     # K = 64: one K-slice per tile, several tiles per workgroup
     "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
 }
@@ -445,6 +450,65 @@ def test_grouped_gemm_shared(name):
     assert np.max(np.abs(got_y - ref_y)) <= TOL[s.act_dtype] * np.max(np.abs(ref_y))
 
 
+# ----------------------------------------------------------------------------- e4m3 activations
+@pytest.mark.parametrize("name", ["fusionllm_bf16", "small_a8_swiglu", "random_wide"])
+def test_quantize_rows_bit_exact(name):
+    if name == "random_wide":
+        rng = np.random.default_rng(45)
+        a32 = (rng.standard_normal((513, 1024)) * rng.random((513, 1)) * 30).astype(np.float32)
+        a32[0] = 0.0
+        a32[1] *= np.float32(1e-30)
+        a32[2, 5] = np.float32(-3e4)
+        x = W.encode_bf16(a32)
+    else:
+        x = layer_of(name).x
+    rows, cols = x.shape
+    cfg = moe.make_config(rows, cols, 8, 2, I=64, weight_dtype="e4m3", fp8_act=True)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    moe.quantize_rows(cfg, to_dev(x), rows, cols, q, sc)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_rows_e4m3(O.decode_bf16(x))
+    assert np.array_equal(sc.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("name", ["small_a8_swiglu", "multi_tile_a8_relu2", "fp8a_relu2"])
+def test_grouped_gemm_up_e4m3_activations(name):
+    """Routed and shared up projections on e4m3 activations: the oracle's codes and scales
+    in, every row (or a sample at full size) against the dequantised fp64 product."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    r = O.route(lay)
+    counts, offsets, perm_token, _ = O.permute(r["idx"], s.E)
+    Tk = s.T * s.k
+    xq, xs = O.quantize_rows_e4m3(r["x"])
+    xdq = O.dequantize_rows_e4m3(xq, xs)
+    cfg = config(s)
+    wts = weights(lay)
+    h = act_empty((Tk, s.I), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, to_dev(xq), to_dev(perm_token),
+                     to_dev(offsets), Tk, wts, to_dev(xs), h)
+    hs = act_empty((s.T, s.S * s.I), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_SHARED, to_dev(xq), None, None, s.T,
+                     wts, to_dev(xs), hs)
+    torch.cuda.synchronize()
+    rows = np.arange(Tk) if Tk <= 40000 else sample_tokens(Tk, n=1024, seed=5)
+    got = act_to_f64(h, s.act_dtype)[rows]
+    ref = np.zeros((len(rows), s.I))
+    for e in range(s.E):
+        sel = np.nonzero((rows >= offsets[e]) & (rows < offsets[e + 1]))[0]
+        if sel.size:
+            w1, w3 = _dense(lay, "up", e)
+            ref[sel] = O.expert_up(xdq[perm_token[rows[sel]]], w1, w3, s.act)
+    assert np.max(np.abs(got - ref)) <= TOL[s.act_dtype] * np.max(np.abs(ref))
+    trows = sample_tokens(s.T, n=512, seed=6)
+    ref_s = np.concatenate([O.expert_up(xdq[trows], *_dense(lay, "up", i, True), s.act)
+                            for i in range(s.S)], axis=1)
+    got_s = act_to_f64(hs, s.act_dtype)[trows]
+    assert np.max(np.abs(got_s - ref_s)) <= TOL[s.act_dtype] * np.max(np.abs(ref_s))
+
+
 # ----------------------------------------------------------------------------- combine
 @pytest.mark.parametrize("name,with_shared,cf", [("small_swiglu", True, None), ("small_f32", True, None),
                                                  ("fusionllm_bf16", True, None),
@@ -475,7 +539,7 @@ def test_combine(name, with_shared, cf):
 FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                  "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
                  "single_token", "topk1_nogroups", "balance_bf16", "biased_softmax_f32",
-                 "biased_groups_n2"]
+                 "biased_groups_n2", "fp8a_relu2", "small_a8_swiglu", "multi_tile_a8_relu2"]
 
 
 def run_forward(name):
