@@ -216,7 +216,12 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
 /* The whole layer: route -> permute -> UP/DOWN grouped GEMMs (routed and shared) ->
  * combine.  x [T, d] and out [T, d] act_dtype; ws at least moe_workspace_size bytes
  * (16-byte aligned).  The per-stage tensors (topk_idx, topk_w, counts, offsets,
- * perm_token, slot_pos, intermediates) live in ws. */
+ * perm_token, slot_pos, intermediates) live in ws.
+ * With shared experts and more rows than the one-launch decode path takes, the shared
+ * GEMMs run on a second stream that the library keeps per device (default priority,
+ * created on first use): it waits for everything queued on `stream` before the call,
+ * and `stream` waits for it before the combine, so the call is ordered on `stream` as a
+ * whole.  Stage events (moe_forward_ex) switch this off. */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 

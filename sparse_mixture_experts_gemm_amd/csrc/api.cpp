@@ -6,6 +6,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 #include "moe.h"
@@ -41,6 +42,29 @@ moe_status current_cus(int* cus) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A second stream per device for the shared experts, which do not depend on the routing:
+// their GEMMs overlap routing, permutation and the routed GEMMs.  Created on first use
+// (default priority, non-blocking) and kept until the process ends.
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices];
+
+moe_status side_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (g_side[dev] == nullptr) {
+    e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      g_side[dev] = nullptr;
+      return hip_status(e);
+    }
+  }
+  *out = g_side[dev];
+  return MOE_OK;
+}
 
 moe_status check_config(const moe_config* c) {
   if (c == nullptr) return MOE_ERR_INVALID_ARG;
@@ -413,11 +437,49 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     };
     const bool stats = opts != nullptr && opts->load_stats != nullptr;
     if (stats && !std::isfinite(opts->aux_alpha)) return MOE_ERR_INVALID_ARG;
+    bool events = false;
+    for (int i = 0; opts != nullptr && i < 8; ++i) events = events || opts->stage_events[i] != nullptr;
+    // few rows per expert: the routed and shared experts stream their weights in one
+    // launch per stage (bf16 activations only)
+    const int adt = cfg->act_dtype;
+    const bool decode = !a8 && moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
+                        (!shared || (moe::decode_gemm_applies(up_s, adt) &&
+                                     moe::decode_gemm_applies(dn_s, adt)));
+    // shared experts on a second stream, unless the stages are being timed one by one
+    const bool fork = shared && !decode && !events;
+    hipStream_t side = nullptr;
+    hipEvent_t fork_ev = nullptr, join = nullptr;
+    if (fork) {
+      st = side_stream(&side);
+      if (st != MOE_OK) return st;
+      hipError_t ce = hipEventCreateWithFlags(&fork_ev, hipEventDisableTiming);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+      if (ce != hipSuccess) {
+        if (fork_ev != nullptr) (void)hipEventDestroy(fork_ev);
+        return hip_status(ce);
+      }
+    }
+    if (a8)
+      e = moe::launch_quant_rows(T, cfg->dim, x, static_cast<uint8_t*>(at(cv.x_q)),
+                                 static_cast<float*>(at(cv.x_scale)), stream);
+    if (fork) {
+      if (e == hipSuccess) e = hipEventRecord(fork_ev, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side, fork_ev, 0);
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(up_s, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
+                                     side, a8);
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
+                                     cus, side);
+      if (e == hipSuccess) e = hipEventRecord(join, side);
+    }
     moe::RouteParams rp = route_params(cfg);
     rp.select_bias = w->select_bias;
     float* scores = stats ? static_cast<float*>(at(cv.scores)) : nullptr;
     mark(0);
-    e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw, stream);
+    if (e == hipSuccess)
+        e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw,
+                              stream);
     mark(1);
     if (e == hipSuccess)
       e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, expert_capacity(cfg), idx, tw,
@@ -429,16 +491,7 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                                  opts->load_stats, opts->load_stats + E,
                                  opts->load_stats + 2 * E, at(cv.stats_ws), stream);
     }
-    if (a8 && e == hipSuccess)
-      e = moe::launch_quant_rows(T, cfg->dim, x, static_cast<uint8_t*>(at(cv.x_q)),
-                                 static_cast<float*>(at(cv.x_scale)), stream);
     mark(2);
-    // few rows per expert: the routed and shared experts stream their weights in one
-    // launch per stage (bf16 activations only)
-    const int adt = cfg->act_dtype;
-    const bool decode = !a8 && moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
-                        (!shared || (moe::decode_gemm_applies(up_s, adt) &&
-                                     moe::decode_gemm_applies(dn_s, adt)));
     if (decode) {
       if (e == hipSuccess)
         e = moe::launch_decode_gemm(up_r, moe::Stage::Up, cfg->act, cfg->weight_dtype, stream,
@@ -450,6 +503,15 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                                     shared ? &dn_s : nullptr);
       mark(5);
       mark(6);
+    } else if (fork) {
+      // routed GEMMs here, shared GEMMs on the side stream since the start of the forward
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
+                                     stream, a8);
+      if (e == hipSuccess)
+        e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
+                                     cus, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
     } else {
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
@@ -472,6 +534,12 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
       e = moe::launch_combine(T, cfg->dim, cfg->top_k, adt, at(cv.y_routed), slot_pos,
                               shared ? at(cv.y_shared) : nullptr, out, stream);
     mark(7);
+    if (fork) {
+      // both events have been waited on or are pending in the streams: their resources
+      // are released once they complete
+      (void)hipEventDestroy(fork_ev);
+      (void)hipEventDestroy(join);
+    }
     return hip_status(e);
   } catch (...) {
     return MOE_ERR_INTERNAL;
