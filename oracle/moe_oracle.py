@@ -56,6 +56,10 @@ design notes):
 * e4m3 activations (optional, with e4m3 weights): each token's x row is quantised with
   its own scale max|x|/448 in fp32 steps (RNE, saturating) before the up projections;
   the router and the down projections are unchanged.
+* Pre-norm layer step (optional): the MoE input is RMSNorm(x) = x / sqrt(mean(x^2) + eps)
+  * gamma (no mean subtraction, a learned per-channel gain gamma), stored in the
+  activation dtype (one rounding of the exact value) before the router and the experts
+  read it; with the residual option the unnormalised x is added to the output.
 """
 from __future__ import annotations
 
@@ -69,7 +73,7 @@ __all__ = [
     "expert_up", "expert_down", "combine",
     "moe_forward", "permute", "expert_weights", "shared_weights", "decode_act",
     "selection_keys", "load_stats", "expert_capacity", "quantize_rows_e4m3",
-    "dequantize_rows_e4m3",
+    "dequantize_rows_e4m3", "rms_norm", "round_to_act", "normalized_input",
 ]
 
 
@@ -190,12 +194,14 @@ def selection_keys(logits, fn: str, select_bias=None) -> np.ndarray:
     return gate_scores(l, fn)
 
 
-def route(layer, tokens=None):
+def route(layer, tokens=None, x=None):
     """Router of a stored layer: returns dict(logits, scores, keys, idx, w) in fp64 (idx
     int32).  The selection is decided on the fp32-rounded selection keys (group sums in
-    fp32); the weights use the unbiased fp64 scores."""
+    fp32); the weights use the unbiased fp64 scores.  ``x`` (fp64 rows, already restricted
+    to ``tokens``) replaces the layer's stored input, e.g. by its normalised rows."""
     s = layer.shape
-    x = decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
+    if x is None:
+        x = decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
     w_r = decode_act(layer.router, s.act_dtype)
     l = router_logits(x, w_r, layer.logit_bias)
     sc = gate_scores(l, s.score)
@@ -204,6 +210,41 @@ def route(layer, tokens=None):
     idx = select_experts(keys.astype(np.float32), s.k, s.G, s.Gk, s.n_g)
     w = routing_weights(sc, idx, s.renormalize, s.route_scale)
     return {"x": x, "logits": l, "scores": sc, "keys": keys, "idx": idx, "w": w}
+
+
+# ----------------------------------------------------------------------------- pre-norm
+def rms_norm(x, gamma, eps: float):
+    """RMSNorm of every row (fp64): y = x / sqrt(mean_c x_c^2 + eps) * gamma.
+
+    [MoE-Eng] section "变了什么，为什么变": item 2 (RMSNorm drops LayerNorm's mean and keeps
+    only the root-mean-square scaling) and the decoder-layer sketch, where the MoE reads
+    rms_norm(h) and its output is added back to h; section "常见陷阱", item 3 (eps 1e-6
+    for bf16 training).  The per-channel gain gamma is the reading taken for the learned
+    scale the pages do not print."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * np.asarray(gamma, np.float64)[None, :]
+
+
+def round_to_act(v, dtype: str) -> np.ndarray:
+    """fp64 values to the nearest value of the activation dtype, ties to even, in one
+    rounding step (bf16: 8 significant bits; fp32: IEEE single).  Returns fp64."""
+    v = np.asarray(v, np.float64)
+    if dtype == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        m, e = np.frexp(v)                           # v = m 2^e, 0.5 <= |m| < 1
+        return np.ldexp(np.rint(m * 256.0), e - 8)   # rint: ties to even
+    raise ValueError(dtype)
+
+
+def normalized_input(layer, tokens=None):
+    """The stored MoE input of a pre-norm layer: RMSNorm of the x rows with the layer's
+    gain and eps (as fp32, the stored precision), rounded to the activation dtype."""
+    s = layer.shape
+    x = decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
+    eps = float(np.float32(s.norm_eps))
+    return round_to_act(rms_norm(x, layer.norm_gamma, eps), s.act_dtype)
 
 
 # ----------------------------------------------------------------------------- e4m3 activations
@@ -341,9 +382,12 @@ def moe_forward(layer, tokens=None, idx=None):
     (computed from the fp32 capacity factor, as stored).  ``idx`` [T, k] replaces the
     selection with a given one for the whole batch (the weights stay the renormalised
     fp64 scores of those experts), for comparing outputs under a routing that was checked
-    separately."""
+    separately.  A pre-norm layer routes and runs its experts on the normalised rows
+    (``normalized_input``) and, with the residual option, adds the stored x."""
     s = layer.shape
-    r = route(layer, tokens)
+    pre = getattr(s, "pre_norm", False)
+    x_in = normalized_input(layer, tokens) if pre else None
+    r = route(layer, tokens, x=x_in)
     if idx is not None:
         idx_all = np.asarray(idx, np.int32)
         r["idx"] = idx_all if tokens is None else idx_all[np.asarray(tokens)]
@@ -355,7 +399,8 @@ def moe_forward(layer, tokens=None, idx=None):
         if idx is not None:
             full_idx = np.asarray(idx, np.int32)
         else:
-            full_idx = (r if tokens is None else route(layer))["idx"]
+            full_idx = (r if tokens is None else
+                        route(layer, x=normalized_input(layer) if pre else None))["idx"]
         cap = expert_capacity(s.T, s.k, s.E, float(np.float32(cf)))
         _, _, _, slot_pos = permute(full_idx, s.E, cap)
         kept_all = slot_pos.reshape(s.T, s.k) >= 0
@@ -376,6 +421,8 @@ def moe_forward(layer, tokens=None, idx=None):
     for i in range(s.S):
         w1, w3, w2 = shared_weights(layer, i)
         out += expert_ffn(xa, w1, w3, w2, s.act)
+    if getattr(s, "residual", False):
+        out = out + decode_act(layer.x if tokens is None else layer.x[tokens], s.act_dtype)
     r["out"] = out
     return r
 

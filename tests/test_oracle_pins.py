@@ -636,6 +636,94 @@ def test_forward_with_e4m3_activations_is_the_forward_of_the_dequantised_rows():
     assert np.array_equal(O.route(plain)["idx"], r["idx"])
 
 
+# ----------------------------------------------------------------------------- pre-norm
+def test_round_to_act_bf16_matches_the_fp32_encoder_and_rounds_once():
+    """On fp32 inputs the single rounding equals the bf16 encoder of the fp32 bits (an
+    independent integer implementation); ties go to even; an fp64 value just above a tie
+    rounds up, which a detour through fp32 (a tie there) would round down."""
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(20000) * np.exp(rng.standard_normal(20000) * 4)).astype(np.float32)
+    ours = O.round_to_act(v.astype(np.float64), "bf16")
+    ref = O.decode_bf16(W.encode_bf16(v))
+    assert np.array_equal(ours, ref)
+    t = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -30])
+    assert list(O.round_to_act(t, "bf16")) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+    assert O.round_to_act(np.array([0.0]), "bf16")[0] == 0.0
+
+
+def test_rms_norm_hand_example():
+    y = O.rms_norm(np.array([[3.0, 4.0]]), np.array([2.0, -1.0]), 0.0)
+    r = math.sqrt((9 + 16) / 2)
+    assert np.allclose(y, [[6 / r, -4 / r]], rtol=1e-15)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 37)) * rng.random((6, 1)) * 10
+    y = O.rms_norm(x, np.ones(37), 0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)
+    assert np.allclose(O.rms_norm(3.5 * x, np.ones(37), 0.0), y, rtol=1e-13)
+    # homogeneity with eps: scaling x by c and eps by c^2 changes nothing
+    assert np.allclose(O.rms_norm(3.5 * x, np.ones(37), 0.3 * 3.5 ** 2),
+                       O.rms_norm(x, np.ones(37), 0.3), rtol=1e-13)
+    g = rng.standard_normal(37)
+    assert np.allclose(O.rms_norm(x, g, 0.1), O.rms_norm(x, np.ones(37), 0.1) * g, rtol=1e-13)
+
+
+def test_rms_norm_keeps_the_mean_and_puts_eps_under_the_root():
+    # a constant row is not centred (LayerNorm would give zeros)
+    assert np.allclose(O.rms_norm(np.full((1, 8), -2.5), np.ones(8), 0.0), -1.0, rtol=1e-15)
+    # x = 1e-3, eps = 1e-6: 1e-3 / sqrt(1e-6 + 1e-6) = 1 / sqrt(2)
+    assert np.allclose(O.rms_norm(np.full((1, 4), 1e-3), np.ones(4), 1e-6), 2 ** -0.5, rtol=1e-12)
+    assert np.all(O.rms_norm(np.zeros((1, 4)), np.ones(4), 1e-6) == 0.0)
+
+
+def _prenorm_layer(**kw):
+    base = dict(act_dtype="f32", weight_dtype="f32", T=6, d=8, E=4, k=2, S=1, I=5, G=2, Gk=1,
+                score="sigmoid", pre_norm=True, residual=True, norm_eps=0.0)
+    base.update(kw)
+    return W.make_layer(W.small_shape(**base), cache=False)
+
+
+def test_prenorm_forward_is_residual_plus_the_layer_on_the_normalised_rows():
+    lay = _prenorm_layer()
+    pre = O.moe_forward(lay)
+    x = O.decode_act(lay.x, "f32")
+    xn = O.rms_norm(x, lay.norm_gamma, 0.0).astype(np.float32)
+    plain = W.Layer(**{**lay.__dict__})
+    plain.shape = W.replace(lay.shape, pre_norm=False, residual=False)
+    plain.x = xn
+    ref = O.moe_forward(plain)
+    assert np.array_equal(pre["idx"], ref["idx"])
+    assert np.allclose(pre["out"], x + ref["out"], rtol=1e-13, atol=1e-13)
+    # brute force for one token: residual + weighted experts + shared expert on x_norm
+    t = 3
+    acc = x[t].copy()
+    for j in range(2):
+        w1, w3, w2 = O.expert_weights(lay, int(pre["idx"][t, j]))
+        acc += pre["w"][t, j] * np.array(_bf_ffn(xn[t].astype(np.float64).tolist(), w1.tolist(),
+                                                 w3.tolist(), w2.tolist(), "swiglu"))
+    w1, w3, w2 = O.shared_weights(lay, 0)
+    acc += np.array(_bf_ffn(xn[t].astype(np.float64).tolist(), w1.tolist(), w3.tolist(),
+                            w2.tolist(), "swiglu"))
+    assert np.allclose(pre["out"][t], acc, rtol=1e-10, atol=1e-12)
+
+
+def test_prenorm_layer_update_is_invariant_to_power_of_two_row_scaling():
+    """With eps = 0 RMSNorm removes any row scale; a power of two scales the stored x
+    exactly, so out(4 x) - 4 x equals out(x) - x bit for bit."""
+    for dt in ("f32", "bf16"):
+        lay = _prenorm_layer(act_dtype=dt, weight_dtype=dt, d=16, I=8)
+        a = O.moe_forward(lay)
+        big = W.Layer(**{**lay.__dict__})
+        x32 = O.decode_act(lay.x, dt).astype(np.float32) * np.float32(4.0)
+        big.x = x32 if dt == "f32" else W.encode_bf16(x32)
+        b = O.moe_forward(big)
+        xa = O.decode_act(lay.x, dt)
+        assert np.array_equal(a["idx"], b["idx"])
+        assert np.allclose(b["out"] - 4 * xa, a["out"] - xa, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- workloads
 def test_fusionllm_shapes_match_the_yaml():
     y = json.load(open(os.path.join(GOLDEN, "fusionllm_moe_yaml.json")))
@@ -673,7 +761,9 @@ def _swapped_ffn(x, w1, w3, w2, act):
 @pytest.mark.parametrize("mutation", ["swap_gate_up", "no_renorm", "tie_high_index",
                                       "token_desc_perm", "drop_shared", "transpose_down",
                                       "biased_weights", "keep_last_at_capacity",
-                                      "truncating_quantiser"])
+                                      "truncating_quantiser", "layernorm_centering",
+                                      "eps_outside_root", "sum_not_mean", "no_residual",
+                                      "double_rounding"])
 def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
     """Each mutation is a plausible slip in the oracle; the named pin must then fail."""
     if mutation == "swap_gate_up":
@@ -738,6 +828,38 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
             return np.where(up, c - 1, c)
         monkeypatch.setattr(O.moe_oracle, "_e4m3_rne_magnitude", trunc)
         check = test_activation_quantiser_matches_torch_e4m3
+    elif mutation == "layernorm_centering":
+        orig = O.moe_oracle.rms_norm
+        def centred(x, gamma, eps):
+            x = np.asarray(x, np.float64)
+            return orig(x - x.mean(axis=1, keepdims=True), gamma, eps)
+        monkeypatch.setattr(O, "rms_norm", centred)
+        check = test_rms_norm_keeps_the_mean_and_puts_eps_under_the_root
+    elif mutation == "eps_outside_root":
+        def outside(x, gamma, eps):
+            x = np.asarray(x, np.float64)
+            return x / (np.sqrt(np.mean(x * x, axis=1, keepdims=True)) + eps) * np.asarray(gamma)[None, :]
+        monkeypatch.setattr(O, "rms_norm", outside)
+        check = test_rms_norm_keeps_the_mean_and_puts_eps_under_the_root
+    elif mutation == "sum_not_mean":
+        def summed(x, gamma, eps):
+            x = np.asarray(x, np.float64)
+            return x / np.sqrt(np.sum(x * x, axis=1, keepdims=True) + eps) * np.asarray(gamma)[None, :]
+        monkeypatch.setattr(O, "rms_norm", summed)
+        check = test_rms_norm_unit_rms_and_scale_invariance
+    elif mutation == "no_residual":
+        orig_fwd = O.moe_oracle.moe_forward
+        def no_res(layer, tokens=None, idx=None):
+            lay = W.Layer(**{**layer.__dict__})
+            lay.shape = W.replace(layer.shape, residual=False)
+            return orig_fwd(lay, tokens, idx)
+        monkeypatch.setattr(O, "moe_forward", no_res)
+        check = test_prenorm_layer_update_is_invariant_to_power_of_two_row_scaling
+    elif mutation == "double_rounding":
+        orig = O.moe_oracle.round_to_act
+        monkeypatch.setattr(O, "round_to_act",
+                            lambda v, dt: orig(np.asarray(v, np.float64).astype(np.float32).astype(np.float64), dt))
+        check = test_round_to_act_bf16_matches_the_fp32_encoder_and_rounds_once
     elif mutation == "drop_shared":
         monkeypatch.setattr(O.moe_oracle, "shared_weights",
                             lambda lay, i: tuple(np.zeros_like(a) if a is not None else None

@@ -18,6 +18,9 @@ seeded Gaussian stand-ins are used):
 * Values are drawn in fp32 and then stored: fp32 as is, bf16 by round-to-nearest-even
   of the fp32 bit pattern, e4m3 by a per-output-channel scale max|W[n,:]|/448 and
   round-to-nearest-even onto the e4m3 grid, saturating at 448.
+* Pre-norm shapes: every stored x row is scaled by exp(0.5 z), z ~ N(0, 1) (a residual
+  stream whose rows differ in magnitude), and the RMSNorm gain is 1 + 0.1 N(0, 1) per
+  channel; both from the stream ``SeedSequence([seed, 0x2A0E])``.
 
 Shapes follow the FusionLLM MoE configuration ("FusionLLM：融合 MLA、GDN 与 MoE 的高效混合架构大模型训练框架",
 section 模型配置与规模: dim 2048, 64 routed experts, 6 active, 4 shared, expert inter dim 1536).
@@ -59,6 +62,9 @@ class MoeShape:
     capacity_factor: Optional[float] = None   # expert capacity c*T*k/E (None: unlimited)
     select_bias_std: Optional[float] = None   # selection-only per-expert bias ~ N(0, std^2)
     fp8_act: bool = False  # up projections take e4m3 activations with per-token scales
+    pre_norm: bool = False     # the MoE reads RMSNorm(x) (gain norm_gamma, eps norm_eps)
+    norm_eps: float = 1e-6
+    residual: bool = False     # the output adds the unnormalised x
 
     @property
     def flops_per_token(self) -> int:
@@ -96,9 +102,14 @@ SHAPES = {
                              Gk=4, S=4, I=1536, act="swiglu", act_dtype="bf16",
                              weight_dtype="bf16", seed=1, x_from="fusionllm_bf16",
                              capacity_factor=1.25, select_bias_std=0.5),
+    # the prefill layer as a pre-norm decoder step: h + MoE(RMSNorm(h))
+    "prenorm_bf16": MoeShape("prenorm_bf16", T=4096, d=2048, E=64, k=6, score="sigmoid", G=8,
+                             Gk=4, S=4, I=1536, act="swiglu", act_dtype="bf16",
+                             weight_dtype="bf16", seed=1, x_from="fusionllm_bf16",
+                             pre_norm=True, residual=True),
 }
 ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2", "balance_bf16",
-         "fp8a_relu2"]
+         "fp8a_relu2", "prenorm_bf16"]
 
 
 def shape_by_name(name: str) -> MoeShape:
@@ -169,6 +180,7 @@ class Layer:
     sh_s_up: Optional[np.ndarray] = None
     sh_s_down: Optional[np.ndarray] = None
     select_bias: Optional[np.ndarray] = None   # [E] fp32, selection only
+    norm_gamma: Optional[np.ndarray] = None    # [d] fp32 RMSNorm gain (pre-norm layers)
     extra: dict = field(default_factory=dict)
 
 
@@ -202,6 +214,27 @@ def _select_bias(s: MoeShape):
     return _normal(st, (s.E,), s.select_bias_std).astype(np.float32)
 
 
+def _decode_stored(a, dtype: str) -> np.ndarray:
+    """Stored activations back to fp32 (bf16 bits are the upper half of an fp32)."""
+    if dtype == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.asarray(a, np.float32)
+
+
+def _pre_norm_inputs(s: MoeShape, x):
+    """Pre-norm layers: the stored x stands for a residual stream whose rows differ in
+    magnitude, so every row is scaled by exp(0.5 z), z ~ N(0, 1); the RMSNorm gain is
+    1 + 0.1 N(0, 1) per channel.  Both come from the shape's own stream."""
+    if not s.pre_norm:
+        return x, None
+    st = np.random.SeedSequence([s.seed, 0x2A0E]).spawn(2)
+    gamma = (np.float32(1.0) + _normal(st[0], (s.d,), 0.1)).astype(np.float32)
+    row = np.exp(_normal(st[1], (s.T, 1), 0.5)).astype(np.float32)
+    x32 = _decode_stored(x, s.act_dtype) * row
+    enc, _ = _store(x32.astype(np.float32), s.act_dtype)
+    return enc, gamma
+
+
 def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> Layer:
     """Build the seeded layer (inputs + weights) of a shape."""
     if isinstance(shape, str):
@@ -210,7 +243,7 @@ def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> L
         base = make_layer(shape.x_from, threads=threads, cache=cache)
         lay = Layer(**{**base.__dict__})
         lay.shape = shape
-        lay.x = base.x[: shape.T].copy()
+        lay.x, lay.norm_gamma = _pre_norm_inputs(shape, base.x[: shape.T].copy())
         lay.select_bias = _select_bias(shape)
         return lay
     if cache and shape.name in _CACHE:
@@ -277,6 +310,7 @@ def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> L
 
     router, _ = _store(_normal(router_stream, (s.E, s.d), 1.0 / math.sqrt(s.d)), s.act_dtype)
     x, _ = _store(_normal(x_stream, (s.T, s.d), 1.0), s.act_dtype)
+    x, gamma = _pre_norm_inputs(s, x)
     bias = None
     if s.zipf_s is not None:
         g = np.random.Generator(np.random.PCG64(perm_stream))
@@ -290,7 +324,7 @@ def make_layer(shape: MoeShape | str, threads: int = 8, cache: bool = True) -> L
                 s_gate=scales[("routed", "gate")], s_up=scales[("routed", "up")],
                 s_down=scales[("routed", "down")], sh_s_gate=scales[("shared", "gate")],
                 sh_s_up=scales[("shared", "up")], sh_s_down=scales[("shared", "down")],
-                select_bias=_select_bias(s))
+                select_bias=_select_bias(s), norm_gamma=gamma)
     if cache:
         _CACHE[shape.name] = lay
     return lay
