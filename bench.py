@@ -61,8 +61,9 @@ def to_dev(a):
 
 
 class Runner:
-    """Device-resident layer; one step = moe_forward_ex with HIP events at its stage
-    boundaries, all recorded on the stream the kernels run on."""
+    """Device-resident layer; one step = one moe_forward call.  Stage times come from
+    separate passes of moe_forward_ex with HIP events at the stage boundaries, recorded on
+    the stream the kernels run on."""
 
     def __init__(self, shape, lay, weights=None):
         import torch
@@ -73,17 +74,20 @@ class Runner:
                                    score=s.score, renormalize=s.renormalize,
                                    route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
                                    weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor,
-                                   fp8_act=s.fp8_act)
+                                   fp8_act=s.fp8_act, pre_norm=s.pre_norm, norm_eps=s.norm_eps,
+                                   residual=s.residual)
         names = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
                  "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"]
         if weights is None:
             t = {n: to_dev(getattr(lay, n)) for n in names}
             t["select_bias"] = to_dev(lay.select_bias)
+            t["norm_gamma"] = to_dev(lay.norm_gamma)
             weights = moe.Weights(**t)
-        elif lay.select_bias is not None:
-            # the same device weights with this layer's selection bias
+        elif lay.select_bias is not None or lay.norm_gamma is not None:
+            # the same device weights with this layer's selection bias and RMSNorm gain
             t = dict(weights.tensors)
             t["select_bias"] = to_dev(lay.select_bias)
+            t["norm_gamma"] = to_dev(lay.norm_gamma)
             weights = moe.Weights(**t)
         self.w = weights
         self.x = to_dev(lay.x)
@@ -236,6 +240,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-prenorm", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
@@ -329,6 +334,19 @@ def main(argv=None):
                           "rows_kept_frac": float(counts.sum()) / (bshape.T * bshape.k),
                           "aux_loss_alpha1": float(stv[2 * bshape.E]),
                           "max_f_over_mean": float(stv[:bshape.E].max() * bshape.E)}
+    if not args.no_prenorm and shape.name == "fusionllm_bf16":
+        # the same layer as a pre-norm decoder step, h + MoE(RMSNorm(h)): the RMSNorm runs in
+        # the routing launch and the residual in the combine
+        pshape = W.SHAPES["prenorm_bf16"]
+        prun = Runner(pshape, W.make_layer(pshape), weights=run.w)
+        p_ms, _ = prun.timed(args.steps, args.warmup)
+        p_route = prun.staged(args.steps, args.warmup, stages=[0, 1])["route"]
+        p_comb = prun.staged(args.steps, args.warmup, stages=[6, 7])["combine"]
+        res["prenorm"] = {"workload": pshape.name, "ms_per_step": p_ms,
+                          "tokens_per_s": pshape.T / (p_ms * 1e-3),
+                          "rmsnorm_route_ms": p_route, "plain_route_ms": stage_ms["route"],
+                          "combine_with_residual_ms": p_comb,
+                          "plain_combine_ms": stage_ms["combine"]}
     if not args.no_fp8 and shape.name == "fusionllm_bf16":
         # the e4m3-weight layer (T = 16384, ReLU^2): bf16 activations, then e4m3 activations
         # in the up projections (same device weights)

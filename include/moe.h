@@ -84,6 +84,16 @@ typedef struct {
                                 weight_dtype MOE_FP8_E4M3.  0: bf16 activations.
                                 Source: FP8 E4M3 products with FP32 accumulation, section
                                 "生产现实：前沿实验室真正交付的内容" of "大模型工程（一）"  */
+  int32_t pre_norm;          /* 1: the layer reads RMSNorm(x) = x / sqrt(mean_c x_c^2 + eps)
+                                * norm_gamma (per token, no mean subtraction): the router and
+                                the experts take the normalised rows, stored in act_dtype
+                                (moe_rmsnorm_route).  0: x as given.
+                                Source: the pre-norm decoder-layer sketch and item 2 (RMSNorm)
+                                of section "变了什么，为什么变" of "大模型工程（一）"       */
+  float norm_eps;            /* eps of the RMSNorm, finite, >= 0 (1e-6 for bf16: section
+                                "常见陷阱", item 3); with eps = 0 an all-zero row is 0/0    */
+  int32_t residual;          /* 1: moe_forward adds x (the unnormalised input) to its output,
+                                h + moe(rms_norm(h)) of the same sketch.  0: no residual    */
 } moe_config;
 
 /* Expert weights.  [out, in] per expert, stacked on dim 0.  e4m3 weights carry one fp32
@@ -104,6 +114,8 @@ typedef struct {
   const float* sh_s_up;      /* [S, I]                                                     */
   const float* sh_s_down;    /* [S, d]                                                     */
   const float* select_bias;  /* [E] selection-only expert bias, or NULL (see moe_route)     */
+  const float* norm_gamma;   /* [d] fp32 RMSNorm gain; required when cfg->pre_norm, else
+                                ignored                                                      */
 } moe_weights;
 
 /* Bytes of device workspace moe_forward needs for this config (host only, no HIP call).
@@ -130,6 +142,20 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
 moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
                      const float* logit_bias, const float* select_bias, float* scores,
                      int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* The pre-norm step in one launch: x_norm = RMSNorm(x) per token, with
+ *   inv_rms[t] = 1 / sqrt(sum_c x[t,c]^2 / d + cfg->norm_eps) (fp32, fixed summation order),
+ *   x_norm[t,c] = act_dtype(x[t,c] * inv_rms[t] * gamma[c]) (fp32 products, one rounding),
+ * then moe_route on x_norm: the router multiplies exactly the stored x_norm values, so the
+ * results equal those of moe_route called on x_norm.  cfg->pre_norm is not consulted.
+ * x, x_norm [T, d] act_dtype (x_norm written; must not alias x); gamma [d] fp32; the other
+ * arguments as in moe_route.  All pointers 16-byte aligned.
+ * Source: RMSNorm before the MoE in the decoder-layer sketch and item 2 of section
+ * "变了什么，为什么变" of "大模型工程（一）：Transformer 到 MoE"; routing as in moe_route. */
+moe_status moe_rmsnorm_route(const moe_config* cfg, const void* x, const float* gamma,
+                             const void* router, const float* logit_bias,
+                             const float* select_bias, void* x_norm, float* scores,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
 /* The selection step of moe_route alone, on given fp32 scores [T, E] and optional
  * selection keys [T, E] (NULL: the scores are the keys).  Every value must be finite and
@@ -216,7 +242,9 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
 /* The whole layer: route -> permute -> UP/DOWN grouped GEMMs (routed and shared) ->
  * combine.  x [T, d] and out [T, d] act_dtype; ws at least moe_workspace_size bytes
  * (16-byte aligned).  The per-stage tensors (topk_idx, topk_w, counts, offsets,
- * perm_token, slot_pos, intermediates) live in ws.
+ * perm_token, slot_pos, intermediates) live in ws.  With cfg->pre_norm the routing is
+ * moe_rmsnorm_route (w->norm_gamma) and the experts read the normalised rows (kept in ws);
+ * with cfg->residual, out[t] also adds x[t], after the expert outputs (fp32 sum).
  * With shared experts and more rows than the one-launch decode path takes, the shared
  * GEMMs run on a second stream that the library keeps per device (default priority,
  * created on first use): it waits for everything queued on `stream` before the call,

@@ -14,7 +14,8 @@ from typing import Optional
 
 __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
-    "workspace_size", "route", "select", "load_stats", "permute", "quantize_rows",
+    "workspace_size", "route", "rmsnorm_route", "select", "load_stats", "permute",
+    "quantize_rows",
     "grouped_gemm", "combine", "forward",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
@@ -28,7 +29,8 @@ MOE_ACT_SWIGLU, MOE_ACT_RELU2 = 0, 1
 MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 
-EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_select", "moe_load_stats",
+EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_rmsnorm_route", "moe_select",
+                    "moe_load_stats",
                     "moe_permute", "moe_quantize_rows", "moe_grouped_gemm", "moe_combine",
                     "moe_forward", "moe_forward_ex", "moe_status_string", "moe_last_hip_error"]
 
@@ -59,11 +61,13 @@ class Config(ctypes.Structure):
         ("renormalize", ctypes.c_int32), ("route_scale", ctypes.c_float),
         ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
         ("capacity_factor", ctypes.c_float), ("fp8_act", ctypes.c_int32),
+        ("pre_norm", ctypes.c_int32), ("norm_eps", ctypes.c_float), ("residual", ctypes.c_int32),
     ]
 
 
 _W_FIELDS = ["router", "logit_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-             "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down", "select_bias"]
+             "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down", "select_bias",
+             "norm_gamma"]
 
 
 class _WeightsC(ctypes.Structure):
@@ -103,6 +107,7 @@ def lib():
         sig = {
             "moe_workspace_size": [cfgp, ctypes.POINTER(sz)],
             "moe_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_rmsnorm_route": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_select": [cfgp, vp, vp, vp, vp, vp],
             "moe_load_stats": [cfgp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp],
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -152,7 +157,8 @@ def _check(status: int, what: str):
 
 def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renormalize=True,
                 route_scale=1.0, act="swiglu", act_dtype="bf16", weight_dtype="bf16",
-                capacity_factor=0.0, fp8_act=False) -> Config:
+                capacity_factor=0.0, fp8_act=False, pre_norm=False, norm_eps=1e-6,
+                residual=False) -> Config:
     dt = {"f32": MOE_F32, "bf16": MOE_BF16, "e4m3": MOE_FP8_E4M3}
     return Config(num_tokens=T, dim=d, num_experts=E, top_k=k, num_groups=G, topk_groups=Gk,
                   group_score_topn=n_g, num_shared=S, inter_dim=I,
@@ -160,7 +166,9 @@ def make_config(T, d, E, k, *, G=1, Gk=1, n_g=1, S=0, I, score="sigmoid", renorm
                   renormalize=int(bool(renormalize)), route_scale=float(route_scale),
                   act={"swiglu": MOE_ACT_SWIGLU, "relu2": MOE_ACT_RELU2}[act],
                   act_dtype=dt[act_dtype], weight_dtype=dt[weight_dtype],
-                  capacity_factor=float(capacity_factor or 0.0), fp8_act=int(bool(fp8_act)))
+                  capacity_factor=float(capacity_factor or 0.0), fp8_act=int(bool(fp8_act)),
+                  pre_norm=int(bool(pre_norm)), norm_eps=float(norm_eps),
+                  residual=int(bool(residual)))
 
 
 def workspace_size(cfg: Config) -> int:
@@ -173,6 +181,14 @@ def route(cfg, x, router, logit_bias, select_bias, scores, topk_idx, topk_w, str
     _check(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(router), _ptr(logit_bias),
                            _ptr(select_bias), _ptr(scores), _ptr(topk_idx), _ptr(topk_w),
                            _stream(stream)), "moe_route")
+
+
+def rmsnorm_route(cfg, x, gamma, router, logit_bias, select_bias, x_norm, scores, topk_idx,
+                  topk_w, stream=None):
+    _check(lib().moe_rmsnorm_route(ctypes.byref(cfg), _ptr(x), _ptr(gamma), _ptr(router),
+                                   _ptr(logit_bias), _ptr(select_bias), _ptr(x_norm),
+                                   _ptr(scores), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_rmsnorm_route")
 
 
 def select(cfg, scores, keys, topk_idx, topk_w, stream=None):

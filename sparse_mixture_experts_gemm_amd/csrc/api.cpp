@@ -81,6 +81,9 @@ moe_status check_config(const moe_config* c) {
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->capacity_factor)) return MOE_ERR_INVALID_ARG;
   if (c->fp8_act != 0 && c->fp8_act != 1) return MOE_ERR_INVALID_ARG;
+  if (c->pre_norm != 0 && c->pre_norm != 1) return MOE_ERR_INVALID_ARG;
+  if (c->residual != 0 && c->residual != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->norm_eps) || c->norm_eps < 0.0f) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
@@ -119,6 +122,9 @@ moe::RouteParams route_params(const moe_config* c) {
   p.renormalize = c->renormalize;
   p.route_scale = c->route_scale;
   p.select_bias = nullptr;
+  p.norm_gamma = nullptr;
+  p.norm_eps = c->norm_eps;
+  p.x_norm = nullptr;
   return p;
 }
 
@@ -139,7 +145,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Workspace of moe_forward, in carve order.
 struct Carve {
   size_t topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, perm_ws;
-  size_t scores, stats_ws, x_q, x_scale;
+  size_t scores, stats_ws, x_norm, x_q, x_scale;
   size_t h_routed, h_shared, y_routed, y_shared, total;
 };
 
@@ -160,6 +166,7 @@ Carve carve(const moe_config* c) {
   w.perm_ws = take(moe::permute_ws_bytes((int)T, (int)E));
   w.scores = take(T * E * 4);                    // only written when statistics are asked
   w.stats_ws = take(moe::stats_ws_bytes((int)T, (int)E));
+  w.x_norm = take(c->pre_norm ? T * d * as : 0); // normalised input of a pre-norm layer
   w.x_q = take(c->fp8_act ? T * d : 0);          // e4m3 activations of the up projections
   w.x_scale = take(c->fp8_act ? T * 4 : 0);
   w.h_routed = take(T * k * I * as);
@@ -268,6 +275,31 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* router,
   }
 }
 
+moe_status moe_rmsnorm_route(const moe_config* cfg, const void* x, const float* gamma,
+                             const void* router, const float* logit_bias,
+                             const float* select_bias, void* x_norm, float* scores,
+                             int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (x == nullptr || gamma == nullptr || router == nullptr || x_norm == nullptr ||
+        topk_idx == nullptr || topk_w == nullptr)
+      return MOE_ERR_INVALID_ARG;
+    if (x_norm == x) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(router) || !aligned16(gamma) || !aligned16(x_norm))
+      return MOE_ERR_UNSUPPORTED;
+    moe::RouteParams rp = route_params(cfg);
+    rp.select_bias = select_bias;
+    rp.norm_gamma = gamma;
+    rp.x_norm = x_norm;
+    return hip_status(moe::launch_route(rp, cfg->act_dtype, x, router, logit_bias, scores,
+                                        topk_idx, topk_w, stream));
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
 moe_status moe_select(const moe_config* cfg, const float* scores, const float* keys,
                       int32_t* topk_idx, float* topk_w, hipStream_t stream) {
   try {
@@ -359,7 +391,7 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
     if (!aligned16(y_perm) || !aligned16(out) || (y_shared != nullptr && !aligned16(y_shared)))
       return MOE_ERR_UNSUPPORTED;
     return hip_status(moe::launch_combine(cfg->num_tokens, cfg->dim, cfg->top_k, cfg->act_dtype,
-                                          y_perm, slot_pos, y_shared, out, stream));
+                                          y_perm, slot_pos, y_shared, nullptr, out, stream));
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -408,7 +440,11 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
 
     // validate every grouped-GEMM argument before the first launch
     const bool a8 = cfg->fp8_act != 0;
-    const void* x_up = a8 ? at(cv.x_q) : x;                   // rows of the up projections
+    const bool pre = cfg->pre_norm != 0;
+    if (pre && (w->norm_gamma == nullptr)) return MOE_ERR_INVALID_ARG;
+    if (pre && !aligned16(w->norm_gamma)) return MOE_ERR_UNSUPPORTED;
+    const void* x_in = pre ? at(cv.x_norm) : x;               // the MoE input rows
+    const void* x_up = a8 ? at(cv.x_q) : x_in;                // rows of the up projections
     const float* x_up_scale = a8 ? static_cast<const float*>(at(cv.x_scale)) : nullptr;
     moe::GemmParams up_r, up_s{}, dn_r, dn_s{};
     st = gemm_params(cfg, MOE_STAGE_UP, MOE_EXPERTS_ROUTED, x_up, perm_token, offsets, Tk, w,
@@ -459,8 +495,25 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
         return hip_status(ce);
       }
     }
-    if (a8)
-      e = moe::launch_quant_rows(T, cfg->dim, x, static_cast<uint8_t*>(at(cv.x_q)),
+    moe::RouteParams rp = route_params(cfg);
+    rp.select_bias = w->select_bias;
+    if (pre) {
+      rp.norm_gamma = w->norm_gamma;
+      rp.x_norm = at(cv.x_norm);
+    }
+    float* scores = stats ? static_cast<float*>(at(cv.scores)) : nullptr;
+    auto route = [&]() {
+      mark(0);
+      if (e == hipSuccess)
+        e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw,
+                              stream);
+      mark(1);
+    };
+    // the shared experts need only the up-projection input: x, or the normalised rows
+    // written by the routing launch of a pre-norm layer (then e4m3-quantised if asked)
+    if (pre) route();
+    if (a8 && e == hipSuccess)
+      e = moe::launch_quant_rows(T, cfg->dim, x_in, static_cast<uint8_t*>(at(cv.x_q)),
                                  static_cast<float*>(at(cv.x_scale)), stream);
     if (fork) {
       if (e == hipSuccess) e = hipEventRecord(fork_ev, stream);
@@ -473,14 +526,7 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                                      cus, side);
       if (e == hipSuccess) e = hipEventRecord(join, side);
     }
-    moe::RouteParams rp = route_params(cfg);
-    rp.select_bias = w->select_bias;
-    float* scores = stats ? static_cast<float*>(at(cv.scores)) : nullptr;
-    mark(0);
-    if (e == hipSuccess)
-        e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw,
-                              stream);
-    mark(1);
+    if (!pre) route();
     if (e == hipSuccess)
       e = moe::launch_permute(T, cfg->num_experts, cfg->top_k, expert_capacity(cfg), idx, tw,
                               counts, offsets, perm_token, slot_pos, perm_weight,
@@ -532,7 +578,8 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     }
     if (e == hipSuccess)
       e = moe::launch_combine(T, cfg->dim, cfg->top_k, adt, at(cv.y_routed), slot_pos,
-                              shared ? at(cv.y_shared) : nullptr, out, stream);
+                              shared ? at(cv.y_shared) : nullptr, cfg->residual ? x : nullptr,
+                              out, stream);
     mark(7);
     if (fork) {
       // both events have been waited on or are pending in the streams: their resources

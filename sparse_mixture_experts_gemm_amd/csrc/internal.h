@@ -15,6 +15,11 @@ struct RouteParams {
   int renormalize;
   float route_scale;
   const float* select_bias;   // [E] selection-only bias or null
+  // pre-norm: route RMSNorm(x) (gain norm_gamma [d] fp32, eps norm_eps) and write it to
+  // x_norm [T, d] (activation dtype); norm_gamma null: route x as given
+  const float* norm_gamma;
+  float norm_eps;
+  void* x_norm;
 };
 
 // Segments of a grouped GEMM.  Routed: segment e = rows [offsets[e], offsets[e+1]).
@@ -77,8 +82,9 @@ bool decode_gemm_applies(const GemmParams& p, int act_dtype);
 hipError_t launch_decode_gemm(const GemmParams& p, Stage stage, int act, int weight_dtype,
                               hipStream_t s, const GemmParams* second = nullptr);
 
+// residual [T, d] or null: added last (the unnormalised input of a pre-norm layer)
 hipError_t launch_combine(int T, int d, int k, int act_dtype, const void* y_perm,
-                          const int32_t* slot_pos, const void* y_shared, void* out,
-                          hipStream_t s);
+                          const int32_t* slot_pos, const void* y_shared, const void* residual,
+                          void* out, hipStream_t s);
 
 }  // namespace moe

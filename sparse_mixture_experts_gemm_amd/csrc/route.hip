@@ -14,6 +14,14 @@
 // group rank by comparing against every group's score (readlane), and k rounds of a DPP
 // wave max over the score bits, where the lowest lane holding the max wins (ballot), i.e.
 // the lower expert index on equal scores.
+//
+// Pre-norm variant: the layer's MoE reads RMSNorm(x) ("大模型工程（一）：Transformer 到 MoE",
+// section "变了什么，为什么变": the decoder-layer sketch and item 2, RMSNorm keeps only the
+// root-mean-square scaling).  The same launch computes every token's 1/rms (one wave per
+// token, its row held in registers, fixed-order sum of squares), writes the normalised row
+// in the activation dtype, and feeds the router GEMM with exactly those values: staged in
+// LDS (rows padded by 16 bytes so the MFMA operand reads of 16 rows hit distinct banks)
+// when d <= 4096, else recomputed from x by the same expression.
 #include "common.h"
 #include "internal.h"
 
@@ -119,21 +127,125 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
 // (wave w takes steps w, w+16, ...), so each wave needs a single round of loads for d = 2048.
 constexpr int kRouteWaves = 16;
 
+// Normalised bf16 values of 8 consecutive channels: bf16(x * inv_rms * gamma), fp32 steps.
+__device__ __forceinline__ uint4 norm_bf16x8(uint4 v, float inv_rms, const float* g) {
+  const float4 g0 = *reinterpret_cast<const float4*>(g);
+  const float4 g1 = *reinterpret_cast<const float4*>(g + 4);
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = (bf16_bits_to_f32(w[i] & 0xffffu) * inv_rms) * gv[2 * i];
+    const float hi = (bf16_bits_to_f32(w[i] >> 16) * inv_rms) * gv[2 * i + 1];
+    o[i] = pack_bf16x2(lo, hi);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// 1 / sqrt(mean of squares + eps) from a wave's sum of squares.
+__device__ __forceinline__ float inv_rms(float sumsq, int d, float eps) {
+  return 1.0f / sqrtf(sumsq / (float)d + eps);
+}
+
+// NORM: 0 = route x; 1 = pre-norm, normalised rows staged in LDS (d <= kNormLdsDim);
+// 2 = pre-norm, normalised values recomputed where the router reads them (any d).
+constexpr int kNormLdsDim = 4096;
+constexpr int kNormRowBytes = kNormLdsDim * 2 + 16;
+constexpr int kPartBytes = kRouteWaves * kRouteTok * 64 * 4;
+
+template <int NORM>
 __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
                                                           const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
                                                           const float* __restrict__ bias,
                                                           float* scores, int32_t* idx,
                                                           float* wout) {
-  __shared__ float part[kRouteWaves][kRouteTok][64];
+  // the partial logits, and with NORM == 1 before them the 16 normalised rows
+  constexpr int kSmem = NORM == 1 ? kRouteTok * kNormRowBytes : kPartBytes;
+  static_assert(kRouteTok * kNormRowBytes >= kPartBytes, "partial logits fit the row tile");
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  auto part = reinterpret_cast<float (*)[kRouteTok][64]>(smem);
+  __shared__ float s_inv_rms[kRouteTok];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * kRouteTok;
+  if (NORM == 1) {
+    // wave w: token t0 + w, its row in registers (8 channels per lane per chunk)
+    constexpr int kChunks = kNormLdsDim / 512;
+    const int t = t0 + wave;
+    if (t < p.T) {
+      const uint16_t* xr = x + (size_t)t * p.d;
+      uint4 xv[kChunks];
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = (i * 64 + lane) * 8;
+        if (c < p.d) {
+          xv[i] = *reinterpret_cast<const uint4*>(xr + c);
+          const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float lo = bf16_bits_to_f32(w[q] & 0xffffu), hi = bf16_bits_to_f32(w[q] >> 16);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+          }
+        }
+      }
+      const float r = inv_rms(wave_sum_f(ss), p.d, p.norm_eps);
+      uint16_t* xo = static_cast<uint16_t*>(p.x_norm) + (size_t)t * p.d;
+      unsigned char* row = smem + wave * kNormRowBytes;
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = (i * 64 + lane) * 8;
+        if (c < p.d) {
+          const uint4 v = norm_bf16x8(xv[i], r, p.norm_gamma + c);
+          *reinterpret_cast<uint4*>(xo + c) = v;
+          *reinterpret_cast<uint4*>(row + c * 2) = v;
+        }
+      }
+    }
+    __syncthreads();
+  } else if (NORM == 2) {
+    // wave w: token t0 + w; lanes stride over the row in 8-channel chunks
+    const int t = t0 + wave;
+    float r = 0.0f;
+    if (t < p.T) {
+      const uint16_t* xr = x + (size_t)t * p.d;
+      float ss = 0.0f;
+      for (int c = lane * 8; c < p.d; c += 64 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_bits_to_f32(w[q] & 0xffffu), hi = bf16_bits_to_f32(w[q] >> 16);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+      r = inv_rms(wave_sum_f(ss), p.d, p.norm_eps);
+      uint16_t* xo = static_cast<uint16_t*>(p.x_norm) + (size_t)t * p.d;
+      for (int c = lane * 8; c < p.d; c += 64 * 8)
+        *reinterpret_cast<uint4*>(xo + c) =
+            norm_bf16x8(*reinterpret_cast<const uint4*>(xr + c), r, p.norm_gamma + c);
+    }
+    if (lane == 0) s_inv_rms[wave] = r;
+    __syncthreads();
+  }
   const int m = lane & 15;        // token row within the block / expert column in a tile
   const int g = lane >> 4;        // 8-element K group
   const int ntiles = (p.E + 15) >> 4;
   const bool row_ok = (t0 + m) < p.T;
   const uint16_t* xrow = x + (size_t)(row_ok ? t0 + m : 0) * p.d;
+  // the A operand: x, or its normalised value (0 for rows past T)
+  const float row_r = NORM == 2 ? s_inv_rms[m] : 0.0f;
+  const unsigned char* lds_row = smem + m * kNormRowBytes;
+  auto load_a = [&](int kk) -> uint4 {
+    if (!row_ok) return make_uint4(0, 0, 0, 0);
+    if (NORM == 1) return *reinterpret_cast<const uint4*>(lds_row + kk * 2);
+    const uint4 v = *reinterpret_cast<const uint4*>(xrow + kk);
+    return NORM == 2 ? norm_bf16x8(v, row_r, p.norm_gamma + kk) : v;
+  };
 
   f32x4 acc[4];
 #pragma unroll
@@ -151,7 +263,7 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kk = (st + kRouteWaves * u) * 32 + g * 8;
-      av[u] = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+      av[u] = load_a(kk);
 #pragma unroll
       for (int n = 0; n < 4; ++n) bv[u][n] = load_b(kk, n);
     }
@@ -165,7 +277,7 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
   }
   for (; st < nsteps; st += kRouteWaves) {
     const int kk = st * 32 + g * 8;
-    const uint4 av = row_ok ? *reinterpret_cast<const uint4*>(xrow + kk) : make_uint4(0, 0, 0, 0);
+    const uint4 av = load_a(kk);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
@@ -173,6 +285,7 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
                                                        acc[n], 0, 0, 0);
   }
   // 16x16 MFMA result: lane holds rows 4*(lane/16)+i of column lane%16.
+  if (NORM == 1) __syncthreads();   // the partial logits overwrite the staged rows
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
 #pragma unroll
@@ -192,7 +305,10 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
   score_select_write(l, valid, lane, p, t, scores, idx, wout);
 }
 
-// fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.
+// fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.  Pre-norm:
+// the wave first computes the token's 1/rms and writes the normalised row, and every lane
+// recomputes the normalised values it multiplies with the same expression.
+template <bool NORM>
 __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p, const float* __restrict__ x,
                                                         const float* __restrict__ wr,
                                                         const float* __restrict__ bias,
@@ -204,9 +320,17 @@ __global__ __launch_bounds__(256) void route_f32_kernel(RouteParams p, const flo
   const bool valid = lane < p.E;
   const float* xr = x + (size_t)t * p.d;
   const float* wrow = wr + (size_t)(valid ? lane : 0) * p.d;
+  float r = 1.0f;
+  if (NORM) {
+    float ss = 0.0f;
+    for (int c = lane; c < p.d; c += 64) ss = fmaf(xr[c], xr[c], ss);
+    r = inv_rms(wave_sum_f(ss), p.d, p.norm_eps);
+    float* xo = static_cast<float*>(p.x_norm) + (size_t)t * p.d;
+    for (int c = lane; c < p.d; c += 64) xo[c] = (xr[c] * r) * p.norm_gamma[c];
+  }
   float l = 0.0f;
   if (valid) {
-    for (int c = 0; c < p.d; ++c) l = fmaf(xr[c], wrow[c], l);
+    for (int c = 0; c < p.d; ++c) l = fmaf(NORM ? (xr[c] * r) * p.norm_gamma[c] : xr[c], wrow[c], l);
     if (bias != nullptr) l += bias[lane];
   }
   score_select_write(l, valid, lane, p, t, scores, idx, wout);
@@ -230,14 +354,18 @@ hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, cons
                         const float* bias, float* scores, int32_t* idx, float* w,
                         hipStream_t s) {
   if (p.T == 0) return hipSuccess;
+  const bool norm = p.norm_gamma != nullptr;
   if (act_dtype == MOE_BF16) {
     dim3 grid((p.T + kRouteTok - 1) / kRouteTok);
-    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(64 * kRouteWaves), 0, s, p,
+    auto kern = !norm ? route_bf16_kernel<0>
+                      : (p.d <= kNormLdsDim ? route_bf16_kernel<1> : route_bf16_kernel<2>);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kRouteWaves), 0, s, p,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router),
                        bias, scores, idx, w);
   } else {
     dim3 grid((p.T + 3) / 4);
-    hipLaunchKernelGGL(route_f32_kernel, grid, dim3(256), 0, s, p, static_cast<const float*>(x),
+    auto kern = norm ? route_f32_kernel<true> : route_f32_kernel<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p, static_cast<const float*>(x),
                        static_cast<const float*>(router), bias, scores, idx, w);
   }
   return hipGetLastError();

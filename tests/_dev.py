@@ -28,7 +28,8 @@ def config(shape, T=None):
                            S=s.S, I=s.I, score=s.score, renormalize=s.renormalize,
                            route_scale=s.route_scale, act=s.act, act_dtype=s.act_dtype,
                            weight_dtype=s.weight_dtype, capacity_factor=s.capacity_factor,
-                           fp8_act=s.fp8_act)
+                           fp8_act=s.fp8_act, pre_norm=s.pre_norm, norm_eps=s.norm_eps,
+                           residual=s.residual)
 
 
 def weights(lay):
@@ -38,6 +39,7 @@ def weights(lay):
     t["router"] = to_dev(lay.router)
     t["logit_bias"] = to_dev(lay.logit_bias)
     t["select_bias"] = to_dev(lay.select_bias)
+    t["norm_gamma"] = to_dev(lay.norm_gamma)
     return moe.Weights(**t)
 
 

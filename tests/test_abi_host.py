@@ -77,6 +77,7 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
     (dict(act_dtype="bf16", weight_dtype="f32"), 2),
     (dict(capacity_factor=float("nan")), 1),
     (dict(fp8_act=True), 2),                       # e4m3 activations need e4m3 weights
+    (dict(pre_norm=True, norm_eps=float("nan")), 1), (dict(norm_eps=-1e-6), 1),
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
     c = cfg(**bad)
@@ -89,6 +90,35 @@ def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
                               None) == status
     with pytest.raises(moe.MoeError):
         moe.workspace_size(c)
+
+
+def test_prenorm_config_and_route_arguments_are_checked_on_the_host(lib):
+    c = cfg(T=64, pre_norm=True, residual=True)
+    plain = moe.workspace_size(cfg(T=64))
+    assert moe.workspace_size(c) == plain + 64 * 2048 * 2       # the normalised rows
+    for field in ("pre_norm", "residual"):
+        bad = cfg(T=64)
+        setattr(bad, field, 2)
+        n = ctypes.c_size_t(0)
+        assert lib.moe_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == 1
+    fake = 4096
+    # moe_rmsnorm_route(cfg, x, gamma, router, logit_bias, select_bias, x_norm, scores, idx, w)
+    assert lib.moe_rmsnorm_route(ctypes.byref(c), fake, None, fake, None, None, fake + 4096, None,
+                                 fake, fake, None) == 1                      # no gain
+    assert lib.moe_rmsnorm_route(ctypes.byref(c), fake, fake, fake, None, None, None, None,
+                                 fake, fake, None) == 1                      # no output rows
+    assert lib.moe_rmsnorm_route(ctypes.byref(c), fake, fake, fake, None, None, fake, None,
+                                 fake, fake, None) == 1                      # x_norm aliases x
+    assert lib.moe_rmsnorm_route(ctypes.byref(c), fake, fake + 4, fake, None, None, fake + 4096,
+                                 None, fake, fake, None) == 2                # misaligned gain
+    c0 = cfg(T=0, pre_norm=True)
+    assert lib.moe_rmsnorm_route(ctypes.byref(c0), None, None, None, None, None, None, None,
+                                 None, None, None) == 0
+    # the forward of a pre-norm layer needs the gain
+    w = moe.Weights(router=fake, w_gate=fake, w_up=fake, w_down=fake, sh_gate=fake, sh_up=fake,
+                    sh_down=fake)
+    need = moe.workspace_size(c)
+    assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), fake, fake, fake, need, None) == 1
 
 
 def test_null_and_workspace_errors_are_reported_before_launch(lib):

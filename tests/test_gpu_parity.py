@@ -54,6 +54,25 @@ SMALL = {
                                          act="relu2", weight_dtype="e4m3", fp8_act=True, seed=44),
     # K = 64: one K-slice per tile, several tiles per workgroup
     "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
+    # pre-norm layers (RMSNorm before the router and experts, optional residual)
+    "small_prenorm_bf16": W.small_shape(T=300, d=320, E=16, k=4, G=4, Gk=2, S=2, I=192,
+                                        pre_norm=True, residual=True, seed=45),
+    "small_prenorm_noresid": W.small_shape(T=257, d=256, E=16, k=4, G=1, Gk=1, S=1, I=128,
+                                           pre_norm=True, norm_eps=1e-5, seed=46),
+    "small_prenorm_f32": W.small_shape(T=77, d=48, E=8, k=3, score="softmax", G=1, Gk=1, S=1,
+                                       I=32, act_dtype="f32", weight_dtype="f32",
+                                       pre_norm=True, residual=True, seed=47),
+    "small_prenorm_a8": W.small_shape(T=300, d=256, E=16, k=4, G=4, Gk=2, S=2, I=192,
+                                      weight_dtype="e4m3", fp8_act=True, pre_norm=True,
+                                      residual=True, seed=48),
+    # the widest rows staged in LDS by the pre-norm routing, and wider ones recomputed
+    "prenorm_d4096": W.small_shape(T=33, d=4096, E=8, k=2, G=1, Gk=1, S=1, I=64,
+                                   pre_norm=True, residual=True, seed=50),
+    "prenorm_d4160": W.small_shape(T=40, d=4160, E=8, k=2, G=2, Gk=1, S=0, I=64,
+                                   pre_norm=True, residual=True, seed=51),
+    "biased_prenorm": W.small_shape(T=333, d=256, E=32, k=4, G=8, Gk=3, n_g=2, S=1, I=128,
+                                    select_bias_std=0.7, capacity_factor=1.0, pre_norm=True,
+                                    residual=True, seed=49),
 }
 
 
@@ -233,6 +252,80 @@ def test_route_matches_oracle(name):
     assert (~clear).sum() <= max(4, T // 200)
     same = (g_idx == r["idx"]).all(axis=1)
     assert np.allclose(w.cpu().numpy()[same], r["w"][same], rtol=1e-5, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- pre-norm routing
+PRENORM_CASES = ["prenorm_bf16", "prenorm_decode_bf16", "small_prenorm_bf16",
+                 "small_prenorm_noresid", "small_prenorm_f32", "biased_prenorm", "prenorm_d4096",
+                 "prenorm_d4160"]
+# A normalised value that differs from the oracle's by one ulp moves a logit by about
+# |W_r| * ulp (~1e-4 here); decisions closer than this are near ties of the pre-norm step.
+PRENORM_MARGIN = 1e-3
+
+
+def _ulp(v, dtype):
+    mant = 7 if dtype == "bf16" else 23
+    a = np.abs(v)
+    return np.where(a > 0, np.ldexp(1.0, (np.floor(np.log2(np.where(a > 0, a, 1.0))) - mant).astype(int)), 0.0)
+
+
+@pytest.mark.parametrize("name", PRENORM_CASES)
+def test_rmsnorm_route_matches_oracle(name):
+    """moe_rmsnorm_route: (1) the stored normalised rows are a faithful rounding of the exact
+    RMSNorm (within one ulp; almost all equal to its nearest-even rounding); (2) its routing
+    equals moe_route on those stored rows bit for bit; (3) moe_route on the oracle's own
+    normalised rows matches the oracle's routing of them; (4) the fused routing matches the
+    oracle's except at near ties of the pre-norm step."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    cfg = config(s)
+    T, dt = s.T, s.act_dtype
+    x, gamma, router = to_dev(lay.x), to_dev(lay.norm_gamma), to_dev(lay.router)
+    lb, sb = to_dev(lay.logit_bias), to_dev(lay.select_bias)
+    x_norm = act_empty((T, s.d), dt)
+    scores = torch.empty((T, s.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.k), dtype=torch.float32, device="cuda")
+    moe.rmsnorm_route(cfg, x, gamma, router, lb, sb, x_norm, scores, idx, w)
+    torch.cuda.synchronize()
+    exact = O.rms_norm(O.decode_act(lay.x, dt), lay.norm_gamma, float(np.float32(s.norm_eps)))
+    got = act_to_f64(x_norm, dt)
+    # fp32 steps before the final rounding: the sum of d squares (relative error <= d u,
+    # u = 2^-24), halved by the root, plus division, root, reciprocal and two products:
+    # <= (d / 2 + 8) u.  For bf16 that is far below half an ulp (2^-9 relative), so the
+    # stored value is one of the two neighbours of the exact one; fp32 outputs are held to
+    # 16 ulp (the bound for d <= 48 is below 32 u = 16 ulp).
+    assert dt == "bf16" or s.d <= 48
+    n_ulp = 1 if dt == "bf16" else 16
+    assert np.all(np.abs(got - exact) <= n_ulp * _ulp(exact, dt))
+    rne = O.round_to_act(exact, dt)
+    frac = np.mean(got == rne)
+    print(f"{name}: {frac:.6f} of normalised values equal the nearest-even rounding")
+    if dt == "bf16":
+        assert frac >= 0.999
+    # (2) the router saw exactly the stored rows
+    sc2, idx2, w2 = torch.empty_like(scores), torch.empty_like(idx), torch.empty_like(w)
+    moe.route(cfg, x_norm, router, lb, sb, sc2, idx2, w2)
+    torch.cuda.synchronize()
+    assert torch.equal(scores, sc2) and torch.equal(idx, idx2) and torch.equal(w, w2)
+    # (3) moe_route on the oracle's normalised rows
+    xo = rne.astype(np.float32)
+    xo_dev = to_dev(W.encode_bf16(xo) if dt == "bf16" else xo)
+    moe.route(cfg, xo_dev, router, lb, sb, sc2, idx2, w2)
+    torch.cuda.synchronize()
+    r = O.route(lay, x=rne)
+    assert np.max(np.abs(sc2.cpu().numpy().astype(np.float64) - r["scores"])) <= 1e-5
+    mar = margins(r["keys"], s)
+    g2 = idx2.cpu().numpy()
+    clear = mar > MARGIN
+    assert np.array_equal(g2[clear], r["idx"][clear])
+    for t in np.nonzero(~clear)[0]:
+        assert valid_within_margin(g2[t], r["keys"][t], s), (t, g2[t], r["idx"][t])
+    # (4) the fused routing against the oracle's
+    g = idx.cpu().numpy()
+    same = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(g, r["idx"])])
+    assert np.all(same | (mar <= PRENORM_MARGIN))
+    assert (~same).sum() <= max(4, T // 200)
 
 
 # ----------------------------------------------------------------------------- load statistics
@@ -584,6 +677,44 @@ def test_forward_matches_oracle(name):
     assert diff <= TOL[s.act_dtype] * scale
 
 
+PRENORM_FORWARD_CASES = PRENORM_CASES + ["small_prenorm_a8"]
+
+
+@pytest.mark.parametrize("name", PRENORM_FORWARD_CASES)
+def test_forward_prenorm_matches_oracle(name):
+    """The pre-norm layer step: routing identical to moe_rmsnorm_route on the same input,
+    the oracle's own routing except at near ties of the pre-norm step, and the output of
+    every agreeing sampled row within TOL * max|MoE part| + half an ulp of the output (the
+    final rounding of a sum that includes the residual x)."""
+    s, lay, cfg, wts, ws, x, out, gpu_idx = run_forward(name)
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+    x_norm = act_empty((s.T, s.d), s.act_dtype)
+    moe.rmsnorm_route(cfg, x, to_dev(lay.norm_gamma), to_dev(lay.router), to_dev(lay.logit_bias),
+                      to_dev(lay.select_bias), x_norm, None, idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), gpu_idx)
+    rows = sample_tokens(s.T, n=128, seed=5)
+    if s.capacity_factor is not None:
+        full = O.route(lay, x=O.normalized_input(lay))
+        same_all = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, full["idx"])])
+        assert np.all(same_all | (margins(full["keys"], s) <= PRENORM_MARGIN))
+        ref = O.moe_forward(lay, tokens=rows, idx=gpu_idx)
+        same = np.ones(len(rows), dtype=bool)
+    else:
+        ref = O.moe_forward(lay, tokens=rows)
+        same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
+        assert np.all(same | (margins(ref["keys"], s) <= PRENORM_MARGIN))
+    got = act_to_f64(out, s.act_dtype)[rows]
+    xr = O.decode_act(lay.x[rows], s.act_dtype)
+    moe_part = ref["out"] - (xr if s.residual else 0.0)
+    scale = np.max(np.abs(moe_part[same]))
+    bound = TOL[s.act_dtype] * scale + 0.5 * _ulp(np.maximum(np.abs(got), np.abs(ref["out"])), s.act_dtype)
+    err = np.abs(got - ref["out"])[same]
+    print(f"{name}: max|d|/max|moe part| = {np.max(err) / scale:.3e} over {same.sum()} rows")
+    assert np.all(err <= bound[same])
+
+
 @pytest.mark.parametrize("name", ["balance_bf16", "small_f32"])
 def test_forward_load_stats_match_oracle(name):
     """The statistics moe_forward_ex writes for its own routing: f from the GPU routing
@@ -611,7 +742,8 @@ def test_forward_load_stats_match_oracle(name):
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("name", ["fusionllm_bf16", "small_swiglu_e4m3", "tiny_fp32"])
+@pytest.mark.parametrize("name", ["fusionllm_bf16", "small_swiglu_e4m3", "tiny_fp32",
+                                  "small_prenorm_bf16"])
 def test_forward_is_deterministic(name):
     s, lay, cfg, wts, ws, x, out, _ = run_forward(name)
     out2 = torch.empty_like(out)

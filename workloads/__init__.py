@@ -107,9 +107,14 @@ SHAPES = {
                              Gk=4, S=4, I=1536, act="swiglu", act_dtype="bf16",
                              weight_dtype="bf16", seed=1, x_from="fusionllm_bf16",
                              pre_norm=True, residual=True),
+    # its decode step: 64 tokens of the pre-norm layer
+    "prenorm_decode_bf16": MoeShape("prenorm_decode_bf16", T=64, d=2048, E=64, k=6,
+                                    score="sigmoid", G=8, Gk=4, S=4, I=1536, act="swiglu",
+                                    act_dtype="bf16", weight_dtype="bf16", seed=1,
+                                    x_from="fusionllm_bf16", pre_norm=True, residual=True),
 }
 ORDER = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2", "balance_bf16",
-         "fp8a_relu2", "prenorm_bf16"]
+         "fp8a_relu2", "prenorm_bf16", "prenorm_decode_bf16"]
 
 
 def shape_by_name(name: str) -> MoeShape:
