@@ -120,6 +120,26 @@ class Runner:
         wall = time.perf_counter() - t0
         return a.elapsed_time(b) / steps, wall
 
+    def graph_timed(self, steps, warmup):
+        """The same forward captured once into a HIP graph, then K replays bracketed by one
+        event pair (launch overhead of the individual kernels removed)."""
+        torch = self.torch
+        self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)   # side stream exists
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     def staged(self, steps, warmup, stages=None):
         """K forwards with events at the given stage boundaries (indices into the eight of
         moe_forward_opts); returns the mean time between consecutive recorded events.  Every
@@ -296,6 +316,7 @@ def main(argv=None):
         dlay = W.make_layer(dshape)
         drun = Runner(dshape, dlay, weights=run.w)     # same weights as the prefill layer
         d_ms, _ = drun.timed(args.steps, args.warmup)
+        d_graph_ms = drun.graph_timed(args.steps, args.warmup)
         d_stage = drun.staged(args.steps, args.warmup)
         d_up_ms = drun.staged(args.steps, args.warmup, stages=[2, 3])["up_routed"]
         counts = drun.counts()
@@ -308,6 +329,8 @@ def main(argv=None):
                          "algorithmic_bytes": nbytes, "experts_touched": touched,
                          "hbm_GBps": nbytes / (d_ms * 1e-3) / 1e9,
                          "hbm_frac": nbytes / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "graph_replay_ms_per_step": d_graph_ms,
+                         "graph_replay_hbm_frac": nbytes / (d_graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                          "stage_ms_with_events": d_stage,
                          "roofline": {"kernel": "decode up projection (routed + shared experts, one launch)",
                                       "bound": "hbm",

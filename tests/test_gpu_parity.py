@@ -742,6 +742,38 @@ def test_forward_load_stats_match_oracle(name):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("name", ["decode_bf16", "small_swiglu", "prenorm_decode_bf16",
+                                  "small_a8_swiglu"])
+def test_forward_graph_replay_matches_eager(name):
+    """moe_forward captured into a HIP graph (the shared experts' side stream joins the
+    capture through its fork and join events) and replayed several times, with eager
+    launches and host synchronisation between the replays: every replay equals the eager
+    forward bit for bit, also after the input changed in place."""
+    s, lay, cfg, wts, ws, x, out, _ = run_forward(name)    # eager run; creates the side stream
+    ref = out.clone()
+    g_out = torch.empty_like(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(cfg, wts, x, g_out, ws)
+    x2 = to_dev(W.random_act((s.T, s.d), 77, s.act_dtype, 1.0))
+    ref2 = torch.empty_like(out)
+    for i in range(4):
+        g_out.zero_()
+        if i == 2:
+            x_saved = x.clone()
+            x.copy_(x2)
+            moe.forward(cfg, wts, x, ref2, ws)       # eager result on the new input
+            torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_out, ref2 if i >= 2 else ref), f"replay {i}"
+        torch.cuda.synchronize()
+    x.copy_(x_saved)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(g_out, ref)
+
+
 @pytest.mark.parametrize("name", ["fusionllm_bf16", "small_swiglu_e4m3", "tiny_fp32",
                                   "small_prenorm_bf16"])
 def test_forward_is_deterministic(name):
