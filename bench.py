@@ -120,6 +120,31 @@ class Runner:
         wall = time.perf_counter() - t0
         return a.elapsed_time(b) / steps, wall
 
+    def backward_timed(self, steps, warmup):
+        """One forward, then K moe_backward calls on its workspace (all weight, router and
+        input gradients), bracketed by one event pair."""
+        torch, s = self.torch, self.s
+        f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+        grads = {"dx": torch.empty_like(self.out), "d_router": f32(s.E, s.d),
+                 "d_logit_bias": f32(s.E), "d_w_gate": f32(s.E, s.I, s.d),
+                 "d_w_up": f32(s.E, s.I, s.d), "d_w_down": f32(s.E, s.d, s.I)}
+        if s.S > 0:
+            grads.update(d_sh_gate=f32(s.S, s.I, s.d), d_sh_up=f32(s.S, s.I, s.d),
+                         d_sh_down=f32(s.S, s.d, s.I))
+        dout = torch.randn((s.T, s.d), device="cuda").to(torch.bfloat16).view(torch.int16)
+        bws = torch.empty(self.moe.backward_workspace_size(self.cfg), dtype=torch.uint8, device="cuda")
+        self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+        for _ in range(warmup):
+            self.moe.backward(self.cfg, self.w, self.x, dout, self.ws, grads, bws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            self.moe.backward(self.cfg, self.w, self.x, dout, self.ws, grads, bws)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps, bws.numel()
+
     def graph_timed(self, steps, warmup):
         """The same forward captured once into a HIP graph, then K replays bracketed by one
         event pair (launch overhead of the individual kernels removed)."""
@@ -261,6 +286,7 @@ def main(argv=None):
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-prenorm", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
@@ -370,6 +396,19 @@ def main(argv=None):
                           "rmsnorm_route_ms": p_route, "plain_route_ms": stage_ms["route"],
                           "combine_with_residual_ms": p_comb,
                           "plain_combine_ms": stage_ms["combine"]}
+    if not args.no_backward and shape.name == "fusionllm_bf16":
+        # gradients of the same layer: every data and weight gradient and the router's
+        b_ms, b_ws = run.backward_timed(max(5, args.steps // 5), 2)
+        c_act = 6 if shape.act == "swiglu" else 4
+        gemm_fwd = (shape.k + shape.S) * T * c_act * shape.d * shape.I
+        alg = 2 * gemm_fwd + 3 * 2 * T * shape.d * shape.E      # dgrad + wgrad of every GEMM
+        res["backward"] = {"workload": shape.name, "ms_per_step": b_ms,
+                           "tokens_per_s": T / (b_ms * 1e-3),
+                           "algorithmic_tflop": alg / 1e12,
+                           "tflops": alg / (b_ms * 1e-3) / 1e12,
+                           "mfma_frac": alg / (b_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "recomputed_up_tflop": gemm_fwd * (2 / 3 if shape.act == "swiglu" else 1 / 2) / 1e12,
+                           "workspace_gb": b_ws / 1e9}
     if not args.no_fp8 and shape.name == "fusionllm_bf16":
         # the e4m3-weight layer (T = 16384, ReLU^2): bf16 activations, then e4m3 activations
         # in the up projections (same device weights)

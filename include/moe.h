@@ -274,6 +274,48 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                           void* out, void* ws, size_t ws_bytes, hipStream_t stream,
                           const moe_forward_opts* opts);
 
+/* ---------------------------------------------------------------------------------- */
+/* Backward pass.                                                                      */
+
+/* Gradients written by moe_backward: dx in the activation dtype, every other one fp32 in
+ * the layout of its parameter.  All device pointers; NULL entries (other than dx) are not
+ * computed. */
+typedef struct {
+  void* dx;             /* [T, d] act_dtype: dL/dx (includes dout when cfg->residual)     */
+  float* d_router;      /* [E, d]                                                         */
+  float* d_logit_bias;  /* [E]   (the gradient of an added logit bias)                    */
+  float* d_w_gate;      /* [E, I, d]                                                      */
+  float* d_w_up;        /* [E, I, d]  (SwiGLU only)                                       */
+  float* d_w_down;      /* [E, d, I]                                                      */
+  float* d_sh_gate;     /* [S, I, d]                                                      */
+  float* d_sh_up;       /* [S, I, d]  (SwiGLU only)                                       */
+  float* d_sh_down;     /* [S, d, I]                                                      */
+} moe_grads;
+
+/* Bytes of device workspace moe_backward needs (host only). */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Gradients of L = sum(dout * out) for the forward that moe_forward computed from the same
+ * cfg, weights and x into fwd_ws (its routing, permutation, h and y are read from there, so
+ * the forward must have been enqueued before on the same stream and fwd_ws left unchanged).
+ * The selection is held fixed (its derivative is zero); every other step is differentiated:
+ *   expert FFNs: dy = w dout, dW2 = dy^T h, dh = dy W2, SwiGLU da = dh b silu'(a),
+ *     db = dh silu(a) (ReLU^2: da = dh 2 max(a, 0)), dW1 = da^T x, dW3 = db^T x,
+ *     dx += da W1 + db W3 (a, b recomputed); shared experts alike with weight 1;
+ *   routing weights: dw_j = dout . y_hat_j; renormalised weights w_j = c s_j / sum_i s_i
+ *     give ds = (c / S)(dw - sum_j dw_j s_j / S) on the selected scores (dropped slots have
+ *     dw = 0 but keep their place in S); sigmoid ds s (1 - s), or softmax through all E
+ *     logits; d_router = dl^T x, d_logit_bias = sum_t dl, dx += dl W_r;
+ *   residual: dx += dout.
+ * Supported: act_dtype and weight_dtype MOE_BF16, no pre_norm, no fp8_act, route_scale != 0
+ * (else MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARG).  dout [T, d] bf16.  Weight gradients
+ * accumulate in fp32 over the tokens in a fixed order; the result is deterministic.
+ * Source: the chain rule through the forward of moe_forward; the router gradient through
+ * the logits follows item 4 of section "常见陷阱" of "大模型工程（一）：Transformer 到 MoE". */
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                        const void* dout, const void* fwd_ws, size_t fwd_ws_bytes,
+                        const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status status);
 

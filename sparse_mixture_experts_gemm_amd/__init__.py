@@ -16,7 +16,7 @@ __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
     "workspace_size", "route", "rmsnorm_route", "select", "load_stats", "permute",
     "quantize_rows",
-    "grouped_gemm", "combine", "forward",
+    "grouped_gemm", "combine", "forward", "backward_workspace_size", "backward", "GRAD_FIELDS",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
     "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
@@ -32,7 +32,8 @@ MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_rmsnorm_route", "moe_select",
                     "moe_load_stats",
                     "moe_permute", "moe_quantize_rows", "moe_grouped_gemm", "moe_combine",
-                    "moe_forward", "moe_forward_ex", "moe_status_string", "moe_last_hip_error"]
+                    "moe_forward", "moe_forward_ex", "moe_backward_workspace_size", "moe_backward",
+                    "moe_status_string", "moe_last_hip_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -85,6 +86,14 @@ class Weights:
         self.c = _WeightsC(**{n: _ptr(t) for n, t in self.tensors.items()})
 
 
+GRAD_FIELDS = ["dx", "d_router", "d_logit_bias", "d_w_gate", "d_w_up", "d_w_down", "d_sh_gate",
+               "d_sh_up", "d_sh_down"]
+
+
+class _GradsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+
+
 class _OptsC(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.c_void_p * 8), ("load_stats", ctypes.c_void_p),
                 ("aux_alpha", ctypes.c_float)]
@@ -116,6 +125,8 @@ def lib():
             "moe_quantize_rows": [cfgp, vp, i32, i32, vp, vp, vp],
             "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
             "moe_forward_ex": [cfgp, wp, vp, vp, vp, sz, vp, ctypes.POINTER(_OptsC)],
+            "moe_backward_workspace_size": [cfgp, ctypes.POINTER(sz)],
+            "moe_backward": [cfgp, wp, vp, vp, vp, sz, ctypes.POINTER(_GradsC), vp, sz, vp],
             "moe_last_hip_error": [],
         }
         for name, args in sig.items():
@@ -250,3 +261,25 @@ def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None, stage
     _check(lib().moe_forward_ex(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
                                 _ptr(ws), nb, _stream(stream), ctypes.byref(opts)),
            "moe_forward_ex")
+
+
+def backward_workspace_size(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_backward_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return n.value
+
+
+def backward(cfg, weights: Weights, x, dout, fwd_ws, grads: dict, ws, fwd_ws_bytes=None,
+             ws_bytes=None, stream=None):
+    """Gradients of sum(dout * out) for the forward computed into fwd_ws.  grads maps the
+    names of GRAD_FIELDS to device tensors (dx required; absent names are not computed)."""
+    unknown = set(grads) - set(GRAD_FIELDS)
+    if unknown:
+        raise TypeError(f"unknown gradient fields {sorted(unknown)}")
+    g = _GradsC(**{n: _ptr(grads.get(n)) for n in GRAD_FIELDS})
+    fb = fwd_ws_bytes if fwd_ws_bytes is not None else fwd_ws.numel() * fwd_ws.element_size()
+    nb = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(lib().moe_backward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(dout),
+                              _ptr(fwd_ws), fb, ctypes.byref(g), _ptr(ws), nb, _stream(stream)),
+           "moe_backward")

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "decode.hip",
-           "stats.hip", "quant.hip"]
+           "stats.hip", "quant.hip", "backward.hip"]
 EXTRA_FLAGS = os.environ.get("MOE_EXTRA_HIPCC_FLAGS", "").split()
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <mutex>
 
+#include "backward.h"
 #include "internal.h"
 #include "moe.h"
 
@@ -175,6 +176,65 @@ Carve carve(const moe_config* c) {
   w.y_shared = take(S > 0 ? T * d * as : 0);
   w.total = o;
   return w;
+}
+
+// Workspace of moe_backward, in carve order.
+struct BwdCarve {
+  size_t w2t, w13t, sh_w2t, sh_w13t;           // transposed weight copies (bf16)
+  size_t scores, idx, tw, dw, dl, koff_r, koff_s;
+  size_t dh_r, dh_s, dab_r, dab_s, dxp_r, dx_s;  // data-gradient intermediates (bf16)
+  size_t xt_r, dyt_r, ht_r, dat_r, dbt_r;        // K-major token copies, routed
+  size_t doutt_s, xt_s, ht_s, dat_s, dbt_s;      // and shared
+  size_t rg, total;
+};
+
+BwdCarve bwd_carve(const moe_config* c) {
+  const size_t T = (size_t)c->num_tokens, k = (size_t)c->top_k, E = (size_t)c->num_experts;
+  const size_t d = (size_t)c->dim, I = (size_t)c->inter_dim, S = (size_t)c->num_shared;
+  const size_t nab = c->act == MOE_ACT_SWIGLU ? 2 : 1;   // pre-activations per inter feature
+  const size_t kr = moe::padded_k_bound((int)(T * k), (int)E), ks = moe::padded_k_bound((int)T, 1);
+  BwdCarve b{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += align_up(bytes); return at; };
+  b.w2t = take(E * I * d * 2);
+  b.w13t = take(E * d * nab * I * 2);
+  b.sh_w2t = take(S * I * d * 2);
+  b.sh_w13t = take(d * nab * S * I * 2);
+  b.scores = take(T * E * 4);
+  b.idx = take(T * k * 4);
+  b.tw = take(T * k * 4);
+  b.dw = take(T * k * 4);
+  b.dl = take(T * E * 4);
+  b.koff_r = take((E + 1) * 4);
+  b.koff_s = take(2 * 4);
+  b.dh_r = take(T * k * I * 2);
+  b.dh_s = take(T * S * I * 2);
+  b.dab_r = take(T * k * nab * I * 2);
+  b.dab_s = take(T * nab * S * I * 2);
+  b.dxp_r = take(T * k * d * 2);
+  b.dx_s = take(S > 0 ? T * d * 2 : 0);
+  b.xt_r = take(d * kr * 2);
+  b.dyt_r = take(d * kr * 2);
+  b.ht_r = take(I * kr * 2);
+  b.dat_r = take(I * kr * 2);
+  b.dbt_r = take(nab == 2 ? I * kr * 2 : 0);
+  b.doutt_s = take(S > 0 ? d * ks * 2 : 0);
+  b.xt_s = take(S > 0 ? d * ks * 2 : 0);
+  b.ht_s = take(S * I * ks * 2);
+  b.dat_s = take(S * I * ks * 2);
+  b.dbt_s = take(nab == 2 ? S * I * ks * 2 : 0);
+  b.rg = take(moe::router_wgrad_ws_bytes((int)T, (int)d, (int)E));
+  b.total = o;
+  return b;
+}
+
+moe_status check_backward_config(const moe_config* c) {
+  moe_status st = check_config(c);
+  if (st != MOE_OK) return st;
+  if (!std::isfinite(c->route_scale) || c->route_scale == 0.0f) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_BF16 || c->pre_norm || c->fp8_act)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
 }
 
 moe_status gemm_params(const moe_config* c, moe_stage stage, moe_expert_set set, const void* a,
@@ -586,6 +646,196 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
       // are released once they complete
       (void)hipEventDestroy(fork_ev);
       (void)hipEventDestroy(join);
+    }
+    return hip_status(e);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_backward_config(cfg);
+    if (st != MOE_OK) return st;
+    *bytes = bwd_carve(cfg).total;
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                        const void* dout, const void* fwd_ws, size_t fwd_ws_bytes,
+                        const moe_grads* grads, void* ws, size_t ws_bytes, hipStream_t stream) {
+  try {
+    moe_status st = check_backward_config(cfg);
+    if (st != MOE_OK) return st;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    if (w == nullptr || x == nullptr || dout == nullptr || grads == nullptr || grads->dx == nullptr ||
+        w->router == nullptr || w->w_gate == nullptr || w->w_down == nullptr)
+      return MOE_ERR_INVALID_ARG;
+    const bool swiglu = cfg->act == MOE_ACT_SWIGLU;
+    const bool shared = cfg->num_shared > 0;
+    if (swiglu && w->w_up == nullptr) return MOE_ERR_INVALID_ARG;
+    if (shared && (w->sh_gate == nullptr || w->sh_down == nullptr || (swiglu && w->sh_up == nullptr)))
+      return MOE_ERR_INVALID_ARG;
+    const Carve cv = carve(cfg);
+    if (fwd_ws == nullptr || fwd_ws_bytes < cv.total) return MOE_ERR_WORKSPACE;
+    const BwdCarve bc = bwd_carve(cfg);
+    if (ws == nullptr || ws_bytes < bc.total) return MOE_ERR_WORKSPACE;
+    const void* ptrs[] = {x, dout, fwd_ws, ws, grads->dx, w->router, w->w_gate, w->w_up, w->w_down,
+                          w->sh_gate, w->sh_up, w->sh_down};
+    for (const void* q : ptrs)
+      if (q != nullptr && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
+    int cus = 0;
+    st = current_cus(&cus);
+    if (st != MOE_OK) return st;
+
+    const int T = cfg->num_tokens, k = cfg->top_k, E = cfg->num_experts, Tk = T * k;
+    const int d = cfg->dim, I = cfg->inter_dim, S = cfg->num_shared, SI = S * I;
+    const int nab = swiglu ? 2 : 1;
+    const char* fb = static_cast<const char*>(fwd_ws);
+    auto fat = [&](size_t off) { return static_cast<const void*>(fb + off); };
+    char* wb = static_cast<char*>(ws);
+    auto at = [&](size_t off) { return static_cast<void*>(wb + off); };
+    const int32_t* idx = static_cast<const int32_t*>(fat(cv.topk_idx));
+    const float* topk_w = static_cast<const float*>(fat(cv.topk_w));
+    const int32_t* offsets = static_cast<const int32_t*>(fat(cv.offsets));
+    const int32_t* perm_token = static_cast<const int32_t*>(fat(cv.perm_token));
+    const int32_t* slot_pos = static_cast<const int32_t*>(fat(cv.slot_pos));
+    const float* perm_weight = static_cast<const float*>(fat(cv.perm_weight));
+    const void* h_r = fat(cv.h_routed);
+    const void* h_s = fat(cv.h_shared);
+    const void* y_r = fat(cv.y_routed);
+    uint16_t* w2t = static_cast<uint16_t*>(at(bc.w2t));
+    uint16_t* w13t = static_cast<uint16_t*>(at(bc.w13t));
+    uint16_t* sh_w2t = static_cast<uint16_t*>(at(bc.sh_w2t));
+    uint16_t* sh_w13t = static_cast<uint16_t*>(at(bc.sh_w13t));
+    float* dw = static_cast<float*>(at(bc.dw));
+    float* dl = static_cast<float*>(at(bc.dl));
+    int32_t* koff_r = static_cast<int32_t*>(at(bc.koff_r));
+    int32_t* koff_s = static_cast<int32_t*>(at(bc.koff_s));
+    const moe_weights wt_fwd = *w;
+
+    hipError_t e = hipSuccess;
+    auto ok = [&]() { return e == hipSuccess; };
+    // 1. transposed weight copies: W2^T [E][I][d]; [W1^T | W3^T] [E][d][nab I]; shared alike
+    if (ok()) e = moe::launch_transpose_mat(w->w_down, w2t, E, d, I, (long long)I * d, d, stream);
+    if (ok()) e = moe::launch_transpose_mat(w->w_gate, w13t, E, I, d, (long long)d * nab * I, nab * I, stream);
+    if (ok() && swiglu)
+      e = moe::launch_transpose_mat(w->w_up, w13t + I, E, I, d, (long long)d * nab * I, nab * I, stream);
+    if (shared) {
+      if (ok()) e = moe::launch_transpose_mat(w->sh_down, sh_w2t, S, d, I, (long long)I * d, d, stream);
+      if (ok()) e = moe::launch_transpose_mat(w->sh_gate, sh_w13t, S, I, d, I, nab * SI, stream);
+      if (ok() && swiglu)
+        e = moe::launch_transpose_mat(w->sh_up, sh_w13t + SI, S, I, d, I, nab * SI, stream);
+    }
+    // 2. dh = (w dout) W2 (routed rows gathered from dout), dout W2 (shared)
+    moe::GemmParams g{};
+    g.a = dout; g.row_index = perm_token; g.offsets = offsets; g.nseg = E; g.rows = Tk;
+    g.d = d; g.I = I; g.S = S; g.N = I; g.K = d; g.kblock = d; g.w_down = w2t;
+    g.row_weight = perm_weight; g.out = at(bc.dh_r);
+    if (ok()) e = moe::launch_grouped_gemm(g, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    if (shared) {
+      moe::GemmParams gs{};
+      gs.a = dout; gs.nseg = 1; gs.rows = T; gs.d = d; gs.I = I; gs.S = S; gs.N = SI; gs.K = d;
+      gs.kblock = d; gs.w_down = sh_w2t; gs.out = at(bc.dh_s);
+      if (ok()) e = moe::launch_grouped_gemm(gs, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    }
+    // 3. up projections recomputed, activation backward in the epilogue: [da | db]
+    moe::GemmParams u{};
+    u.a = x; u.row_index = perm_token; u.offsets = offsets; u.nseg = E; u.rows = Tk; u.d = d;
+    u.I = I; u.S = S; u.N = I; u.K = d; u.kblock = d; u.w_gate = wt_fwd.w_gate; u.w_up = wt_fwd.w_up;
+    u.out = at(bc.dab_r); u.dact = at(bc.dh_r);
+    if (ok()) e = moe::launch_up_backward(u, cfg->act, cus, stream);
+    if (shared) {
+      moe::GemmParams us{};
+      us.a = x; us.nseg = 1; us.rows = T; us.d = d; us.I = I; us.S = S; us.N = SI; us.K = d;
+      us.kblock = d; us.w_gate = w->sh_gate; us.w_up = w->sh_up; us.out = at(bc.dab_s);
+      us.dact = at(bc.dh_s);
+      if (ok()) e = moe::launch_up_backward(us, cfg->act, cus, stream);
+    }
+    // 4. dx of the experts: [da | db] [W1 ; W3] per row (permuted for the routed ones)
+    moe::GemmParams dxg{};
+    dxg.a = at(bc.dab_r); dxg.offsets = offsets; dxg.nseg = E; dxg.rows = Tk; dxg.d = d; dxg.I = I;
+    dxg.S = S; dxg.N = d; dxg.K = nab * I; dxg.kblock = nab * I; dxg.w_down = w13t; dxg.out = at(bc.dxp_r);
+    if (ok()) e = moe::launch_grouped_gemm(dxg, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    if (shared) {
+      moe::GemmParams dxs{};
+      dxs.a = at(bc.dab_s); dxs.nseg = 1; dxs.rows = T; dxs.d = d; dxs.I = I; dxs.S = S; dxs.N = d;
+      dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = sh_w13t; dxs.out = at(bc.dx_s);
+      if (ok()) e = moe::launch_grouped_gemm(dxs, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    }
+    // 5. router: scores recomputed, routing-weight and logit gradients
+    moe::RouteParams rp = route_params(cfg);
+    rp.select_bias = w->select_bias;
+    if (ok())
+      e = moe::launch_route(rp, MOE_BF16, x, w->router, w->logit_bias, static_cast<float*>(at(bc.scores)),
+                            static_cast<int32_t*>(at(bc.idx)), static_cast<float*>(at(bc.tw)), stream);
+    if (ok()) e = moe::launch_routing_weight_grad(T, k, d, dout, y_r, slot_pos, topk_w, dw, stream);
+    if (ok()) e = moe::launch_router_grad(rp, static_cast<const float*>(at(bc.scores)), idx, dw, dl, stream);
+    if (ok() && (grads->d_router != nullptr || grads->d_logit_bias != nullptr))
+      e = moe::launch_router_wgrad(T, d, E, x, dl, grads->d_router, grads->d_logit_bias, at(bc.rg), stream);
+    // 6. dx = dl W_r + experts (+ dout)
+    if (ok())
+      e = moe::launch_dx_combine(T, d, E, k, dl, w->router, at(bc.dxp_r), slot_pos,
+                                 shared ? at(bc.dx_s) : nullptr, cfg->residual ? dout : nullptr,
+                                 grads->dx, stream);
+    // 7. weight gradients: contractions over each expert's tokens, on K-major copies
+    if (grads->d_w_gate != nullptr || grads->d_w_up != nullptr || grads->d_w_down != nullptr) {
+      if (ok()) e = moe::launch_seg_koff(offsets, E, Tk, koff_r, stream);
+      auto tr = [&](const void* src, int ld, int col, const int32_t* ri, const float* sc, int C, size_t dst) {
+        if (ok()) e = moe::launch_transpose_rows(src, ld, col, ri, sc, offsets, E, Tk, koff_r, C, at(dst), stream);
+      };
+      auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
+        moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_r,
+                           M, N, nsplit, out};
+        if (ok()) e = moe::launch_wgrad(p, E, stream);
+      };
+      if (grads->d_w_down != nullptr) {
+        tr(dout, d, 0, perm_token, perm_weight, d, bc.dyt_r);
+        tr(h_r, I, 0, nullptr, nullptr, I, bc.ht_r);
+        wg(bc.dyt_r, bc.ht_r, d, I, I, grads->d_w_down);
+      }
+      if (grads->d_w_gate != nullptr || (swiglu && grads->d_w_up != nullptr)) {
+        tr(x, d, 0, perm_token, nullptr, d, bc.xt_r);
+        if (grads->d_w_gate != nullptr) {
+          tr(at(bc.dab_r), nab * I, 0, nullptr, nullptr, I, bc.dat_r);
+          wg(bc.dat_r, bc.xt_r, I, d, d, grads->d_w_gate);
+        }
+        if (swiglu && grads->d_w_up != nullptr) {
+          tr(at(bc.dab_r), 2 * I, I, nullptr, nullptr, I, bc.dbt_r);
+          wg(bc.dbt_r, bc.xt_r, I, d, d, grads->d_w_up);
+        }
+      }
+    }
+    if (shared && (grads->d_sh_gate != nullptr || grads->d_sh_up != nullptr || grads->d_sh_down != nullptr)) {
+      if (ok()) e = moe::launch_seg_koff(nullptr, 1, T, koff_s, stream);
+      auto tr = [&](const void* src, int ld, int col, int C, size_t dst) {
+        if (ok()) e = moe::launch_transpose_rows(src, ld, col, nullptr, nullptr, nullptr, 1, T, koff_s, C, at(dst), stream);
+      };
+      auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
+        moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_s,
+                           M, N, nsplit, out};
+        if (ok()) e = moe::launch_wgrad(p, 1, stream);
+      };
+      if (grads->d_sh_down != nullptr) {
+        tr(dout, d, 0, d, bc.doutt_s);
+        tr(h_s, SI, 0, SI, bc.ht_s);
+        wg(bc.doutt_s, bc.ht_s, d, SI, I, grads->d_sh_down);
+      }
+      if (grads->d_sh_gate != nullptr || (swiglu && grads->d_sh_up != nullptr)) {
+        tr(x, d, 0, d, bc.xt_s);
+        if (grads->d_sh_gate != nullptr) {
+          tr(at(bc.dab_s), nab * SI, 0, SI, bc.dat_s);
+          wg(bc.dat_s, bc.xt_s, SI, d, d, grads->d_sh_gate);
+        }
+        if (swiglu && grads->d_sh_up != nullptr) {
+          tr(at(bc.dab_s), 2 * SI, SI, SI, bc.dbt_s);
+          wg(bc.dbt_s, bc.xt_s, SI, d, d, grads->d_sh_up);
+        }
+      }
     }
     return hip_status(e);
   } catch (...) {

@@ -1,0 +1,60 @@
+// Host-side declarations of the backward-pass launchers (backward.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace moe {
+
+// Weight-gradient GEMM: out(seg, m, n) = sum_k A_seg[m][k] B_seg[n][k] over the padded
+// tokens of each segment (see backward.hip for the layouts).
+struct WgradParams {
+  const uint16_t* a;        // K-major copies, segment seg at a + M * koff[seg]
+  const uint16_t* b;        // at b + N * koff[seg]
+  const int32_t* koff;      // [nseg + 1] padded token offsets (multiples of 64)
+  int M, N;
+  int nsplit;               // column-block size of the output layout (N: plain [M][N])
+  float* out;               // fp32 [nseg][M][N] (in nsplit blocks)
+};
+
+// out[b * obs + c * ld + r] = in[b][r][c] (bf16, R and C multiples of 64).
+hipError_t launch_transpose_mat(const void* in, void* out, int batch, int R, int C, long long obs,
+                                int ld, hipStream_t s);
+
+// koff[e] = exclusive scan of the segments' rows rounded up to 64 (offsets null: one
+// segment of `rows` rows).
+hipError_t launch_seg_koff(const int32_t* offsets, int nseg, int rows, int32_t* koff, hipStream_t s);
+
+// Upper bound of koff[nseg] (elements of the padded token axis).
+size_t padded_k_bound(int rows, int nseg);
+
+// K-major, zero-padded copy of the segment rows of in (bf16, row stride ld_in, columns
+// [col_in, col_in + C)), rows gathered through row_index and scaled by row_scale if given.
+hipError_t launch_transpose_rows(const void* in, int ld_in, int col_in, const int32_t* row_index,
+                                 const float* row_scale, const int32_t* offsets, int nseg, int rows,
+                                 const int32_t* koff, int C, void* out, hipStream_t s);
+
+// dw[t*k + j] = dout[t] . y[slot_pos[t*k + j]] / topk_w[t*k + j] (0 for dropped slots).
+hipError_t launch_routing_weight_grad(int T, int k, int d, const void* dout, const void* y,
+                                      const int32_t* slot_pos, const float* topk_w, float* dw,
+                                      hipStream_t s);
+
+// Logit gradients dl [T, E] from the scores [T, E], the selection and dw.
+hipError_t launch_router_grad(const RouteParams& p, const float* scores, const int32_t* idx,
+                              const float* dw, float* dl, hipStream_t s);
+
+// d_router [E, d] = dl^T x and d_bias [E] = column sums of dl (either may be null).
+size_t router_wgrad_ws_bytes(int T, int d, int E);
+hipError_t launch_router_wgrad(int T, int d, int E, const void* x, const float* dl, float* d_router,
+                               float* d_bias, void* ws, hipStream_t s);
+
+// dx = dl W_r + scattered dx_perm rows + dx_shared (+ residual), bf16.
+hipError_t launch_dx_combine(int T, int d, int E, int k, const float* dl, const void* wr,
+                             const void* dx_perm, const int32_t* slot_pos, const void* dx_shared,
+                             const void* residual, void* dx, hipStream_t s);
+
+hipError_t launch_wgrad(const WgradParams& p, int nseg, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,509 @@
+// Backward pass of the MoE layer: the kernels besides the grouped GEMMs.
+//
+// The layer's gradients follow the chain rule through the forward ("大模型工程（一）：Transformer
+// 到 MoE": the MoEBlock listing and section "MoE 数学：路由、容量与平衡详解" for the routing,
+// section "变了什么，为什么变" item 3 for SwiGLU; section "常见陷阱" item 4: the router
+// gradient goes through the logits themselves).  The data gradients (dh = dy W2, dx =
+// da W1 + db W3) run on the forward's grouped-GEMM kernel with transposed weight copies;
+// the kernels here are the transposes, the routing-weight and router gradients, the final
+// combine of dx, and the weight-gradient GEMMs, whose contraction runs over the tokens of
+// each expert (K differs per expert).
+//
+// Layouts (bf16 unless noted):
+//  * K-major copies of activations for the weight gradients: segment e holds [C][Kp_e] with
+//    Kp_e = n_e rounded up to 64 and zero padding, at element offset C * koff[e], where koff
+//    is the exclusive scan of the Kp_e (built on the device from the expert offsets).
+//  * weight gradients are fp32 in the weights' [out, in] layout.
+#include "backward.h"
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kT = 64;   // transpose tile
+
+// out[b * obs + c * ld + r] = in[b * R * C + r * C + c] for r < R, c < C (both multiples of
+// 64): 64 x 64 tiles through LDS, 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __restrict__ in,
+                                                            uint16_t* __restrict__ out, int R,
+                                                            int C, long long obs, int ld) {
+  __shared__ uint16_t t[kT][kT + 8];
+  const int tiles_c = C / kT;
+  const int r0 = (blockIdx.x / tiles_c) * kT, c0 = (blockIdx.x % tiles_c) * kT;
+  const uint16_t* src = in + (size_t)blockIdx.y * R * C;
+  uint16_t* dst = out + (size_t)blockIdx.y * obs;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = h * 32 + tid / 8, c = (tid % 8) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + r) * C + c0 + c);
+    *reinterpret_cast<uint4*>(&t[r][c]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 32 + tid / 8, r = (tid % 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[r + 2 * i][c] | ((uint32_t)t[r + 2 * i + 1][c] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * ld + r0 + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// koff[e] = sum over e' < e of (rows of e' rounded up to 64); koff[nseg] = total.  One wave.
+__global__ void seg_koff_kernel(const int32_t* __restrict__ offsets, int nseg, int rows,
+                                int32_t* __restrict__ koff) {
+  const int lane = threadIdx.x;
+  int n = 0;
+  if (lane < nseg) n = offsets != nullptr ? offsets[lane + 1] - offsets[lane] : rows;
+  int incl = (n + 63) & ~63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane < nseg) koff[lane + 1] = incl;
+  if (lane == 0) koff[0] = 0;
+}
+
+// K-major, zero-padded copy of segment rows: out[C * koff[e] + c * Kp_e + k] =
+// scale(p) * in[src(p) * ld_in + col_in + c] for p = row0_e + k, k < n_e; 0 for n_e <= k < Kp_e.
+// src(p) = row_index[p] (or p); scale(p) = row_scale[p] (or 1), applied in fp32 before the
+// rounding to bf16.  Blocks: (64-row block of the padded K space) x (64-column block).
+__global__ __launch_bounds__(256) void transpose_rows_kernel(
+    const uint16_t* __restrict__ in, int ld_in, int col_in, const int32_t* __restrict__ row_index,
+    const float* __restrict__ row_scale, const int32_t* __restrict__ offsets, int nseg, int rows,
+    const int32_t* __restrict__ koff, int C, uint16_t* __restrict__ out) {
+  __shared__ uint16_t t[kT][kT + 8];
+  const int cblocks = C / kT;
+  const int kb = blockIdx.x / cblocks, c0 = (blockIdx.x % cblocks) * kT;
+  const int k0 = kb * kT;
+  if (k0 >= koff[nseg]) return;   // uniform: beyond the padded K space
+  int lo = 0, hi = nseg - 1;      // last segment with koff[seg] <= k0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (koff[mid] <= k0) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int kp = koff[e + 1] - koff[e];
+  const int kl0 = k0 - koff[e];
+  const int row0 = offsets != nullptr ? offsets[e] : 0;
+  const int n = offsets != nullptr ? offsets[e + 1] - row0 : rows;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = h * 32 + tid / 8, c = (tid % 8) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (kl0 + k < n) {
+      const int p = row0 + kl0 + k;
+      const int sr = row_index != nullptr ? row_index[p] : p;
+      v = *reinterpret_cast<const uint4*>(in + (size_t)sr * ld_in + col_in + c0 + c);
+      if (row_scale != nullptr) {
+        const float s = row_scale[p];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = pack_bf16x2(s * bf16_bits_to_f32(w[i] & 0xffffu), s * bf16_bits_to_f32(w[i] >> 16));
+        v = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    *reinterpret_cast<uint4*>(&t[k][c]) = v;
+  }
+  __syncthreads();
+  uint16_t* dst = out + (size_t)C * koff[e];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 32 + tid / 8, k = (tid % 8) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[k + 2 * i][c] | ((uint32_t)t[k + 2 * i + 1][c] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * kp + kl0 + k) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Gradient of each routing weight: dw[t, j] = dout[t] . y_hat[p], with y_hat = y[p] / w[t, j]
+// the expert's unweighted output (y is the forward's weighted output); 0 for dropped slots.
+// One wave per slot, fixed-order sum.
+__global__ __launch_bounds__(256) void routing_weight_grad_kernel(
+    int Tk, int k, int d, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y,
+    const int32_t* __restrict__ slot_pos, const float* __restrict__ topk_w, float* __restrict__ dw) {
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (q >= Tk) return;   // whole wave
+  const int p = slot_pos[q];
+  if (p < 0) {
+    if (lane == 0) dw[q] = 0.0f;
+    return;
+  }
+  const uint16_t* g = dout + (size_t)(q / k) * d;
+  const uint16_t* yr = y + (size_t)p * d;
+  float acc = 0.0f;
+  for (int c = lane * 8; c < d; c += 64 * 8) {
+    const uint4 a = *reinterpret_cast<const uint4*>(g + c);
+    const uint4 b = *reinterpret_cast<const uint4*>(yr + c);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(bf16_bits_to_f32(wa[i] & 0xffffu), bf16_bits_to_f32(wb[i] & 0xffffu), acc);
+      acc = fmaf(bf16_bits_to_f32(wa[i] >> 16), bf16_bits_to_f32(wb[i] >> 16), acc);
+    }
+  }
+  acc = wave_sum_f(acc);
+  if (lane == 0) dw[q] = acc / topk_w[q];
+}
+
+// Logit gradients of one token per wave (lane = expert): the routing weights w_j = c s_j /
+// sum_i s_i over the selected experts (or c s_j) are differentiated with respect to every
+// score, then through sigmoid, or through softmax over all E logits.
+__global__ __launch_bounds__(256) void router_grad_kernel(RouteParams p, const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ dw,
+                                                          float* __restrict__ dl) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= p.T) return;   // whole wave
+  const bool valid = lane < p.E;
+  const float s = valid ? scores[(size_t)t * p.E + lane] : 0.0f;
+  float tot = 0.0f, wsum = 0.0f;
+  for (int j = 0; j < p.k; ++j) {
+    const int e = idx[(size_t)t * p.k + j];
+    const float se = __shfl(s, e, 64);
+    tot += se;
+    wsum += dw[(size_t)t * p.k + j] * se;
+  }
+  float ds = 0.0f;
+  for (int j = 0; j < p.k; ++j) {
+    if (idx[(size_t)t * p.k + j] != lane) continue;
+    const float g = dw[(size_t)t * p.k + j];
+    ds += p.renormalize ? (p.route_scale / tot) * (g - wsum / tot) : p.route_scale * g;
+  }
+  float g;
+  if (p.score_fn == MOE_SCORE_SIGMOID) {
+    g = ds * s * (1.0f - s);
+  } else {
+    const float dot = wave_sum_f(valid ? ds * s : 0.0f);
+    g = s * (ds - dot);
+  }
+  if (valid) dl[(size_t)t * p.E + lane] = g;
+}
+
+// Router weight and logit-bias gradients, in two passes with a fixed summation order:
+// partials over chunks of 256 tokens, then their sum.  Block (64-column block of d, chunk);
+// thread: 4 experts x 4 columns.
+constexpr int kRgChunk = 256;
+
+__global__ __launch_bounds__(256) void router_wgrad_partial_kernel(
+    int T, int d, int E, const uint16_t* __restrict__ x, const float* __restrict__ dl,
+    float* __restrict__ part, float* __restrict__ part_bias) {
+  const int c0 = blockIdx.x * 64, chunk = blockIdx.y;
+  const int eg = threadIdx.x / 16, cg = threadIdx.x % 16;
+  const int t0 = chunk * kRgChunk, t1 = min(T, t0 + kRgChunk);
+  float acc[4][4] = {};
+  float accb[4] = {};
+  for (int t = t0; t < t1; ++t) {
+    const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + c0 + cg * 4);
+    const float xf[4] = {bf16_bits_to_f32(xv.x & 0xffffu), bf16_bits_to_f32(xv.x >> 16),
+                         bf16_bits_to_f32(xv.y & 0xffffu), bf16_bits_to_f32(xv.y >> 16)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = eg * 4 + i;
+      const float g = e < E ? dl[(size_t)t * E + e] : 0.0f;
+      accb[i] += g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(g, xf[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = eg * 4 + i;
+    if (e >= E) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[((size_t)chunk * E + e) * d + c0 + cg * 4 + j] = acc[i][j];
+    if (blockIdx.x == 0 && cg == 0) part_bias[(size_t)chunk * E + e] = accb[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(
+    int nchunks, int n, const float* __restrict__ part, float* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int c = 0; c < nchunks; ++c) s += part[(size_t)c * n + i];
+  out[i] = s;
+}
+
+// dx[t] = sum_e dl[t, e] W_r[e] + sum_j dx_perm[slot_pos[t, j]] + dx_shared[t] (+ dout[t]),
+// fp32 in that order, rounded to bf16.  Block: 16 tokens x 256 columns; thread: 16 columns
+// of one token.
+__global__ __launch_bounds__(256) void dx_combine_kernel(
+    int T, int d, int E, int k, const float* __restrict__ dl, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ dx_perm, const int32_t* __restrict__ slot_pos,
+    const uint16_t* __restrict__ dx_shared, const uint16_t* __restrict__ residual,
+    uint16_t* __restrict__ dx) {
+  __shared__ float s_dl[16][64];
+  __shared__ __align__(16) uint16_t s_wr[64][256];
+  const int t0 = blockIdx.x * 16, c0 = blockIdx.y * 256;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 16 * 64; i += 256) {
+    const int tl = i / 64, e = i % 64;
+    s_dl[tl][e] = (t0 + tl < T && e < E) ? dl[(size_t)(t0 + tl) * E + e] : 0.0f;
+  }
+  for (int i = tid; i < 64 * 32; i += 256) {
+    const int e = i / 32, c = (i % 32) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (e < E && c0 + c < d) v = *reinterpret_cast<const uint4*>(wr + (size_t)e * d + c0 + c);
+    *reinterpret_cast<uint4*>(&s_wr[e][c]) = v;
+  }
+  __syncthreads();
+  const int tl = tid / 16, cl = (tid % 16) * 16;
+  const int t = t0 + tl, c = c0 + cl;
+  if (t >= T || c >= d) return;
+  float acc[16] = {};
+  for (int e = 0; e < E; ++e) {
+    const float g = s_dl[tl][e];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = fmaf(g, bf16_bits_to_f32(s_wr[e][cl + i]), acc[i]);
+  }
+  auto add16 = [&](const uint16_t* src) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src), b = *reinterpret_cast<const uint4*>(src + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[2 * i] += bf16_bits_to_f32(w[i] & 0xffffu);
+      acc[2 * i + 1] += bf16_bits_to_f32(w[i] >> 16);
+    }
+  };
+  for (int j = 0; j < k; ++j) {
+    const int p = slot_pos[(size_t)t * k + j];
+    if (p >= 0) add16(dx_perm + (size_t)p * d + c);
+  }
+  if (dx_shared != nullptr) add16(dx_shared + (size_t)t * d + c);
+  if (residual != nullptr) add16(residual + (size_t)t * d + c);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  uint4* dst = reinterpret_cast<uint4*>(dx + (size_t)t * d + c);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// ------------------------------------------------------------------------------------
+// Weight-gradient GEMM with the contraction over each segment's tokens:
+//   out(seg, m, n) = sum_{k < Kp_seg} A_seg[m][k] B_seg[n][k]    (fp32 accumulation and output)
+// A_seg = A + M * koff[seg] ([M][Kp_seg]), B_seg = B + N * koff[seg] ([N][Kp_seg]), both
+// K-major copies with zero padding; out(seg, m, n) is stored at
+//   out + seg * M * N + (n / nsplit) * M * nsplit + m * nsplit + n % nsplit
+// (nsplit = N: the plain [M][N] layout; a smaller nsplit stores column blocks of nsplit
+// columns as consecutive [M][nsplit] matrices).
+// One workgroup per 128 x 128 output tile, 4 waves of 64 x 64 (MFMA 32x32x16, A as first
+// operand so that a lane holds 16 rows of one output column), K in slices of 64 through a
+// two-stage LDS ring filled by global_load_lds_dwordx4 (16-byte chunks XOR-swizzled per row).
+constexpr int kWgBM = 128, kWgBN = 128, kWgBK = 64, kWgWaves = 4;
+
+__device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
+
+__device__ __forceinline__ int swz8w(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+__global__ __launch_bounds__(kWgWaves * 64) void wgrad_kernel(WgradParams p) {
+  constexpr int ROWB = kWgBK * 2;                      // bytes per LDS row
+  constexpr int A_BYTES = kWgBM * ROWB, ST_BYTES = A_BYTES + kWgBN * ROWB;
+  constexpr int NDMA = ST_BYTES / 1024 / kWgWaves;     // 8 per wave per slice
+  __shared__ __align__(1024) unsigned char lds[2 * ST_BYTES];
+  const int tiles_m = (p.M + kWgBM - 1) / kWgBM, tiles_n = (p.N + kWgBN - 1) / kWgBN;
+  const int seg = blockIdx.x / (tiles_m * tiles_n);
+  const int rem = blockIdx.x % (tiles_m * tiles_n);
+  const int m0 = (rem / tiles_n) * kWgBM, n0 = (rem % tiles_n) * kWgBN;
+  const int kp = p.koff[seg + 1] - p.koff[seg];
+  const int nk = kp / kWgBK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 2, wn = wave % 2;
+  const uint16_t* A = p.a + (size_t)p.M * p.koff[seg];
+  const uint16_t* B = p.b + (size_t)p.N * p.koff[seg];
+  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
+
+  // this lane's DMA sources: DMA q covers 8 LDS rows of 128 bytes (A rows, then B rows)
+  const uint16_t* src[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int q = wave * NDMA + i;
+    const int row = q * 8 + lane / 8;                 // 0 .. 255
+    const int chunk = (lane % 8) ^ swz8w(row & 127);
+    if (row < kWgBM) {
+      const int m = min(m0 + row, p.M - 1);
+      src[i] = A + (size_t)m * kp + chunk * 8;
+    } else {
+      const int n = min(n0 + row - kWgBM, p.N - 1);
+      src[i] = B + (size_t)n * kp + chunk * 8;
+    }
+  }
+  auto issue = [&](int kt) {
+    const uint32_t st = lds_base + (uint32_t)((kt & 1) * ST_BYTES);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      dma16_wg(st + (uint32_t)((wave * NDMA + i) * 1024), src[i] + (size_t)kt * kWgBK);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) {
+      issue(kt + 1);
+      __builtin_amdgcn_s_waitcnt((NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    }
+    __syncthreads();
+    const unsigned char* As = lds + (kt & 1) * ST_BYTES;
+    const unsigned char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < kWgBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int ra = wm * 64 + f * 32 + (lane & 31);
+        af[f] = *reinterpret_cast<const bf16x8*>(As + ra * ROWB + ((c ^ swz8w(ra)) << 4));
+        const int rb = wn * 64 + f * 32 + (lane & 31);
+        bf[f] = *reinterpret_cast<const bf16x8*>(Bs + rb * ROWB + ((c ^ swz8w(rb)) << 4));
+      }
+#pragma unroll
+      for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+          acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fa], bf[fb], acc[fa][fb], 0, 0, 0);
+    }
+    __syncthreads();   // the next issue overwrites the stage just read
+  }
+  // element i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4 of A's block, column l % 32 of B's
+  float* out = p.out + (size_t)seg * p.M * p.N;
+#pragma unroll
+  for (int fa = 0; fa < 2; ++fa)
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) {
+      const int n = n0 + wn * 64 + fb * 32 + (lane & 31);
+      if (n >= p.N) continue;
+      float* col = out + (size_t)(n / p.nsplit) * p.M * p.nsplit + (n % p.nsplit);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * 64 + fa * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+        if (m < p.M) col[(size_t)m * p.nsplit] = acc[fa][fb][i];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_mat(const void* in, void* out, int batch, int R, int C, long long obs,
+                                int ld, hipStream_t s) {
+  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  dim3 grid((unsigned)((R / kT) * (C / kT)), (unsigned)batch);
+  hipLaunchKernelGGL(transpose_mat_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C, obs, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_koff(const int32_t* offsets, int nseg, int rows, int32_t* koff, hipStream_t s) {
+  hipLaunchKernelGGL(seg_koff_kernel, dim3(1), dim3(64), 0, s, offsets, nseg, rows, koff);
+  return hipGetLastError();
+}
+
+// sum over segments of (n_e rounded up to 64) <= rows + 63 nseg <= this bound (a multiple of 64)
+size_t padded_k_bound(int rows, int nseg) { return (((size_t)rows + 63) & ~(size_t)63) + 64 * (size_t)nseg; }
+
+hipError_t launch_transpose_rows(const void* in, int ld_in, int col_in, const int32_t* row_index,
+                                 const float* row_scale, const int32_t* offsets, int nseg, int rows,
+                                 const int32_t* koff, int C, void* out, hipStream_t s) {
+  const size_t kblocks = padded_k_bound(rows, nseg) / kT;
+  const size_t blocks = kblocks * (size_t)(C / kT);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(in), ld_in, col_in, row_index, row_scale, offsets,
+                     nseg, rows, koff, C, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_routing_weight_grad(int T, int k, int d, const void* dout, const void* y,
+                                      const int32_t* slot_pos, const float* topk_w, float* dw,
+                                      hipStream_t s) {
+  const int Tk = T * k;
+  if (Tk == 0) return hipSuccess;
+  hipLaunchKernelGGL(routing_weight_grad_kernel, dim3((Tk + 3) / 4), dim3(256), 0, s, Tk, k, d,
+                     static_cast<const uint16_t*>(dout), static_cast<const uint16_t*>(y), slot_pos,
+                     topk_w, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_grad(const RouteParams& p, const float* scores, const int32_t* idx,
+                              const float* dw, float* dl, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_grad_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p, scores, idx, dw, dl);
+  return hipGetLastError();
+}
+
+size_t router_wgrad_ws_bytes(int T, int d, int E) {
+  const size_t chunks = ((size_t)T + kRgChunk - 1) / kRgChunk;
+  return chunks * (size_t)E * ((size_t)d + 1) * sizeof(float);
+}
+
+hipError_t launch_router_wgrad(int T, int d, int E, const void* x, const float* dl, float* d_router,
+                               float* d_bias, void* ws, hipStream_t s) {
+  const int chunks = (T + kRgChunk - 1) / kRgChunk;
+  if (chunks == 0) return hipSuccess;
+  float* part = static_cast<float*>(ws);
+  float* part_bias = part + (size_t)chunks * E * d;
+  hipLaunchKernelGGL(router_wgrad_partial_kernel, dim3((unsigned)(d / 64), (unsigned)chunks), dim3(256),
+                     0, s, T, d, E, static_cast<const uint16_t*>(x), dl, part, part_bias);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d_router != nullptr) {
+    const int n = E * d;
+    hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, chunks, n,
+                       part, d_router);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (d_bias != nullptr) {
+    hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3((E + 255) / 256), dim3(256), 0, s, chunks, E,
+                       part_bias, d_bias);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_dx_combine(int T, int d, int E, int k, const float* dl, const void* wr,
+                             const void* dx_perm, const int32_t* slot_pos, const void* dx_shared,
+                             const void* residual, void* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)((T + 15) / 16), (unsigned)((d + 255) / 256));
+  hipLaunchKernelGGL(dx_combine_kernel, grid, dim3(256), 0, s, T, d, E, k, dl,
+                     static_cast<const uint16_t*>(wr), static_cast<const uint16_t*>(dx_perm),
+                     slot_pos, static_cast<const uint16_t*>(dx_shared),
+                     static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const WgradParams& p, int nseg, hipStream_t s) {
+  const long long tiles = (long long)nseg * ((p.M + kWgBM - 1) / kWgBM) * ((p.N + kWgBN - 1) / kWgBN);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(kWgWaves * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

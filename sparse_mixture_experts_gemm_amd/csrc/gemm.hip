@@ -178,7 +178,7 @@ __device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false>
+          bool A8 = false, bool BWD = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   constexpr int BK = 64;
@@ -189,6 +189,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   // 64-byte LDS rows; every lane reads 32 bytes of a row as two 16-byte chunks, swizzled
   // by (row >> 2) & 3 so that 16 consecutive rows hit distinct 16-byte bank groups
   static_assert(!A8 || (FP8 && STAGE == 0), "e4m3 activations: up projection, e4m3 weights");
+  // BWD: the UP stage recomputed in the backward pass; the epilogue turns dh into the
+  // gradients of the two pre-activations instead of applying the activation
+  static_assert(!BWD || (STAGE == 0 && !FP8 && !A8), "backward epilogue: bf16 up projection");
   constexpr int ESZ_A = A8 ? 1 : 2;                 // bytes per A element
   constexpr int AROW = BK * ESZ_A;                  // bytes per A row in LDS
   constexpr int CPR_A = AROW / 16;                  // 16-byte chunks per A row
@@ -510,6 +513,37 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
           const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
                                   : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
           if (hcol >= N) continue;
+          if (BWD) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+              const int r = m0 + wm * WTM + fm * 32 + col_in;
+              if (r >= tc.rows) continue;
+              const size_t row = (size_t)(tc.row0 + r);
+              // dh of these 16 features (bf16)
+              const uint4* dsrc = reinterpret_cast<const uint4*>(
+                  static_cast<const uint16_t*>(p.dact) + row * N + hcol);
+              const uint4 d0 = dsrc[0], d1 = dsrc[1];
+              const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+              float da[16], db[16];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const float dh = bf16_bits_to_f32((i & 1) ? (dw[i >> 1] >> 16) : (dw[i >> 1] & 0xffffu));
+                const float a = acc[fm][fh][i];
+                if (SWIGLU) {
+                  const float b = acc[fm][fh + FN / 2][i];
+                  const float sig = 1.0f / (1.0f + __expf(-a));
+                  da[i] = dh * b * (sig * (1.0f + a * (1.0f - sig)));   // silu'(a)
+                  db[i] = dh * (a * sig);                                // silu(a)
+                } else {
+                  da[i] = dh * 2.0f * fmaxf(a, 0.f);
+                }
+              }
+              uint16_t* o = static_cast<uint16_t*>(p.out) + row * (SWIGLU ? 2 * N : N);
+              store16_bf16(o + hcol, da);
+              if (SWIGLU) store16_bf16(o + N + hcol, db);
+            }
+            continue;
+          }
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
             const int r = m0 + wm * WTM + fm * 32 + col_in;
@@ -717,9 +751,9 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false>
+          bool A8 = false, bool BWD = false>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -745,6 +779,15 @@ hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
   else return launch_cfg<MOE_CFG_NARROW_DOWN, STAGE, ACT, FP8>(p, num_cus, s);
 }
 
+template <int ACT>
+hipError_t launch_bwd(const GemmParams& p, int num_cus, hipStream_t s) {
+  const long long bcols = ACT == MOE_ACT_SWIGLU ? 2LL * p.N : p.N;
+  const long long wide_tiles = ((p.rows + 255) / 256) * ((bcols + 255) / 256);
+  if (wide_tiles >= 2LL * num_cus)
+    return launch_cfg<MOE_CFG_WIDE, 0, ACT, false, false, true>(p, num_cus, s);
+  return launch_cfg<MOE_CFG_NARROW_UP, 0, ACT, false, false, true>(p, num_cus, s);
+}
+
 template <int STAGE, int ACT>
 hipError_t launch_f32(const GemmParams& p, int num_cus, hipStream_t s) {
   const int grid = num_cus * 4;
@@ -753,6 +796,12 @@ hipError_t launch_f32(const GemmParams& p, int num_cus, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_up_backward(const GemmParams& p, int act, int num_cus, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  return act == MOE_ACT_RELU2 ? launch_bwd<MOE_ACT_RELU2>(p, num_cus, s)
+                              : launch_bwd<MOE_ACT_SWIGLU>(p, num_cus, s);
+}
 
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
                                int weight_dtype, int num_cus, hipStream_t s, bool fp8_act) {

@@ -42,7 +42,8 @@ struct GemmParams {
   const float* s_up;
   const float* s_down;
   const float* row_weight;  // DOWN: per-row multiplier or null
-  void* out;                // [rows][N]
+  void* out;                // [rows][N]  (UP backward: [rows][2N] SwiGLU, [rows][N] ReLU^2)
+  const void* dact;         // UP backward: gradient of the activation output h, [rows][N]
 };
 
 enum class Stage { Up = 0, Down = 1 };
@@ -75,6 +76,11 @@ hipError_t launch_quant_rows(int rows, int cols, const void* a, uint8_t* q, floa
 // e4m3 weights.
 hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int act_dtype,
                                int weight_dtype, int num_cus, hipStream_t s, bool fp8_act = false);
+
+// UP stage recomputed for the backward pass (bf16 weights and activations): the epilogue
+// reads dh = p.dact [rows][N] and writes the gradients of the two pre-activations a = A W1^T
+// and b = A W3^T: SwiGLU out[r] = [da (N) | db (N)], ReLU^2 out[r] = da.
+hipError_t launch_up_backward(const GemmParams& p, int act, int num_cus, hipStream_t s);
 
 // Weight-streaming variant of the grouped GEMM for few rows per segment.  `second`, when
 // given, is a second segment set (e.g. the shared experts) run in the same launch.

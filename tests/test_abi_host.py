@@ -121,6 +121,33 @@ def test_prenorm_config_and_route_arguments_are_checked_on_the_host(lib):
     assert lib.moe_forward(ctypes.byref(c), ctypes.byref(w.c), fake, fake, fake, need, None) == 1
 
 
+def test_backward_arguments_are_checked_on_the_host(lib):
+    c = cfg(T=64)
+    n = moe.backward_workspace_size(c)
+    assert n > moe.workspace_size(c)
+    fake = 4096
+    w = moe.Weights(router=fake, w_gate=fake, w_up=fake, w_down=fake, sh_gate=fake, sh_up=fake,
+                    sh_down=fake)
+    fwd = moe.workspace_size(c)
+    g = moe._GradsC(dx=fake)
+    call = lambda cc, ww, gg, fb=fwd, nb=n, x=fake: lib.moe_backward(
+        ctypes.byref(cc), ctypes.byref(ww.c), x, fake, fake, fb, ctypes.byref(gg), fake, nb, None)
+    assert call(c, w, moe._GradsC()) == 1                  # dx is required
+    assert call(c, w, g, x=None) == 1
+    assert call(c, w, g, fb=fwd - 1) == 3                   # forward workspace too small
+    assert call(c, w, g, nb=n - 1) == 3                     # backward workspace too small
+    assert call(c, w, g, x=fake + 2) == 2                   # misaligned
+    for bad, status in [(dict(weight_dtype="e4m3"), 2), (dict(act_dtype="f32", weight_dtype="f32"), 2),
+                        (dict(pre_norm=True), 2), (dict(route_scale=0.0), 1)]:
+        cb = cfg(T=64, **bad)
+        nn = ctypes.c_size_t(0)
+        assert lib.moe_backward_workspace_size(ctypes.byref(cb), ctypes.byref(nn)) == status
+        assert call(cb, w, g) == status
+    c0 = cfg(T=0)
+    assert lib.moe_backward(ctypes.byref(c0), ctypes.byref(w.c), None, None, None, 0,
+                            ctypes.byref(g), None, 0, None) == 0
+
+
 def test_null_and_workspace_errors_are_reported_before_launch(lib):
     c = cfg(T=64)
     fake = 4096
