@@ -791,7 +791,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
         moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_r,
                            M, N, nsplit, out};
-        if (ok()) e = moe::launch_wgrad(p, E, stream);
+        if (ok()) e = moe::launch_wgrad(p, E, cus, stream);
       };
       if (grads->d_w_down != nullptr) {
         tr(dout, d, 0, perm_token, perm_weight, d, bc.dyt_r);
@@ -818,7 +818,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
         moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_s,
                            M, N, nsplit, out};
-        if (ok()) e = moe::launch_wgrad(p, 1, stream);
+        if (ok()) e = moe::launch_wgrad(p, 1, cus, stream);
       };
       if (grads->d_sh_down != nullptr) {
         tr(dout, d, 0, d, bc.doutt_s);

@@ -55,6 +55,6 @@ hipError_t launch_dx_combine(int T, int d, int E, int k, const float* dl, const 
                              const void* dx_perm, const int32_t* slot_pos, const void* dx_shared,
                              const void* residual, void* dx, hipStream_t s);
 
-hipError_t launch_wgrad(const WgradParams& p, int nseg, hipStream_t s);
+hipError_t launch_wgrad(const WgradParams& p, int nseg, int num_cus, hipStream_t s);
 
 }  // namespace moe

@@ -197,23 +197,42 @@ constexpr int kRgChunk = 256;
 __global__ __launch_bounds__(256) void router_wgrad_partial_kernel(
     int T, int d, int E, const uint16_t* __restrict__ x, const float* __restrict__ dl,
     float* __restrict__ part, float* __restrict__ part_bias) {
+  // the chunk is walked in sub-chunks of 64 tokens staged in LDS (dl rows padded to 64
+  // experts with zeros, x as 64 columns)
+  __shared__ __align__(16) float s_dl[64][64];
+  __shared__ __align__(16) uint16_t s_x[64][64];
   const int c0 = blockIdx.x * 64, chunk = blockIdx.y;
-  const int eg = threadIdx.x / 16, cg = threadIdx.x % 16;
+  const int tid = threadIdx.x;
+  const int eg = tid / 16, cg = tid % 16;
   const int t0 = chunk * kRgChunk, t1 = min(T, t0 + kRgChunk);
   float acc[4][4] = {};
   float accb[4] = {};
-  for (int t = t0; t < t1; ++t) {
-    const uint2 xv = *reinterpret_cast<const uint2*>(x + (size_t)t * d + c0 + cg * 4);
-    const float xf[4] = {bf16_bits_to_f32(xv.x & 0xffffu), bf16_bits_to_f32(xv.x >> 16),
-                         bf16_bits_to_f32(xv.y & 0xffffu), bf16_bits_to_f32(xv.y >> 16)};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = eg * 4 + i;
-      const float g = e < E ? dl[(size_t)t * E + e] : 0.0f;
-      accb[i] += g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(g, xf[j], acc[i][j]);
+  for (int ts = t0; ts < t1; ts += 64) {
+    for (int i = tid; i < 64 * 64; i += 256) {
+      const int tl = i / 64, e = i % 64;
+      s_dl[tl][e] = (ts + tl < t1 && e < E) ? dl[(size_t)(ts + tl) * E + e] : 0.0f;
     }
+    for (int i = tid; i < 64 * 8; i += 256) {
+      const int tl = i / 8, c = (i % 8) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ts + tl < t1) v = *reinterpret_cast<const uint4*>(x + (size_t)(ts + tl) * d + c0 + c);
+      *reinterpret_cast<uint4*>(&s_x[tl][c]) = v;
+    }
+    __syncthreads();
+    for (int tl = 0; tl < 64; ++tl) {
+      const float4 g4 = *reinterpret_cast<const float4*>(&s_dl[tl][eg * 4]);
+      const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[tl][cg * 4]);
+      const float g[4] = {g4.x, g4.y, g4.z, g4.w};
+      const float xf[4] = {bf16_bits_to_f32(xv.x & 0xffffu), bf16_bits_to_f32(xv.x >> 16),
+                           bf16_bits_to_f32(xv.y & 0xffffu), bf16_bits_to_f32(xv.y >> 16)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accb[i] += g[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(g[i], xf[j], acc[i][j]);
+      }
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -297,11 +316,11 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(
 //   out + seg * M * N + (n / nsplit) * M * nsplit + m * nsplit + n % nsplit
 // (nsplit = N: the plain [M][N] layout; a smaller nsplit stores column blocks of nsplit
 // columns as consecutive [M][nsplit] matrices).
-// One workgroup per 128 x 128 output tile, 4 waves of 64 x 64 (MFMA 32x32x16, A as first
-// operand so that a lane holds 16 rows of one output column), K in slices of 64 through a
-// two-stage LDS ring filled by global_load_lds_dwordx4 (16-byte chunks XOR-swizzled per row).
-constexpr int kWgBM = 128, kWgBN = 128, kWgBK = 64, kWgWaves = 4;
-
+// One workgroup per BM x BN output tile (256 x 256 with 8 waves of 128 x 64, or 128 x 128
+// with 4 waves of 64 x 64; MFMA 32x32x16), K in slices of 64 through a two-stage LDS ring
+// filled by global_load_lds_dwordx4 (16-byte chunks XOR-swizzled per row), one barrier per
+// slice.  A is the MFMA's first operand: a lane holds 16 rows of one output column, and each
+// fp32 store instruction writes two full 128-byte row segments.
 __device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
   uint32_t save;
   asm volatile(
@@ -316,20 +335,25 @@ __device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
 
 __device__ __forceinline__ int swz8w(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__global__ __launch_bounds__(kWgWaves * 64) void wgrad_kernel(WgradParams p) {
+constexpr int kWgBK = 64;
+
+template <int BM, int BN, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void wgrad_kernel(WgradParams p) {
   constexpr int ROWB = kWgBK * 2;                      // bytes per LDS row
-  constexpr int A_BYTES = kWgBM * ROWB, ST_BYTES = A_BYTES + kWgBN * ROWB;
-  constexpr int NDMA = ST_BYTES / 1024 / kWgWaves;     // 8 per wave per slice
+  constexpr int WN = WAVES / 2, WTM = BM / 2, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  constexpr int A_BYTES = BM * ROWB, ST_BYTES = A_BYTES + BN * ROWB;
+  constexpr int NDMA = ST_BYTES / 1024 / WAVES;        // 1 KB DMAs per wave per slice
+  static_assert(ST_BYTES % (1024 * WAVES) == 0, "DMA split");
   __shared__ __align__(1024) unsigned char lds[2 * ST_BYTES];
-  const int tiles_m = (p.M + kWgBM - 1) / kWgBM, tiles_n = (p.N + kWgBN - 1) / kWgBN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int seg = blockIdx.x / (tiles_m * tiles_n);
   const int rem = blockIdx.x % (tiles_m * tiles_n);
-  const int m0 = (rem / tiles_n) * kWgBM, n0 = (rem % tiles_n) * kWgBN;
+  const int m0 = (rem / tiles_n) * BM, n0 = (rem % tiles_n) * BN;
   const int kp = p.koff[seg + 1] - p.koff[seg];
   const int nk = kp / kWgBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / WN, wn = wave % WN;
   const uint16_t* A = p.a + (size_t)p.M * p.koff[seg];
   const uint16_t* B = p.b + (size_t)p.N * p.koff[seg];
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
@@ -339,14 +363,13 @@ __global__ __launch_bounds__(kWgWaves * 64) void wgrad_kernel(WgradParams p) {
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int q = wave * NDMA + i;
-    const int row = q * 8 + lane / 8;                 // 0 .. 255
-    const int chunk = (lane % 8) ^ swz8w(row & 127);
-    if (row < kWgBM) {
+    const int row = q * 8 + lane / 8;
+    if (row < BM) {
       const int m = min(m0 + row, p.M - 1);
-      src[i] = A + (size_t)m * kp + chunk * 8;
+      src[i] = A + (size_t)m * kp + ((lane % 8) ^ swz8w(row)) * 8;
     } else {
-      const int n = min(n0 + row - kWgBM, p.N - 1);
-      src[i] = B + (size_t)n * kp + chunk * 8;
+      const int n = min(n0 + row - BM, p.N - 1);
+      src[i] = B + (size_t)n * kp + ((lane % 8) ^ swz8w(row - BM)) * 8;
     }
   }
   auto issue = [&](int kt) {
@@ -356,53 +379,57 @@ __global__ __launch_bounds__(kWgWaves * 64) void wgrad_kernel(WgradParams p) {
       dma16_wg(st + (uint32_t)((wave * NDMA + i) * 1024), src[i] + (size_t)kt * kWgBK);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-  if (nk > 0) issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) {
-      issue(kt + 1);
-      __builtin_amdgcn_s_waitcnt((NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14));
-    } else {
-      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
-    }
+    for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
+  if (nk > 0) {
+    issue(0);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt + 1 goes to the stage read in slice kt - 1 (all waves passed the barrier
+    // that ended it) and lands while slice kt is multiplied
+    if (kt + 1 < nk) issue(kt + 1);
     const unsigned char* As = lds + (kt & 1) * ST_BYTES;
     const unsigned char* Bs = As + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < kWgBK / 16; ++ks) {
       const int c = ks * 2 + (lane >> 5);
-      bf16x8 af[2], bf[2];
+      bf16x8 af[FM], bf[FN];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int ra = wm * 64 + f * 32 + (lane & 31);
+      for (int f = 0; f < FM; ++f) {
+        const int ra = wm * WTM + f * 32 + (lane & 31);
         af[f] = *reinterpret_cast<const bf16x8*>(As + ra * ROWB + ((c ^ swz8w(ra)) << 4));
-        const int rb = wn * 64 + f * 32 + (lane & 31);
+      }
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int rb = wn * WTN + f * 32 + (lane & 31);
         bf[f] = *reinterpret_cast<const bf16x8*>(Bs + rb * ROWB + ((c ^ swz8w(rb)) << 4));
       }
 #pragma unroll
-      for (int fa = 0; fa < 2; ++fa)
+      for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
+        for (int fb = 0; fb < FN; ++fb)
           acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fa], bf[fb], acc[fa][fb], 0, 0, 0);
     }
-    __syncthreads();   // the next issue overwrites the stage just read
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // slice kt + 1 landed (own DMAs)
+    __syncthreads();                                        // ... everyone's; stage kt free
   }
   // element i of lane l: row 8 (i / 4) + 4 (l / 32) + i % 4 of A's block, column l % 32 of B's
   float* out = p.out + (size_t)seg * p.M * p.N;
 #pragma unroll
-  for (int fa = 0; fa < 2; ++fa)
+  for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb) {
-      const int n = n0 + wn * 64 + fb * 32 + (lane & 31);
+    for (int fb = 0; fb < FN; ++fb) {
+      const int n = n0 + wn * WTN + fb * 32 + (lane & 31);
       if (n >= p.N) continue;
       float* col = out + (size_t)(n / p.nsplit) * p.M * p.nsplit + (n % p.nsplit);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * 64 + fa * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+        const int m = m0 + wm * WTM + fa * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
         if (m < p.M) col[(size_t)m * p.nsplit] = acc[fa][fb][i];
       }
     }
@@ -499,10 +526,17 @@ hipError_t launch_dx_combine(int T, int d, int E, int k, const float* dl, const 
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad(const WgradParams& p, int nseg, hipStream_t s) {
-  const long long tiles = (long long)nseg * ((p.M + kWgBM - 1) / kWgBM) * ((p.N + kWgBN - 1) / kWgBN);
-  if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(kWgWaves * 64), 0, s, p);
+hipError_t launch_wgrad(const WgradParams& p, int nseg, int num_cus, hipStream_t s) {
+  auto tiles = [&](int bm, int bn) {
+    return (long long)nseg * ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+  };
+  // 256 x 256 tiles when every CU still gets two, else 128 x 128
+  const long long wide = tiles(256, 256);
+  if (wide == 0) return hipSuccess;
+  if (wide >= 2LL * num_cus)
+    hipLaunchKernelGGL((wgrad_kernel<256, 256, 8>), dim3((unsigned)wide), dim3(8 * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<128, 128, 4>), dim3((unsigned)tiles(128, 128)), dim3(4 * 64), 0, s, p);
   return hipGetLastError();
 }
 
