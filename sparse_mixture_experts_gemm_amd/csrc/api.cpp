@@ -181,10 +181,9 @@ Carve carve(const moe_config* c) {
 // Workspace of moe_backward, in carve order.
 struct BwdCarve {
   size_t w2t, w13t, sh_w2t, sh_w13t;           // transposed weight copies (bf16)
-  size_t scores, idx, tw, dw, dl, koff_r, koff_s;
+  size_t scores, idx, tw, dw, dl;
   size_t dh_r, dh_s, dab_r, dab_s, dxp_r, dx_s;  // data-gradient intermediates (bf16)
-  size_t xt_r, dyt_r, ht_r, dat_r, dbt_r;        // K-major token copies, routed
-  size_t doutt_s, xt_s, ht_s, dat_s, dbt_s;      // and shared
+  size_t x_perm, dy_perm;                        // routed rows in permuted order (bf16)
   size_t rg, total;
 };
 
@@ -192,7 +191,6 @@ BwdCarve bwd_carve(const moe_config* c) {
   const size_t T = (size_t)c->num_tokens, k = (size_t)c->top_k, E = (size_t)c->num_experts;
   const size_t d = (size_t)c->dim, I = (size_t)c->inter_dim, S = (size_t)c->num_shared;
   const size_t nab = c->act == MOE_ACT_SWIGLU ? 2 : 1;   // pre-activations per inter feature
-  const size_t kr = moe::padded_k_bound((int)(T * k), (int)E), ks = moe::padded_k_bound((int)T, 1);
   BwdCarve b{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align_up(bytes); return at; };
@@ -205,24 +203,14 @@ BwdCarve bwd_carve(const moe_config* c) {
   b.tw = take(T * k * 4);
   b.dw = take(T * k * 4);
   b.dl = take(T * E * 4);
-  b.koff_r = take((E + 1) * 4);
-  b.koff_s = take(2 * 4);
   b.dh_r = take(T * k * I * 2);
   b.dh_s = take(T * S * I * 2);
   b.dab_r = take(T * k * nab * I * 2);
   b.dab_s = take(T * nab * S * I * 2);
   b.dxp_r = take(T * k * d * 2);
   b.dx_s = take(S > 0 ? T * d * 2 : 0);
-  b.xt_r = take(d * kr * 2);
-  b.dyt_r = take(d * kr * 2);
-  b.ht_r = take(I * kr * 2);
-  b.dat_r = take(I * kr * 2);
-  b.dbt_r = take(nab == 2 ? I * kr * 2 : 0);
-  b.doutt_s = take(S > 0 ? d * ks * 2 : 0);
-  b.xt_s = take(S > 0 ? d * ks * 2 : 0);
-  b.ht_s = take(S * I * ks * 2);
-  b.dat_s = take(S * I * ks * 2);
-  b.dbt_s = take(nab == 2 ? S * I * ks * 2 : 0);
+  b.x_perm = take(T * k * d * 2);
+  b.dy_perm = take(T * k * d * 2);
   b.rg = take(moe::router_wgrad_ws_bytes((int)T, (int)d, (int)E));
   b.total = o;
   return b;
@@ -714,8 +702,6 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     uint16_t* sh_w13t = static_cast<uint16_t*>(at(bc.sh_w13t));
     float* dw = static_cast<float*>(at(bc.dw));
     float* dl = static_cast<float*>(at(bc.dl));
-    int32_t* koff_r = static_cast<int32_t*>(at(bc.koff_r));
-    int32_t* koff_s = static_cast<int32_t*>(at(bc.koff_s));
     const moe_weights wt_fwd = *w;
 
     hipError_t e = hipSuccess;
@@ -782,60 +768,34 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       e = moe::launch_dx_combine(T, d, E, k, dl, w->router, at(bc.dxp_r), slot_pos,
                                  shared ? at(bc.dx_s) : nullptr, cfg->residual ? dout : nullptr,
                                  grads->dx, stream);
-    // 7. weight gradients: contractions over each expert's tokens, on K-major copies
-    if (grads->d_w_gate != nullptr || grads->d_w_up != nullptr || grads->d_w_down != nullptr) {
-      if (ok()) e = moe::launch_seg_koff(offsets, E, Tk, koff_r, stream);
-      auto tr = [&](const void* src, int ld, int col, const int32_t* ri, const float* sc, int C, size_t dst) {
-        if (ok()) e = moe::launch_transpose_rows(src, ld, col, ri, sc, offsets, E, Tk, koff_r, C, at(dst), stream);
-      };
-      auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
-        moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_r,
-                           M, N, nsplit, out};
-        if (ok()) e = moe::launch_wgrad(p, E, cus, stream);
-      };
-      if (grads->d_w_down != nullptr) {
-        tr(dout, d, 0, perm_token, perm_weight, d, bc.dyt_r);
-        tr(h_r, I, 0, nullptr, nullptr, I, bc.ht_r);
-        wg(bc.dyt_r, bc.ht_r, d, I, I, grads->d_w_down);
-      }
-      if (grads->d_w_gate != nullptr || (swiglu && grads->d_w_up != nullptr)) {
-        tr(x, d, 0, perm_token, nullptr, d, bc.xt_r);
-        if (grads->d_w_gate != nullptr) {
-          tr(at(bc.dab_r), nab * I, 0, nullptr, nullptr, I, bc.dat_r);
-          wg(bc.dat_r, bc.xt_r, I, d, d, grads->d_w_gate);
-        }
-        if (swiglu && grads->d_w_up != nullptr) {
-          tr(at(bc.dab_r), 2 * I, I, nullptr, nullptr, I, bc.dbt_r);
-          wg(bc.dbt_r, bc.xt_r, I, d, d, grads->d_w_up);
-        }
-      }
+    // 7. weight gradients: contractions over each expert's rows, read token-major; the
+    //    routed x rows and the weighted dout rows are first copied into permuted order
+    auto wg = [&](const void* a, int lda, int a_col, const void* b, int ldb, int b_col,
+                  const int32_t* offs, int nseg, int rows, int M, int N, int nsplit, float* out) {
+      moe::WgradParams wp{static_cast<const uint16_t*>(a), lda, a_col, static_cast<const uint16_t*>(b),
+                          ldb, b_col, offs, rows, M, N, nsplit, out};
+      if (ok()) e = moe::launch_wgrad(wp, nseg, cus, stream);
+    };
+    if (grads->d_w_down != nullptr) {
+      if (ok()) e = moe::launch_gather_rows(dout, perm_token, perm_weight, offsets + E, Tk, d,
+                                             at(bc.dy_perm), stream);
+      wg(at(bc.dy_perm), d, 0, h_r, I, 0, offsets, E, Tk, d, I, I, grads->d_w_down);
     }
-    if (shared && (grads->d_sh_gate != nullptr || grads->d_sh_up != nullptr || grads->d_sh_down != nullptr)) {
-      if (ok()) e = moe::launch_seg_koff(nullptr, 1, T, koff_s, stream);
-      auto tr = [&](const void* src, int ld, int col, int C, size_t dst) {
-        if (ok()) e = moe::launch_transpose_rows(src, ld, col, nullptr, nullptr, nullptr, 1, T, koff_s, C, at(dst), stream);
-      };
-      auto wg = [&](size_t a, size_t b, int M, int N, int nsplit, float* out) {
-        moe::WgradParams p{static_cast<const uint16_t*>(at(a)), static_cast<const uint16_t*>(at(b)), koff_s,
-                           M, N, nsplit, out};
-        if (ok()) e = moe::launch_wgrad(p, 1, cus, stream);
-      };
-      if (grads->d_sh_down != nullptr) {
-        tr(dout, d, 0, d, bc.doutt_s);
-        tr(h_s, SI, 0, SI, bc.ht_s);
-        wg(bc.doutt_s, bc.ht_s, d, SI, I, grads->d_sh_down);
-      }
-      if (grads->d_sh_gate != nullptr || (swiglu && grads->d_sh_up != nullptr)) {
-        tr(x, d, 0, d, bc.xt_s);
-        if (grads->d_sh_gate != nullptr) {
-          tr(at(bc.dab_s), nab * SI, 0, SI, bc.dat_s);
-          wg(bc.dat_s, bc.xt_s, SI, d, d, grads->d_sh_gate);
-        }
-        if (swiglu && grads->d_sh_up != nullptr) {
-          tr(at(bc.dab_s), 2 * SI, SI, SI, bc.dbt_s);
-          wg(bc.dbt_s, bc.xt_s, SI, d, d, grads->d_sh_up);
-        }
-      }
+    if (grads->d_w_gate != nullptr || (swiglu && grads->d_w_up != nullptr)) {
+      if (ok()) e = moe::launch_gather_rows(x, perm_token, nullptr, offsets + E, Tk, d, at(bc.x_perm),
+                                             stream);
+      if (grads->d_w_gate != nullptr)
+        wg(at(bc.dab_r), nab * I, 0, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_gate);
+      if (swiglu && grads->d_w_up != nullptr)
+        wg(at(bc.dab_r), 2 * I, I, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_up);
+    }
+    if (shared) {
+      if (grads->d_sh_down != nullptr)
+        wg(dout, d, 0, h_s, SI, 0, nullptr, 1, T, d, SI, I, grads->d_sh_down);
+      if (grads->d_sh_gate != nullptr)
+        wg(at(bc.dab_s), nab * SI, 0, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_gate);
+      if (swiglu && grads->d_sh_up != nullptr)
+        wg(at(bc.dab_s), 2 * SI, SI, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_up);
     }
     return hip_status(e);
   } catch (...) {

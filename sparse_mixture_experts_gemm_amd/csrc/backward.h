@@ -8,12 +8,15 @@
 
 namespace moe {
 
-// Weight-gradient GEMM: out(seg, m, n) = sum_k A_seg[m][k] B_seg[n][k] over the padded
-// tokens of each segment (see backward.hip for the layouts).
+// Weight-gradient GEMM on token-major rows: out(seg, m, n) = sum over the segment's rows p
+// of A(p, m) B(p, n) (see backward.hip for the layouts).
 struct WgradParams {
-  const uint16_t* a;        // K-major copies, segment seg at a + M * koff[seg]
-  const uint16_t* b;        // at b + N * koff[seg]
-  const int32_t* koff;      // [nseg + 1] padded token offsets (multiples of 64)
+  const uint16_t* a;        // A(p, m) = a[p * lda + a_col + m]
+  int lda, a_col;
+  const uint16_t* b;        // B(p, n) = b[p * ldb + b_col + n]
+  int ldb, b_col;
+  const int32_t* offsets;   // [nseg + 1] row ranges of the segments, or null: rows [0, rows)
+  int rows;
   int M, N;
   int nsplit;               // column-block size of the output layout (N: plain [M][N])
   float* out;               // fp32 [nseg][M][N] (in nsplit blocks)
@@ -23,18 +26,11 @@ struct WgradParams {
 hipError_t launch_transpose_mat(const void* in, void* out, int batch, int R, int C, long long obs,
                                 int ld, hipStream_t s);
 
-// koff[e] = exclusive scan of the segments' rows rounded up to 64 (offsets null: one
-// segment of `rows` rows).
-hipError_t launch_seg_koff(const int32_t* offsets, int nseg, int rows, int32_t* koff, hipStream_t s);
-
-// Upper bound of koff[nseg] (elements of the padded token axis).
-size_t padded_k_bound(int rows, int nseg);
-
-// K-major, zero-padded copy of the segment rows of in (bf16, row stride ld_in, columns
-// [col_in, col_in + C)), rows gathered through row_index and scaled by row_scale if given.
-hipError_t launch_transpose_rows(const void* in, int ld_in, int col_in, const int32_t* row_index,
-                                 const float* row_scale, const int32_t* offsets, int nseg, int rows,
-                                 const int32_t* koff, int C, void* out, hipStream_t s);
+// out[p] = scale[p] * in[index[p]] for p < *valid_rows (a device count <= max_rows; bf16 rows
+// of C columns; scale may be null).  Rows past the count are neither read nor written.
+hipError_t launch_gather_rows(const void* in, const int32_t* index, const float* scale,
+                              const int32_t* valid_rows, int max_rows, int C, void* out,
+                              hipStream_t s);
 
 // dw[t*k + j] = dout[t] . y[slot_pos[t*k + j]] / topk_w[t*k + j] (0 for dropped slots).
 hipError_t launch_routing_weight_grad(int T, int k, int d, const void* dout, const void* y,

@@ -9,11 +9,9 @@
 // combine of dx, and the weight-gradient GEMMs, whose contraction runs over the tokens of
 // each expert (K differs per expert).
 //
-// Layouts (bf16 unless noted):
-//  * K-major copies of activations for the weight gradients: segment e holds [C][Kp_e] with
-//    Kp_e = n_e rounded up to 64 and zero padding, at element offset C * koff[e], where koff
-//    is the exclusive scan of the Kp_e (built on the device from the expert offsets).
-//  * weight gradients are fp32 in the weights' [out, in] layout.
+// Layouts: activations bf16 and token-major ([rows][features]), as the forward leaves them
+// (the weight gradients read them in place, transposing in LDS); weight gradients fp32 in
+// the weights' [out, in] layout.
 #include "backward.h"
 #include "common.h"
 
@@ -51,75 +49,31 @@ __global__ __launch_bounds__(256) void transpose_mat_kernel(const uint16_t* __re
   }
 }
 
-// koff[e] = sum over e' < e of (rows of e' rounded up to 64); koff[nseg] = total.  One wave.
-__global__ void seg_koff_kernel(const int32_t* __restrict__ offsets, int nseg, int rows,
-                                int32_t* __restrict__ koff) {
-  const int lane = threadIdx.x;
-  int n = 0;
-  if (lane < nseg) n = offsets != nullptr ? offsets[lane + 1] - offsets[lane] : rows;
-  int incl = (n + 63) & ~63;
+// out[p] = scale(p) * in[index[p]] for p < *valid_rows (bf16 rows of C columns; scale in
+// fp32, one rounding): a permuted, optionally weighted copy of token rows.  The grid covers
+// the largest row count; the device-side count bounds it, because index is only written up
+// to there (a capacity drops slots, and the permutation then has fewer rows).  One workgroup
+// per row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ in,
+                                                          const int32_t* __restrict__ index,
+                                                          const float* __restrict__ scale,
+                                                          const int32_t* __restrict__ valid_rows,
+                                                          int C, uint16_t* __restrict__ out) {
+  const int p = blockIdx.x;
+  if (p >= *valid_rows) return;   // uniform: past the permuted rows
+  const uint16_t* src = in + (size_t)index[p] * C;
+  const float s = scale != nullptr ? scale[p] : 1.0f;
+  for (int c = threadIdx.x * 8; c < C; c += 256 * 8) {
+    uint4 v = *reinterpret_cast<const uint4*>(src + c);
+    if (scale != nullptr) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane < nseg) koff[lane + 1] = incl;
-  if (lane == 0) koff[0] = 0;
-}
-
-// K-major, zero-padded copy of segment rows: out[C * koff[e] + c * Kp_e + k] =
-// scale(p) * in[src(p) * ld_in + col_in + c] for p = row0_e + k, k < n_e; 0 for n_e <= k < Kp_e.
-// src(p) = row_index[p] (or p); scale(p) = row_scale[p] (or 1), applied in fp32 before the
-// rounding to bf16.  Blocks: (64-row block of the padded K space) x (64-column block).
-__global__ __launch_bounds__(256) void transpose_rows_kernel(
-    const uint16_t* __restrict__ in, int ld_in, int col_in, const int32_t* __restrict__ row_index,
-    const float* __restrict__ row_scale, const int32_t* __restrict__ offsets, int nseg, int rows,
-    const int32_t* __restrict__ koff, int C, uint16_t* __restrict__ out) {
-  __shared__ uint16_t t[kT][kT + 8];
-  const int cblocks = C / kT;
-  const int kb = blockIdx.x / cblocks, c0 = (blockIdx.x % cblocks) * kT;
-  const int k0 = kb * kT;
-  if (k0 >= koff[nseg]) return;   // uniform: beyond the padded K space
-  int lo = 0, hi = nseg - 1;      // last segment with koff[seg] <= k0
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (koff[mid] <= k0) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int kp = koff[e + 1] - koff[e];
-  const int kl0 = k0 - koff[e];
-  const int row0 = offsets != nullptr ? offsets[e] : 0;
-  const int n = offsets != nullptr ? offsets[e + 1] - row0 : rows;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = h * 32 + tid / 8, c = (tid % 8) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (kl0 + k < n) {
-      const int p = row0 + kl0 + k;
-      const int sr = row_index != nullptr ? row_index[p] : p;
-      v = *reinterpret_cast<const uint4*>(in + (size_t)sr * ld_in + col_in + c0 + c);
-      if (row_scale != nullptr) {
-        const float s = row_scale[p];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o[i] = pack_bf16x2(s * bf16_bits_to_f32(w[i] & 0xffffu), s * bf16_bits_to_f32(w[i] >> 16));
-        v = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(s * bf16_bits_to_f32(w[i] & 0xffffu), s * bf16_bits_to_f32(w[i] >> 16));
+      v = make_uint4(o[0], o[1], o[2], o[3]);
     }
-    *reinterpret_cast<uint4*>(&t[k][c]) = v;
-  }
-  __syncthreads();
-  uint16_t* dst = out + (size_t)C * koff[e];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = h * 32 + tid / 8, k = (tid % 8) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[k + 2 * i][c] | ((uint32_t)t[k + 2 * i + 1][c] << 16);
-    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * kp + kl0 + k) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(out + (size_t)p * C + c) = v;
   }
 }
 
@@ -309,18 +263,24 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-// Weight-gradient GEMM with the contraction over each segment's tokens:
-//   out(seg, m, n) = sum_{k < Kp_seg} A_seg[m][k] B_seg[n][k]    (fp32 accumulation and output)
-// A_seg = A + M * koff[seg] ([M][Kp_seg]), B_seg = B + N * koff[seg] ([N][Kp_seg]), both
-// K-major copies with zero padding; out(seg, m, n) is stored at
-//   out + seg * M * N + (n / nsplit) * M * nsplit + m * nsplit + n % nsplit
-// (nsplit = N: the plain [M][N] layout; a smaller nsplit stores column blocks of nsplit
-// columns as consecutive [M][nsplit] matrices).
+// Weight-gradient GEMM with the contraction over each segment's tokens, on token-major data:
+//   out(seg, m, n) = sum over rows p of the segment of A(p, m) B(p, n),
+//   A(p, m) = a[p * lda + a_col + m], B(p, n) = b[p * ldb + b_col + n]     (bf16 in, fp32 out)
+// out(seg, m, n) is stored at out + seg * M * N + (n / nsplit) * M * nsplit + m * nsplit +
+// n % nsplit (nsplit = N: the plain [M][N] layout; a smaller nsplit stores column blocks of
+// nsplit columns as consecutive [M][nsplit] matrices).
+//
 // One workgroup per BM x BN output tile (256 x 256 with 8 waves of 128 x 64, or 128 x 128
-// with 4 waves of 64 x 64; MFMA 32x32x16), K in slices of 64 through a two-stage LDS ring
-// filled by global_load_lds_dwordx4 (16-byte chunks XOR-swizzled per row), one barrier per
-// slice.  A is the MFMA's first operand: a lane holds 16 rows of one output column, and each
-// fp32 store instruction writes two full 128-byte row segments.
+// with 4 waves of 64 x 64; MFMA 32x32x16), the segment's rows in slices of 64 through a
+// two-stage LDS ring filled by global_load_lds_dwordx4, one barrier per slice.  A slice is
+// stored as it arrives, [64 rows][BM columns] and [64 rows][BN columns]; the MFMA operands,
+// which need 8 consecutive rows (the contraction index) of one column per lane, are read with
+// the transposing LDS load ds_read_b64_tr_b16.  Within a group of 16 lanes that load hands
+// lane i element i % 4 of the 8-byte pieces addressed by lanes (i % 16) / 4 + 4 r, r = 0..3;
+// so lane 16 g + j addresses row r = j / 4 of a 4-row block at column 4 (j % 4) of its
+// 16-column group, and two loads (rows 0-3, 4-7) give each lane its 8 rows.  16-byte chunks
+// are XOR-swizzled by 4 (row & 3), which puts the four rows read together in different bank
+// windows.  Rows past the segment's end and columns past M or N read a zero row.
 __device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
   uint32_t save;
   asm volatile(
@@ -333,50 +293,81 @@ __device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
       : "memory");
 }
 
-__device__ __forceinline__ int swz8w(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
 constexpr int kWgBK = 64;
+__device__ const uint16_t kZeroRow[256] = {};   // source of rows and columns out of range
+
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 template <int BM, int BN, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void wgrad_kernel(WgradParams p) {
-  constexpr int ROWB = kWgBK * 2;                      // bytes per LDS row
   constexpr int WN = WAVES / 2, WTM = BM / 2, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_BYTES = BM * ROWB, ST_BYTES = A_BYTES + BN * ROWB;
+  constexpr int AROW = BM * 2, BROW = BN * 2;          // bytes per LDS row
+  constexpr int A_BYTES = kWgBK * AROW, ST_BYTES = A_BYTES + kWgBK * BROW;
   constexpr int NDMA = ST_BYTES / 1024 / WAVES;        // 1 KB DMAs per wave per slice
-  static_assert(ST_BYTES % (1024 * WAVES) == 0, "DMA split");
+  static_assert(ST_BYTES % (1024 * WAVES) == 0 && A_BYTES % 1024 == 0, "DMA split");
+  static_assert(BM >= 128 && BN >= 128 && BM <= 256 && BN <= 256, "swizzle and zero row");
   __shared__ __align__(1024) unsigned char lds[2 * ST_BYTES];
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int seg = blockIdx.x / (tiles_m * tiles_n);
   const int rem = blockIdx.x % (tiles_m * tiles_n);
   const int m0 = (rem / tiles_n) * BM, n0 = (rem % tiles_n) * BN;
-  const int kp = p.koff[seg + 1] - p.koff[seg];
-  const int nk = kp / kWgBK;
+  const int r0 = p.offsets != nullptr ? p.offsets[seg] : 0;
+  const int nrows = p.offsets != nullptr ? p.offsets[seg + 1] - r0 : p.rows;
+  const int nk = (nrows + kWgBK - 1) / kWgBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const uint16_t* A = p.a + (size_t)p.M * p.koff[seg];
-  const uint16_t* B = p.b + (size_t)p.N * p.koff[seg];
   const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)lds;
 
-  // this lane's DMA sources: DMA q covers 8 LDS rows of 128 bytes (A rows, then B rows)
-  const uint16_t* src[NDMA];
+  // DMA q of a slice covers 1 KB of LDS: A rows for q < A_BYTES / 1 KB, then B rows.  This
+  // lane's slice row, operand and source column for each of its DMAs (the row moves with
+  // the slice; the column is fixed).
+  int drow[NDMA];
+  bool dis_b[NDMA], dcol_ok[NDMA];
+  const uint16_t* dbase[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int q = wave * NDMA + i;
-    const int row = q * 8 + lane / 8;
-    if (row < BM) {
-      const int m = min(m0 + row, p.M - 1);
-      src[i] = A + (size_t)m * kp + ((lane % 8) ^ swz8w(row)) * 8;
-    } else {
-      const int n = min(n0 + row - BM, p.N - 1);
-      src[i] = B + (size_t)n * kp + ((lane % 8) ^ swz8w(row - BM)) * 8;
-    }
+    const bool isb = q * 1024 >= A_BYTES;
+    const int rowb = isb ? BROW : AROW;
+    const int off = isb ? q * 1024 - A_BYTES : q * 1024;
+    const int row = off / rowb + (lane * 16) / rowb;           // slice row 0..63
+    const int pchunk = ((lane * 16) % rowb) / 16;               // physical 16-byte chunk
+    const int col = (pchunk ^ ((row & 3) << 2)) * 8;            // logical column in the tile
+    const int gcol = (isb ? n0 : m0) + col;
+    drow[i] = row;
+    dis_b[i] = isb;
+    dcol_ok[i] = gcol < (isb ? p.N : p.M);
+    dbase[i] = isb ? p.b + p.b_col + gcol : p.a + p.a_col + gcol;
   }
   auto issue = [&](int kt) {
     const uint32_t st = lds_base + (uint32_t)((kt & 1) * ST_BYTES);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      dma16_wg(st + (uint32_t)((wave * NDMA + i) * 1024), src[i] + (size_t)kt * kWgBK);
+    for (int i = 0; i < NDMA; ++i) {
+      const int rr = kt * kWgBK + drow[i];
+      const bool ok = rr < nrows && dcol_ok[i];
+      const size_t ld = dis_b[i] ? (size_t)p.ldb : (size_t)p.lda;
+      const uint16_t* src = ok ? dbase[i] + (size_t)(r0 + rr) * ld : kZeroRow;
+      dma16_wg(st + (uint32_t)((wave * NDMA + i) * 1024), src);
+    }
+  };
+  // transposing operand load: 8 rows (k) of column base + (lane % 32) in two halves
+  const int g = lane >> 4, jj = lane & 15;
+  const int trow = 8 * (g >> 1) + (jj >> 2);                   // + 4 h + 16 ks
+  const int tcol = 16 * (g & 1) + 4 * (jj & 3);               // + fragment base column
+  auto ld_tr = [&](const unsigned char* base, int rowb, int ks, int colbase) -> bf16x8 {
+    v4s v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = ks * 16 + 4 * h + trow;
+      const int col = colbase + tcol;
+      const int addr = row * rowb + ((((col >> 3) ^ ((row & 3) << 2)) << 4) | ((col & 7) << 1));
+      v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(base + addr));
+    }
+    const v4s lo = v[0], hi = v[1];
+    return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+        lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
 
   f32x16 acc[FM][FN];
@@ -397,18 +388,11 @@ __global__ __launch_bounds__(WAVES * 64) void wgrad_kernel(WgradParams p) {
     const unsigned char* Bs = As + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < kWgBK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
       bf16x8 af[FM], bf[FN];
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int ra = wm * WTM + f * 32 + (lane & 31);
-        af[f] = *reinterpret_cast<const bf16x8*>(As + ra * ROWB + ((c ^ swz8w(ra)) << 4));
-      }
+      for (int f = 0; f < FM; ++f) af[f] = ld_tr(As, AROW, ks, wm * WTM + f * 32);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int rb = wn * WTN + f * 32 + (lane & 31);
-        bf[f] = *reinterpret_cast<const bf16x8*>(Bs + rb * ROWB + ((c ^ swz8w(rb)) << 4));
-      }
+      for (int f = 0; f < FN; ++f) bf[f] = ld_tr(Bs, BROW, ks, wn * WTN + f * 32);
 #pragma unroll
       for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
@@ -446,23 +430,13 @@ hipError_t launch_transpose_mat(const void* in, void* out, int batch, int R, int
   return hipGetLastError();
 }
 
-hipError_t launch_seg_koff(const int32_t* offsets, int nseg, int rows, int32_t* koff, hipStream_t s) {
-  hipLaunchKernelGGL(seg_koff_kernel, dim3(1), dim3(64), 0, s, offsets, nseg, rows, koff);
-  return hipGetLastError();
-}
-
-// sum over segments of (n_e rounded up to 64) <= rows + 63 nseg <= this bound (a multiple of 64)
-size_t padded_k_bound(int rows, int nseg) { return (((size_t)rows + 63) & ~(size_t)63) + 64 * (size_t)nseg; }
-
-hipError_t launch_transpose_rows(const void* in, int ld_in, int col_in, const int32_t* row_index,
-                                 const float* row_scale, const int32_t* offsets, int nseg, int rows,
-                                 const int32_t* koff, int C, void* out, hipStream_t s) {
-  const size_t kblocks = padded_k_bound(rows, nseg) / kT;
-  const size_t blocks = kblocks * (size_t)(C / kT);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(in), ld_in, col_in, row_index, row_scale, offsets,
-                     nseg, rows, koff, C, static_cast<uint16_t*>(out));
+hipError_t launch_gather_rows(const void* in, const int32_t* index, const float* scale,
+                              const int32_t* valid_rows, int max_rows, int C, void* out,
+                              hipStream_t s) {
+  if (max_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)max_rows), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(in), index, scale, valid_rows, C,
+                     static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 
@@ -530,10 +504,10 @@ hipError_t launch_wgrad(const WgradParams& p, int nseg, int num_cus, hipStream_t
   auto tiles = [&](int bm, int bn) {
     return (long long)nseg * ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
   };
-  // 256 x 256 tiles when every CU still gets two, else 128 x 128
+  // 256 x 256 tiles (less LDS traffic per MFMA) unless they would leave most CUs idle
   const long long wide = tiles(256, 256);
   if (wide == 0) return hipSuccess;
-  if (wide >= 2LL * num_cus)
+  if (2 * wide >= num_cus)
     hipLaunchKernelGGL((wgrad_kernel<256, 256, 8>), dim3((unsigned)wide), dim3(8 * 64), 0, s, p);
   else
     hipLaunchKernelGGL((wgrad_kernel<128, 128, 4>), dim3((unsigned)tiles(128, 128)), dim3(4 * 64), 0, s, p);
