@@ -180,7 +180,7 @@ Carve carve(const moe_config* c) {
 
 // Workspace of moe_backward, in carve order.
 struct BwdCarve {
-  size_t w2t, w13t, sh_w2t, sh_w13t;           // transposed weight copies (bf16)
+  size_t sh_w2t;                               // shared W2 transposed to [S I][d] (bf16)
   size_t scores, idx, tw, dw, dl;
   size_t dh_r, dh_s, dab_r, dab_s, dxp_r, dx_s;  // data-gradient intermediates (bf16)
   size_t x_perm, dy_perm;                        // routed rows in permuted order (bf16)
@@ -194,10 +194,7 @@ BwdCarve bwd_carve(const moe_config* c) {
   BwdCarve b{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += align_up(bytes); return at; };
-  b.w2t = take(E * I * d * 2);
-  b.w13t = take(E * d * nab * I * 2);
   b.sh_w2t = take(S * I * d * 2);
-  b.sh_w13t = take(d * nab * S * I * 2);
   b.scores = take(T * E * 4);
   b.idx = take(T * k * 4);
   b.tw = take(T * k * 4);
@@ -696,33 +693,24 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     const void* h_r = fat(cv.h_routed);
     const void* h_s = fat(cv.h_shared);
     const void* y_r = fat(cv.y_routed);
-    uint16_t* w2t = static_cast<uint16_t*>(at(bc.w2t));
-    uint16_t* w13t = static_cast<uint16_t*>(at(bc.w13t));
     uint16_t* sh_w2t = static_cast<uint16_t*>(at(bc.sh_w2t));
-    uint16_t* sh_w13t = static_cast<uint16_t*>(at(bc.sh_w13t));
     float* dw = static_cast<float*>(at(bc.dw));
     float* dl = static_cast<float*>(at(bc.dl));
     const moe_weights wt_fwd = *w;
 
     hipError_t e = hipSuccess;
     auto ok = [&]() { return e == hipSuccess; };
-    // 1. transposed weight copies: W2^T [E][I][d]; [W1^T | W3^T] [E][d][nab I]; shared alike
-    if (ok()) e = moe::launch_transpose_mat(w->w_down, w2t, E, d, I, (long long)I * d, d, stream);
-    if (ok()) e = moe::launch_transpose_mat(w->w_gate, w13t, E, I, d, (long long)d * nab * I, nab * I, stream);
-    if (ok() && swiglu)
-      e = moe::launch_transpose_mat(w->w_up, w13t + I, E, I, d, (long long)d * nab * I, nab * I, stream);
-    if (shared) {
-      if (ok()) e = moe::launch_transpose_mat(w->sh_down, sh_w2t, S, d, I, (long long)I * d, d, stream);
-      if (ok()) e = moe::launch_transpose_mat(w->sh_gate, sh_w13t, S, I, d, I, nab * SI, stream);
-      if (ok() && swiglu)
-        e = moe::launch_transpose_mat(w->sh_up, sh_w13t + SI, S, I, d, I, nab * SI, stream);
-    }
-    // 2. dh = (w dout) W2 (routed rows gathered from dout), dout W2 (shared)
+    // 1. the shared W2 stacked [S][d][I] is not one [d][S I] matrix: a transposed copy
+    //    [S I][d] for its data gradient (the routed and the other weights are read as stored)
+    if (shared && ok())
+      e = moe::launch_transpose_mat(w->sh_down, sh_w2t, S, d, I, (long long)I * d, d, stream);
+    // 2. dh = (w dout) W2 (routed rows gathered from dout; W2 [E][d][I] is [K][N]), dout W2
+    //    (shared)
     moe::GemmParams g{};
     g.a = dout; g.row_index = perm_token; g.offsets = offsets; g.nseg = E; g.rows = Tk;
-    g.d = d; g.I = I; g.S = S; g.N = I; g.K = d; g.kblock = d; g.w_down = w2t;
-    g.row_weight = perm_weight; g.out = at(bc.dh_r);
-    if (ok()) e = moe::launch_grouped_gemm(g, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    g.d = d; g.I = I; g.S = S; g.N = I; g.K = d; g.kblock = d; g.w_down = w->w_down;
+    g.trb_split = d; g.row_weight = perm_weight; g.out = at(bc.dh_r);
+    if (ok()) e = moe::launch_down_trb(g, cus, stream);
     if (shared) {
       moe::GemmParams gs{};
       gs.a = dout; gs.nseg = 1; gs.rows = T; gs.d = d; gs.I = I; gs.S = S; gs.N = SI; gs.K = d;
@@ -742,16 +730,19 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       us.dact = at(bc.dh_s);
       if (ok()) e = moe::launch_up_backward(us, cfg->act, cus, stream);
     }
-    // 4. dx of the experts: [da | db] [W1 ; W3] per row (permuted for the routed ones)
+    // 4. dx of the experts: [da | db] [W1 ; W3] per row (permuted for the routed ones); W1 and
+    //    W3 [I][d] are [K][N], stacked along K
     moe::GemmParams dxg{};
     dxg.a = at(bc.dab_r); dxg.offsets = offsets; dxg.nseg = E; dxg.rows = Tk; dxg.d = d; dxg.I = I;
-    dxg.S = S; dxg.N = d; dxg.K = nab * I; dxg.kblock = nab * I; dxg.w_down = w13t; dxg.out = at(bc.dxp_r);
-    if (ok()) e = moe::launch_grouped_gemm(dxg, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+    dxg.S = S; dxg.N = d; dxg.K = nab * I; dxg.kblock = nab * I; dxg.w_down = w->w_gate;
+    dxg.w_up = w->w_up; dxg.trb_split = I; dxg.out = at(bc.dxp_r);
+    if (ok()) e = moe::launch_down_trb(dxg, cus, stream);
     if (shared) {
       moe::GemmParams dxs{};
       dxs.a = at(bc.dab_s); dxs.nseg = 1; dxs.rows = T; dxs.d = d; dxs.I = I; dxs.S = S; dxs.N = d;
-      dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = sh_w13t; dxs.out = at(bc.dx_s);
-      if (ok()) e = moe::launch_grouped_gemm(dxs, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
+      dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = w->sh_gate; dxs.w_up = w->sh_up;
+      dxs.trb_split = SI; dxs.out = at(bc.dx_s);
+      if (ok()) e = moe::launch_down_trb(dxs, cus, stream);
     }
     // 5. router: scores recomputed, routing-weight and logit gradients
     moe::RouteParams rp = route_params(cfg);

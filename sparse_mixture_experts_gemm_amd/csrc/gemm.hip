@@ -178,7 +178,7 @@ __device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false>
+          bool A8 = false, bool BWD = false, bool TRB = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   constexpr int BK = 64;
@@ -192,6 +192,14 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   // BWD: the UP stage recomputed in the backward pass; the epilogue turns dh into the
   // gradients of the two pre-activations instead of applying the activation
   static_assert(!BWD || (STAGE == 0 && !FP8 && !A8), "backward epilogue: bf16 up projection");
+  // TRB: bf16 weights stored [K][N] (the transpose of the usual layout).  A B slice is staged
+  // as it lies in memory, [BK rows k][BN columns n] (16-byte chunks XOR-swizzled by
+  // 4 (k & 3)), and the MFMA operand, 8 consecutive k of one weight row n per lane, is read
+  // with the transposing load ds_read_b64_tr_b16: within a group of 16 lanes it gives lane i
+  // element i % 4 of the 8-byte pieces addressed by lanes (i % 16) / 4 + 4 r, so lane 16 g +
+  // j addresses row j / 4 of a 4-row block at a column chosen per lane quad; the columns
+  // reproduce the perm32 order of the usual staging, so the epilogue is unchanged.
+  static_assert(!TRB || (STAGE == 1 && !FP8 && !A8 && BN == 256), "transposed weights: bf16 DOWN");
   constexpr int ESZ_A = A8 ? 1 : 2;                 // bytes per A element
   constexpr int AROW = BK * ESZ_A;                  // bytes per A row in LDS
   constexpr int CPR_A = AROW / 16;                  // 16-byte chunks per A row
@@ -279,6 +287,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   bool is_b[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) is_b[i] = wave * NDMA + i >= A_DMA;
+  int src_seg = 0;   // segment of the tile being loaded (TRB: offset of the second matrix)
 
   auto set_sources = [&](int j) {
     const TileCoord tc = tile_at(j);
@@ -289,10 +298,20 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       __syncthreads();
     }
     const size_t seg_off = (size_t)tc.seg * N * K;   // weight elements per segment
+    src_seg = tc.seg;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
-      if (!is_b[i]) {
+      if (TRB && is_b[i]) {
+        // two k rows of BN columns per DMA; lane -> (row, physical chunk)
+        const int qb = q - A_DMA;
+        const int kr = qb * 2 + lane / 32;
+        const int lc = (lane % 32) ^ ((kr & 3) << 2);                    // logical chunk
+        int n = tc.n_tile * BN + lc * 8;
+        n = n < N ? n : 0;
+        src[i] = static_cast<const unsigned char*>(p.w_down) +
+                 ((size_t)tc.seg * p.trb_split * N + (size_t)kr * N + n) * 2;
+      } else if (!is_b[i]) {
         const int row = q * (1024 / AROW) + lane / CPR_A;
         const int srow = gather ? s_arow[j & 1][row] : seg_row(tc, row);
         src[i] = a_base + (size_t)srow * K * ESZ_A + (size_t)(((lane % CPR_A) ^ swz_a(row)) * 16);
@@ -337,7 +356,17 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     const uint32_t st = lds_base + (uint32_t)(ist * ST_BYTES);
     const size_t aoff = (size_t)k0 * ESZ_A;
     const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
-    const size_t boff = FP8 ? koff : koff * 2;
+    ptrdiff_t boff = FP8 ? koff : koff * 2;
+    if (TRB) {
+      // rows k0 .. of the first matrix, or (k0 >= trb_split) of the second one
+      const ptrdiff_t nb = (ptrdiff_t)N * 2;
+      if (k0 < p.trb_split) {
+        boff = (ptrdiff_t)k0 * nb;
+      } else {
+        boff = (static_cast<const unsigned char*>(p.w_up) - static_cast<const unsigned char*>(p.w_down)) +
+               ((ptrdiff_t)src_seg * (K - 2 * p.trb_split) + (k0 - p.trb_split)) * nb;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
@@ -418,7 +447,21 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int row = wn * WTN + fn * 32 + (lane & 31);
-        if (!FP8) {
+        if (TRB) {
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const int g = lane >> 4, jj = lane & 15, q4 = jj & 3;
+          const int col = wn * WTN + fn * 32 + 16 * (q4 & 1) + 8 * (g & 1) + 4 * (q4 >> 1);
+          v4s v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int kr = ks * 16 + 8 * (g >> 1) + 4 * h + (jj >> 2);
+            const int addr = kr * (BN * 2) + ((((col >> 3) ^ ((kr & 3) << 2)) << 4) | ((col & 7) << 1));
+            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(B + addr));
+          }
+          b[fn] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+              v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]});
+        } else if (!FP8) {
           b[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
         } else {
           const uint2 q = *reinterpret_cast<const uint2*>(
@@ -751,9 +794,9 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false>
+          bool A8 = false, bool BWD = false, bool TRB = false>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -796,6 +839,14 @@ hipError_t launch_f32(const GemmParams& p, int num_cus, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_down_trb(const GemmParams& p, int num_cus, hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  const long long wide_tiles = ((p.rows + 255) / 256) * ((p.N + 255LL) / 256);
+  if (wide_tiles >= 2LL * num_cus)
+    return launch_cfg<MOE_CFG_WIDE, 1, MOE_ACT_SWIGLU, false, false, false, true>(p, num_cus, s);
+  return launch_cfg<MOE_CFG_NARROW_DOWN, 1, MOE_ACT_SWIGLU, false, false, false, true>(p, num_cus, s);
+}
 
 hipError_t launch_up_backward(const GemmParams& p, int act, int num_cus, hipStream_t s) {
   if (p.rows == 0) return hipSuccess;

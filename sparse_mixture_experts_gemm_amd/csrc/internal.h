@@ -44,6 +44,9 @@ struct GemmParams {
   const float* row_weight;  // DOWN: per-row multiplier or null
   void* out;                // [rows][N]  (UP backward: [rows][2N] SwiGLU, [rows][N] ReLU^2)
   const void* dact;         // UP backward: gradient of the activation output h, [rows][N]
+  // DOWN stage on weights stored [K][N] per segment (launch_down_trb): B(n, k) is
+  // w_down[seg][k][n] for k < trb_split, then w_up[seg][k - trb_split][n]
+  int trb_split;
 };
 
 enum class Stage { Up = 0, Down = 1 };
@@ -81,6 +84,12 @@ hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int ac
 // reads dh = p.dact [rows][N] and writes the gradients of the two pre-activations a = A W1^T
 // and b = A W3^T: SwiGLU out[r] = [da (N) | db (N)], ReLU^2 out[r] = da.
 hipError_t launch_up_backward(const GemmParams& p, int act, int num_cus, hipStream_t s);
+
+// DOWN-stage grouped GEMM whose weights are stored [K][N] (row k of N contiguous outputs)
+// instead of [N][K]: out[r] = row_weight[r] * sum_k a[r][k] B(n, k), with B as described at
+// GemmParams::trb_split (bf16 only).  The data gradients of the backward pass use it on the
+// forward weights as they are.
+hipError_t launch_down_trb(const GemmParams& p, int num_cus, hipStream_t s);
 
 // Weight-streaming variant of the grouped GEMM for few rows per segment.  `second`, when
 // given, is a second segment set (e.g. the shared experts) run in the same launch.
