@@ -233,15 +233,19 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   __syncthreads();
   const int total = s_tile0[p.nseg];
 
-  // this workgroup's tiles: first + j * per_x, j < ntiles, inside its XCD's range
+  // this workgroup's tiles inside its XCD's range [lo, hi): at step j the XCD's per_x
+  // workgroups take the j-th block of per_x consecutive tiles, slot s the tile
+  // (s + j) mod per_x of the block.  The rotation mixes the tiles of different cost: an
+  // expert's m-tiles alternate in the tile order (full, then part padding), so a fixed
+  // slot would see only one kind with an even per_x.
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
   const int per_x = (nwg - xcd + kNumXcd - 1) / kNumXcd;
   const int lo = (int)(((long long)xcd * total) / kNumXcd);
   const int hi = (int)(((long long)(xcd + 1) * total) / kNumXcd);
-  const int first = lo + slot;
-  const int ntiles = first < hi ? (hi - first + per_x - 1) / per_x : 0;
+  const int full = (hi - lo) / per_x, rem = (hi - lo) % per_x;
+  const int ntiles = full + ((slot + full) % per_x < rem ? 1 : 0);
   if (ntiles == 0) return;   // uniform over the workgroup
   const int nk = K / BK;
   const int nslices = ntiles * nk;
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   const int sw = swz_a(lane & 31);     // swizzle of every A operand row this lane reads
 
   auto tile_at = [&](int j) {
-    return decode_tile(first + j * per_x, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
+    return decode_tile(lo + j * per_x + (slot + j) % per_x, p.nseg, BM, NT, s_tile0, s_row0, s_rows);
   };
   // row of the segment's row space that A row r of a tile reads (clamped into the segment;
   // the results of clamped rows are never stored)
