@@ -514,6 +514,27 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
             acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
                                                                   acc[fm][fn], 0, 0, 0);
       }
+      {
+        // instruction order for the scheduler: the LDS reads of K-step ks + 1 interleaved
+        // one by one with the MFMAs of step ks, so that they land while it multiplies
+        // (left to itself it issues some of them just before their first use)
+        constexpr int NDS = FM + (TRB ? 2 : 1) * FN, NMF = FM * FN;
+        constexpr int NPAIR = NDS < NMF ? NDS : NMF;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          if (ks + 1 < BK / 16) {
+#pragma unroll
+            for (int i = 0; i < NPAIR; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (NMF > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NPAIR, 0);
+            if (NDS > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NPAIR, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+          }
+        }
+      }
     }
     __builtin_amdgcn_s_setprio(0);
 
