@@ -386,18 +386,38 @@ __global__ __launch_bounds__(WAVES * 64) void wgrad_kernel(WgradParams p) {
     if (kt + 1 < nk) issue(kt + 1);
     const unsigned char* As = lds + (kt & 1) * ST_BYTES;
     const unsigned char* Bs = As + A_BYTES;
+    // operands of K-step ks + 1 are read while the MFMAs of step ks run
+    bf16x8 af[2][FM], bf[2][FN];
+    auto load = [&](int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+#pragma unroll
+      for (int f = 0; f < FM; ++f) a[f] = ld_tr(As, AROW, ks, wm * WTM + f * 32);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b[f] = ld_tr(Bs, BROW, ks, wn * WTN + f * 32);
+    };
+    load(0, af[0], bf[0]);
 #pragma unroll
     for (int ks = 0; ks < kWgBK / 16; ++ks) {
-      bf16x8 af[FM], bf[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) af[f] = ld_tr(As, AROW, ks, wm * WTM + f * 32);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) bf[f] = ld_tr(Bs, BROW, ks, wn * WTN + f * 32);
+      if (ks + 1 < kWgBK / 16) load(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
       for (int fa = 0; fa < FM; ++fa)
 #pragma unroll
         for (int fb = 0; fb < FN; ++fb)
-          acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fa], bf[fb], acc[fa][fb], 0, 0, 0);
+          acc[fa][fb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][fa], bf[ks & 1][fb], acc[fa][fb], 0, 0, 0);
+      // instruction order for the scheduler: the transposing reads of step ks + 1 (two per
+      // operand) spread over the MFMAs of step ks
+      constexpr int NDS = 2 * (FM + FN), NMF = FM * FN;
+      constexpr int DPM = NDS / NMF, R = NDS - DPM * NMF;   // the first R MFMAs take one more
+      static_assert(DPM >= 1, "a read after every MFMA");
+      if (ks + 1 < kWgBK / 16) {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < R) __builtin_amdgcn_sched_group_barrier(0x100, DPM + 1, 0);
+          else __builtin_amdgcn_sched_group_barrier(0x100, DPM, 0);
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // slice kt + 1 landed (own DMAs)
     __syncthreads();                                        // ... everyone's; stage kt free
