@@ -24,8 +24,11 @@
 // LDS; their per-channel scales multiply the fp32 accumulator.  Tiles are walked in
 // XCD-contiguous order: workgroup b runs on XCD b % 8, and each XCD takes a contiguous range
 // of (expert, n-tile, m-tile) tiles so that tiles sharing an expert's weights share that
-// XCD's L2.  The K-slices of a workgroup's consecutive tiles form one stream, so the loads
-// of the next tile are in flight while the current tile's epilogue runs.
+// XCD's L2; the slot-to-tile map rotates by one per step, so that every workgroup alternates
+// an expert's full and padded m-tiles and the two stay in step over the same weights.  The
+// K-slices of a workgroup's consecutive tiles form one stream, so the loads of the next
+// tile are in flight while the current tile's epilogue runs.  Within a slice, scheduling
+// directives place the LDS reads of the next K-step between the MFMAs of the current one.
 #include "common.h"
 #include "internal.h"
 
