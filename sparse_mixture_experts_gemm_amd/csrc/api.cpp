@@ -700,50 +700,83 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
 
     hipError_t e = hipSuccess;
     auto ok = [&]() { return e == hipSuccess; };
-    // 1. the shared W2 stacked [S][d][I] is not one [d][S I] matrix: a transposed copy
-    //    [S I][d] for its data gradient (the routed and the other weights are read as stored)
-    if (shared && ok())
-      e = moe::launch_transpose_mat(w->sh_down, sh_w2t, S, d, I, (long long)I * d, d, stream);
-    // 2. dh = (w dout) W2 (routed rows gathered from dout; W2 [E][d][I] is [K][N]), dout W2
-    //    (shared)
+    // weight gradients: contractions over each expert's rows, read token-major
+    auto wg = [&](const void* a, int lda, int a_col, const void* b, int ldb, int b_col,
+                  const int32_t* offs, int nseg, int rows, int M, int N, int nsplit, float* out,
+                  hipStream_t s) {
+      moe::WgradParams wp{static_cast<const uint16_t*>(a), lda, a_col, static_cast<const uint16_t*>(b),
+                          ldb, b_col, offs, rows, M, N, nsplit, out};
+      if (ok()) e = moe::launch_wgrad(wp, nseg, cus, s);
+    };
+    // The shared experts' chain (steps 1-4 and 7 below for them) runs on a second stream:
+    // its GEMMs overlap the routed ones, and its weight gradients, bound by the MFMAs,
+    // share the CUs with the routed weight gradients, bound by their fp32 stores.  The main
+    // stream waits for its dx rows before the combine and for all of it at the end.
+    hipStream_t side = stream;
+    hipEvent_t fork_ev = nullptr, dxs_ev = nullptr, join = nullptr;
+    if (shared) {
+      st = side_stream(&side);
+      if (st != MOE_OK) return st;
+      hipError_t ce = hipEventCreateWithFlags(&fork_ev, hipEventDisableTiming);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&dxs_ev, hipEventDisableTiming);
+      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+      if (ce != hipSuccess) {
+        for (hipEvent_t ev : {fork_ev, dxs_ev, join})
+          if (ev != nullptr) (void)hipEventDestroy(ev);
+        return hip_status(ce);
+      }
+      e = hipEventRecord(fork_ev, stream);
+      if (ok()) e = hipStreamWaitEvent(side, fork_ev, 0);
+      // 1. the shared W2 stacked [S][d][I] is not one [d][S I] matrix: a transposed copy
+      //    [S I][d] for its data gradient (the routed and the other weights are read as
+      //    stored)
+      if (ok()) e = moe::launch_transpose_mat(w->sh_down, sh_w2t, S, d, I, (long long)I * d, d, side);
+      // 2. dh = dout W2
+      moe::GemmParams gs{};
+      gs.a = dout; gs.nseg = 1; gs.rows = T; gs.d = d; gs.I = I; gs.S = S; gs.N = SI; gs.K = d;
+      gs.kblock = d; gs.w_down = sh_w2t; gs.out = at(bc.dh_s);
+      if (ok()) e = moe::launch_grouped_gemm(gs, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, side);
+      // 3. up projection recomputed, activation backward in the epilogue
+      moe::GemmParams us{};
+      us.a = x; us.nseg = 1; us.rows = T; us.d = d; us.I = I; us.S = S; us.N = SI; us.K = d;
+      us.kblock = d; us.w_gate = w->sh_gate; us.w_up = w->sh_up; us.out = at(bc.dab_s);
+      us.dact = at(bc.dh_s);
+      if (ok()) e = moe::launch_up_backward(us, cfg->act, cus, side);
+      // 4. dx rows: [da | db] [W1 ; W3]
+      moe::GemmParams dxs{};
+      dxs.a = at(bc.dab_s); dxs.nseg = 1; dxs.rows = T; dxs.d = d; dxs.I = I; dxs.S = S; dxs.N = d;
+      dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = w->sh_gate; dxs.w_up = w->sh_up;
+      dxs.trb_split = SI; dxs.out = at(bc.dx_s);
+      if (ok()) e = moe::launch_down_trb(dxs, cus, side);
+      if (ok()) e = hipEventRecord(dxs_ev, side);
+      // 7. weight gradients
+      if (grads->d_sh_down != nullptr)
+        wg(dout, d, 0, h_s, SI, 0, nullptr, 1, T, d, SI, I, grads->d_sh_down, side);
+      if (grads->d_sh_gate != nullptr)
+        wg(at(bc.dab_s), nab * SI, 0, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_gate, side);
+      if (swiglu && grads->d_sh_up != nullptr)
+        wg(at(bc.dab_s), 2 * SI, SI, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_up, side);
+      if (ok()) e = hipEventRecord(join, side);
+    }
+    // 2. dh = (w dout) W2 (routed rows gathered from dout; W2 [E][d][I] is [K][N])
     moe::GemmParams g{};
     g.a = dout; g.row_index = perm_token; g.offsets = offsets; g.nseg = E; g.rows = Tk;
     g.d = d; g.I = I; g.S = S; g.N = I; g.K = d; g.kblock = d; g.w_down = w->w_down;
     g.trb_split = d; g.row_weight = perm_weight; g.out = at(bc.dh_r);
     if (ok()) e = moe::launch_down_trb(g, cus, stream);
-    if (shared) {
-      moe::GemmParams gs{};
-      gs.a = dout; gs.nseg = 1; gs.rows = T; gs.d = d; gs.I = I; gs.S = S; gs.N = SI; gs.K = d;
-      gs.kblock = d; gs.w_down = sh_w2t; gs.out = at(bc.dh_s);
-      if (ok()) e = moe::launch_grouped_gemm(gs, moe::Stage::Down, cfg->act, MOE_BF16, MOE_BF16, cus, stream);
-    }
     // 3. up projections recomputed, activation backward in the epilogue: [da | db]
     moe::GemmParams u{};
     u.a = x; u.row_index = perm_token; u.offsets = offsets; u.nseg = E; u.rows = Tk; u.d = d;
     u.I = I; u.S = S; u.N = I; u.K = d; u.kblock = d; u.w_gate = wt_fwd.w_gate; u.w_up = wt_fwd.w_up;
     u.out = at(bc.dab_r); u.dact = at(bc.dh_r);
     if (ok()) e = moe::launch_up_backward(u, cfg->act, cus, stream);
-    if (shared) {
-      moe::GemmParams us{};
-      us.a = x; us.nseg = 1; us.rows = T; us.d = d; us.I = I; us.S = S; us.N = SI; us.K = d;
-      us.kblock = d; us.w_gate = w->sh_gate; us.w_up = w->sh_up; us.out = at(bc.dab_s);
-      us.dact = at(bc.dh_s);
-      if (ok()) e = moe::launch_up_backward(us, cfg->act, cus, stream);
-    }
-    // 4. dx of the experts: [da | db] [W1 ; W3] per row (permuted for the routed ones); W1 and
-    //    W3 [I][d] are [K][N], stacked along K
+    // 4. dx of the experts: [da | db] [W1 ; W3] per permuted row; W1 and W3 [I][d] are
+    //    [K][N], stacked along K
     moe::GemmParams dxg{};
     dxg.a = at(bc.dab_r); dxg.offsets = offsets; dxg.nseg = E; dxg.rows = Tk; dxg.d = d; dxg.I = I;
     dxg.S = S; dxg.N = d; dxg.K = nab * I; dxg.kblock = nab * I; dxg.w_down = w->w_gate;
     dxg.w_up = w->w_up; dxg.trb_split = I; dxg.out = at(bc.dxp_r);
     if (ok()) e = moe::launch_down_trb(dxg, cus, stream);
-    if (shared) {
-      moe::GemmParams dxs{};
-      dxs.a = at(bc.dab_s); dxs.nseg = 1; dxs.rows = T; dxs.d = d; dxs.I = I; dxs.S = S; dxs.N = d;
-      dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = w->sh_gate; dxs.w_up = w->sh_up;
-      dxs.trb_split = SI; dxs.out = at(bc.dx_s);
-      if (ok()) e = moe::launch_down_trb(dxs, cus, stream);
-    }
     // 5. router: scores recomputed, routing-weight and logit gradients
     moe::RouteParams rp = route_params(cfg);
     rp.select_bias = w->select_bias;
@@ -755,38 +788,35 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     if (ok() && (grads->d_router != nullptr || grads->d_logit_bias != nullptr))
       e = moe::launch_router_wgrad(T, d, E, x, dl, grads->d_router, grads->d_logit_bias, at(bc.rg), stream);
     // 6. dx = dl W_r + experts (+ dout)
+    if (shared && ok()) e = hipStreamWaitEvent(stream, dxs_ev, 0);
     if (ok())
       e = moe::launch_dx_combine(T, d, E, k, dl, w->router, at(bc.dxp_r), slot_pos,
                                  shared ? at(bc.dx_s) : nullptr, cfg->residual ? dout : nullptr,
                                  grads->dx, stream);
-    // 7. weight gradients: contractions over each expert's rows, read token-major; the
-    //    routed x rows and the weighted dout rows are first copied into permuted order
-    auto wg = [&](const void* a, int lda, int a_col, const void* b, int ldb, int b_col,
-                  const int32_t* offs, int nseg, int rows, int M, int N, int nsplit, float* out) {
-      moe::WgradParams wp{static_cast<const uint16_t*>(a), lda, a_col, static_cast<const uint16_t*>(b),
-                          ldb, b_col, offs, rows, M, N, nsplit, out};
-      if (ok()) e = moe::launch_wgrad(wp, nseg, cus, stream);
-    };
+    // 7. weight gradients of the routed experts: the x rows and the weighted dout rows are
+    //    first copied into permuted order
     if (grads->d_w_down != nullptr) {
       if (ok()) e = moe::launch_gather_rows(dout, perm_token, perm_weight, offsets + E, Tk, d,
                                              at(bc.dy_perm), stream);
-      wg(at(bc.dy_perm), d, 0, h_r, I, 0, offsets, E, Tk, d, I, I, grads->d_w_down);
+      wg(at(bc.dy_perm), d, 0, h_r, I, 0, offsets, E, Tk, d, I, I, grads->d_w_down, stream);
     }
     if (grads->d_w_gate != nullptr || (swiglu && grads->d_w_up != nullptr)) {
       if (ok()) e = moe::launch_gather_rows(x, perm_token, nullptr, offsets + E, Tk, d, at(bc.x_perm),
                                              stream);
       if (grads->d_w_gate != nullptr)
-        wg(at(bc.dab_r), nab * I, 0, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_gate);
+        wg(at(bc.dab_r), nab * I, 0, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_gate,
+           stream);
       if (swiglu && grads->d_w_up != nullptr)
-        wg(at(bc.dab_r), 2 * I, I, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_up);
+        wg(at(bc.dab_r), 2 * I, I, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_up,
+           stream);
     }
     if (shared) {
-      if (grads->d_sh_down != nullptr)
-        wg(dout, d, 0, h_s, SI, 0, nullptr, 1, T, d, SI, I, grads->d_sh_down);
-      if (grads->d_sh_gate != nullptr)
-        wg(at(bc.dab_s), nab * SI, 0, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_gate);
-      if (swiglu && grads->d_sh_up != nullptr)
-        wg(at(bc.dab_s), 2 * SI, SI, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_up);
+      // also after an error: the side stream's work is ordered before what follows
+      const hipError_t we = hipStreamWaitEvent(stream, join, 0);
+      if (ok()) e = we;
+      // every event has been waited on or is pending in a stream: its resources are
+      // released once it completes
+      for (hipEvent_t ev : {fork_ev, dxs_ev, join}) (void)hipEventDestroy(ev);
     }
     return hip_status(e);
   } catch (...) {
