@@ -181,7 +181,7 @@ __device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   constexpr int BK = 64;
@@ -388,7 +388,11 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   for (int a = 0; a < FM; ++a)
 #pragma unroll
     for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
-  constexpr int TFM = (FP8 && STAGE == 1) ? FM : 1, TFN = (FP8 && STAGE == 1) ? FN : 1;
+  // e4m3 DOWN over several weight-scale blocks of K (the stacked shared experts): the
+  // finished blocks are folded into a second accumulator set.  KBLK = false: one block
+  // (p.kblock == K, checked by the launcher), the scale is applied in the epilogue only.
+  constexpr bool FOLD = FP8 && STAGE == 1 && KBLK;
+  constexpr int TFM = FOLD ? FM : 1, TFN = FOLD ? FN : 1;
   f32x16 acc_tot[TFM][TFN];
 #pragma unroll
   for (int a = 0; a < TFM; ++a)
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   int j3 = 0;                      // j mod 3
   for (int g = 0; g < nslices; ++g) {
     if (g + NSTAGE - 1 < nslices) issue_next();
-    if (FP8 && STAGE == 1 && kt > 0 && ((kt * BK) % p.kblock) == 0) {
+    if (FOLD && kt > 0 && ((kt * BK) % p.kblock) == 0) {
       // the next K block belongs to another shared expert: fold the finished block
       // with its per-channel scales
       const int blk = (kt * BK) / p.kblock - 1;
@@ -822,9 +826,9 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB, KBLK>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -839,12 +843,18 @@ hipError_t launch_mfma_a8(const GemmParams& p, int num_cus, hipStream_t s) {
 
 template <int STAGE, int ACT, bool FP8>
 hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
-  constexpr bool kWideOk = !(FP8 && STAGE == 1);   // e4m3 down: two accumulator sets
   const bool swiglu = STAGE == 0 && ACT == MOE_ACT_SWIGLU;
   const long long bcols = swiglu ? 2LL * p.N : p.N;
   const long long wide_tiles = ((p.rows + 255) / 256) * ((bcols + 255) / 256);
-  if (kWideOk && wide_tiles >= 2LL * num_cus) {
-    if constexpr (kWideOk) return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
+  if (wide_tiles >= 2LL * num_cus) {
+    if constexpr (FP8 && STAGE == 1) {
+      // e4m3 down: 256 x 256 tiles only with one weight-scale block (no second
+      // accumulator set)
+      if (p.kblock == p.K)
+        return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, false>(p, num_cus, s);
+    } else {
+      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
+    }
   }
   if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_NARROW_UP, STAGE, ACT, FP8>(p, num_cus, s);
   else return launch_cfg<MOE_CFG_NARROW_DOWN, STAGE, ACT, FP8>(p, num_cus, s);

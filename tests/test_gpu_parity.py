@@ -39,8 +39,11 @@ SMALL = {
     "multi_tile_swiglu": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256, seed=37),
     "multi_tile_relu2_e4m3": W.small_shape(T=8192, d=512, E=8, k=4, G=2, Gk=1, S=1, I=256,
                                            act="relu2", weight_dtype="e4m3", seed=38),
-    # enough rows for 256 x 256 tiles in the routed GEMMs
+    # enough rows for 256 x 256 tiles in the routed GEMMs (bf16; e4m3 weights, whose down
+    # projection takes them with a single weight-scale block)
     "multi_tile_wide": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512, seed=40),
+    "multi_tile_wide_e4m3": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512,
+                                          act="relu2", weight_dtype="e4m3", seed=52),
     # selection-only expert bias: softmax gating (fp32) and n_g = 2 groups (bf16)
     "biased_softmax_f32": W.small_shape(T=257, d=128, E=16, k=3, score="softmax", G=1, Gk=1,
                                         S=0, I=64, act_dtype="f32", weight_dtype="f32",
@@ -476,7 +479,7 @@ def test_grouped_gemm_down_routed(name):
 
 
 @pytest.mark.parametrize("name", ["multi_tile_swiglu", "multi_tile_relu2_e4m3", "short_k",
-                                  "multi_tile_wide"])
+                                  "multi_tile_wide", "multi_tile_wide_e4m3"])
 def test_grouped_gemm_routed_every_row(name):
     """Up and down routed GEMMs with several tiles per workgroup, every output row checked."""
     s = shape_of(name)
