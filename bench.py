@@ -287,6 +287,7 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-prenorm", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-skewed", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
@@ -396,6 +397,19 @@ def main(argv=None):
                           "rmsnorm_route_ms": p_route, "plain_route_ms": stage_ms["route"],
                           "combine_with_residual_ms": p_comb,
                           "plain_combine_ms": stage_ms["combine"]}
+    if not args.no_skewed and shape.name == "fusionllm_bf16":
+        # the skewed prefill: 32768 tokens, Zipf(1.2) logit offsets (own weights)
+        kshape = W.SHAPES["skewed_bf16"]
+        krun = Runner(kshape, W.make_layer(kshape))
+        k_ms, _ = krun.timed(max(5, args.steps // 5), args.warmup)
+        kfl = sum(stage_flops(kshape, kshape.T).values())
+        kc = krun.counts()
+        res["skewed"] = {"workload": kshape.name, "ms_per_step": k_ms,
+                         "tokens_per_s": kshape.T / (k_ms * 1e-3),
+                         "layer_tflops": kfl / (k_ms * 1e-3) / 1e12,
+                         "layer_mfma_frac": kfl / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "expert_rows_max": int(kc.max()), "expert_rows_min": int(kc.min())}
+        del krun
     if not args.no_backward and shape.name == "fusionllm_bf16":
         # gradients of the same layer: every data and weight gradient and the router's
         b_ms, b_ws = run.backward_timed(max(5, args.steps // 5), 2)
