@@ -34,6 +34,8 @@ SHAPES = {
                                        select_bias_std=0.7, capacity_factor=1.0, seed=64),
     "bwd_residual_noshared": W.small_shape(T=257, d=256, E=16, k=4, G=1, Gk=1, S=0, I=128,
                                            residual=True, seed=65),
+    # more slots per token than the combine keeps in flight (k = 12)
+    "bwd_k12": W.small_shape(T=96, d=128, E=16, k=12, G=1, Gk=1, S=1, I=64, seed=68),
     # several tiles per workgroup in every GEMM
     "bwd_multi_tile": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256, seed=66),
 }

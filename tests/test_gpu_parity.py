@@ -35,6 +35,9 @@ SMALL = {
     "single_token": W.small_shape(T=1, d=128, E=64, k=6, G=8, Gk=4, S=1, I=64, seed=35),
     "topk1_nogroups": W.small_shape(T=130, d=128, E=32, k=1, G=1, Gk=1, S=0, I=64, seed=36,
                                     renormalize=False, route_scale=2.5),
+    # the largest selection: every token to every expert (k = E, softmax, no groups)
+    "all_experts": W.small_shape(T=100, d=128, E=16, k=16, score="softmax", G=1, Gk=1, S=0, I=64,
+                                 seed=53),
     # more tiles than workgroups: each persistent workgroup streams several tiles
     "multi_tile_swiglu": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256, seed=37),
     "multi_tile_relu2_e4m3": W.small_shape(T=8192, d=512, E=8, k=4, G=2, Gk=1, S=1, I=256,
@@ -205,7 +208,7 @@ def adversarial_scores(T, E, seed):
 
 @pytest.mark.parametrize("E,k,G,Gk,n_g", [(64, 6, 8, 4, 1), (64, 6, 8, 4, 2), (64, 8, 1, 1, 1),
                                           (16, 4, 4, 1, 2), (8, 8, 1, 1, 1), (64, 1, 64, 3, 1),
-                                          (12, 5, 3, 2, 2)])
+                                          (12, 5, 3, 2, 2), (64, 64, 1, 1, 1), (64, 32, 8, 4, 2)])
 def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
     T = 1000
     sc = adversarial_scores(T, E, seed=E * 100 + k * 10 + G + n_g)
@@ -635,7 +638,8 @@ def test_combine(name, with_shared, cf):
 FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                  "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
                  "single_token", "topk1_nogroups", "balance_bf16", "biased_softmax_f32",
-                 "biased_groups_n2", "fp8a_relu2", "small_a8_swiglu", "multi_tile_a8_relu2"]
+                 "biased_groups_n2", "fp8a_relu2", "small_a8_swiglu", "multi_tile_a8_relu2",
+                 "all_experts"]
 
 
 def run_forward(name):
