@@ -92,6 +92,7 @@ moe_status check_config(const moe_config* c) {
   if (E > 64) return MOE_ERR_UNSUPPORTED;
   if (c->fp8_act && (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_FP8_E4M3))
     return MOE_ERR_UNSUPPORTED;
+  if (c->fp8_act && c->dim % 128 != 0) return MOE_ERR_UNSUPPORTED;   // 128-byte K-slices
   if (c->act_dtype == MOE_F32) {
     if (c->weight_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (c->dim % 16 != 0 || c->inter_dim % 16 != 0) return MOE_ERR_UNSUPPORTED;

@@ -184,13 +184,14 @@ template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bo
           bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
-  constexpr int BK = 64;
+  // K values per slice: 64 (128-byte bf16 rows), or 128 e4m3 bytes with e4m3 activations
+  constexpr int BK = A8 ? 128 : 64;
   constexpr int WM = 2, WN = WAVES / 2;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   constexpr bool SWIGLU = (STAGE == 0) && (ACT == MOE_ACT_SWIGLU);
   // A8: e4m3 activations and weights, v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) on
-  // 64-byte LDS rows; every lane reads 32 bytes of a row as two 16-byte chunks, swizzled
-  // by (row >> 2) & 3 so that 16 consecutive rows hit distinct 16-byte bank groups
+  // 128-byte LDS rows (two 64-K MFMA steps per slice, the chunks swizzled as for bf16);
+  // in each step every lane reads 32 bytes of a row as two 16-byte chunks
   static_assert(!A8 || (FP8 && STAGE == 0), "e4m3 activations: up projection, e4m3 weights");
   // BWD: the UP stage recomputed in the backward pass; the epilogue turns dh into the
   // gradients of the two pre-activations instead of applying the activation
@@ -214,8 +215,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   static_assert((A_DMA + B_DMA) % WAVES == 0, "DMA split");
   static_assert(!SWIGLU || FN % 2 == 0, "SwiGLU pairs gate/up MFMA tiles");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
-  auto swz_a = [](int r) { return A8 ? ((r >> 2) & 3) : swz8(r); };   // A rows
-  auto swz_b8 = [](int r) { return A8 ? ((r >> 2) & 3) : swz4(r); };  // e4m3 B rows
+  auto swz_a = [](int r) { return swz8(r); };                        // A rows (128 bytes)
+  auto swz_b8 = [](int r) { return swz4(r); };                       // 64-byte e4m3 B rows
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
 
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         src[i] = a_base + (size_t)srow * K * ESZ_A + (size_t)(((lane % CPR_A) ^ swz_a(row)) * 16);
       } else {
         const int qb = q - A_DMA;
-        const int n = FP8 ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;   // LDS row
+        const int n = (FP8 && !A8) ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;   // LDS row
         const int nl = (n & ~31) | perm32(n & 31);                           // weight row
         int wrow;
         const void* wb;
@@ -345,7 +346,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         wrow = wrow < N ? wrow : 0;
         const size_t e = seg_off + (size_t)wrow * p.kblock;
         src[i] = static_cast<const unsigned char*>(wb) +
-                 (FP8 ? e + ((lane & 3) ^ swz_b8(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
+                 (A8    ? e + ((lane & 7) ^ swz8(n)) * 16
+                  : FP8 ? e + ((lane & 3) ^ swz_b8(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
       }
     }
   };
@@ -485,28 +487,47 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     // of an expert's last 256-row tile) skips its LDS reads and MFMAs
     if (A8) {
       if (wave_rows > 0) {
-        // one 32x32x64 e4m3 MFMA per block and K-slice: lane half h holds K bytes
-        // [32 h, 32 h + 32) of its row in both operands
+        // two 32x32x64 e4m3 MFMA steps per block and slice: in step ks, lane half h holds K
+        // bytes [64 ks + 32 h, + 32) of its row in both operands (logical chunks 4 ks + 2 h
+        // and 4 ks + 2 h + 1); the operands of step 1 are read while step 0 multiplies
         typedef int v8i __attribute__((ext_vector_type(8)));
         const int h = lane >> 5;
-        auto frag8 = [&](const unsigned char* base, int row) {
-          const int z = (row >> 2) & 3;
-          const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 64 + (((2 * h) ^ z) << 4));
-          const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 64 + (((2 * h + 1) ^ z) << 4));
+        auto frag8 = [&](const unsigned char* base, int row, int ks) {
+          const int z = swz8(row), c0 = 4 * ks + 2 * h;
+          const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ z) << 4));
+          const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ z) << 4));
           return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         };
-        v8i a8[FM], b8[FN];
+        // B fragments of both steps and the A fragments of step 0 first; each A fragment of
+        // step 1 is read into its register once step 0's MFMAs of that fragment are issued
+        v8i a8[FM], b8[2][FN];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31));
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) b8[fn] = frag8(B, wn * WTN + fn * 32 + (lane & 31));
+          for (int fn = 0; fn < FN; ++fn) b8[ks][fn] = frag8(B, wn * WTN + fn * 32 + (lane & 31), ks);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                b8[fn], a8[fm], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+          for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  b8[ks][fn], a8[fm], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+            if (ks == 0) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 1);
+          }
+        }
+        // instruction order: the two reads of A fragment fm of step 1 right after step 0's
+        // MFMAs of fm
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * FN + 2 * FM, 0);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
       }
     } else if (wave_rows > 0) {
       load_frags(0, af[0], bfr[0]);
@@ -817,12 +838,12 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #define MOE_CFG_WIDE 256, 256, 8, 2, 1
 #endif
 
-// e4m3 activations: a K-slice is half the bytes, so the ring holds four slices
+// e4m3 activations: 128-byte slices of 128 K values (two MFMA steps), the bf16 ring depths
 #ifndef MOE_CFG_NARROW_A8
-#define MOE_CFG_NARROW_A8 128, 256, 8, 4, 1
+#define MOE_CFG_NARROW_A8 128, 256, 8, 3, 1
 #endif
 #ifndef MOE_CFG_WIDE_A8
-#define MOE_CFG_WIDE_A8 256, 256, 8, 4, 1
+#define MOE_CFG_WIDE_A8 256, 256, 8, 2, 1
 #endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,

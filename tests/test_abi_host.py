@@ -77,6 +77,7 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
     (dict(act_dtype="bf16", weight_dtype="f32"), 2),
     (dict(capacity_factor=float("nan")), 1),
     (dict(fp8_act=True), 2),                       # e4m3 activations need e4m3 weights
+    (dict(fp8_act=True, weight_dtype="e4m3", d=192), 2),   # ... and 128-byte K-slices
     (dict(pre_norm=True, norm_eps=float("nan")), 1), (dict(norm_eps=-1e-6), 1),
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):

@@ -58,6 +58,9 @@ SMALL = {
                                      weight_dtype="e4m3", fp8_act=True, seed=43),
     "multi_tile_a8_relu2": W.small_shape(T=8192, d=512, E=8, k=4, G=1, Gk=1, S=1, I=256,
                                          act="relu2", weight_dtype="e4m3", fp8_act=True, seed=44),
+    # SwiGLU on e4m3 activations with 256 x 256 tiles in the routed up projection
+    "wide_a8_swiglu": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512,
+                                    weight_dtype="e4m3", fp8_act=True, seed=54),
     # K = 64: one K-slice per tile, several tiles per workgroup
     "short_k": W.small_shape(T=40000, d=64, E=4, k=2, G=1, Gk=1, S=1, I=64, seed=39),
     # pre-norm layers (RMSNorm before the router and experts, optional residual)
@@ -572,7 +575,8 @@ def test_quantize_rows_bit_exact(name):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
-@pytest.mark.parametrize("name", ["small_a8_swiglu", "multi_tile_a8_relu2", "fp8a_relu2"])
+@pytest.mark.parametrize("name", ["small_a8_swiglu", "multi_tile_a8_relu2", "fp8a_relu2",
+                                  "wide_a8_swiglu"])
 def test_grouped_gemm_up_e4m3_activations(name):
     """Routed and shared up projections on e4m3 activations: the oracle's codes and scales
     in, every row (or a sample at full size) against the dequantised fp64 product."""
