@@ -80,8 +80,9 @@ typedef struct {
                                 "MoE 数学：路由、容量与平衡详解" of "大模型工程（一）"   */
   int32_t fp8_act;           /* 1: the up projections multiply e4m3 activations (each token
                                 row quantised with scale max|x|/448, moe_quantize_rows) by the
-                                e4m3 weights, fp32 accumulation; needs act_dtype MOE_BF16 and
-                                weight_dtype MOE_FP8_E4M3.  0: bf16 activations.
+                                e4m3 weights, fp32 accumulation; needs act_dtype MOE_BF16,
+                                weight_dtype MOE_FP8_E4M3 and dim a multiple of 128
+                                (MOE_ERR_UNSUPPORTED otherwise).  0: bf16 activations.
                                 Source: FP8 E4M3 products with FP32 accumulation, section
                                 "生产现实：前沿实验室真正交付的内容" of "大模型工程（一）"  */
   int32_t pre_norm;          /* 1: the layer reads RMSNorm(x) = x / sqrt(mean_c x_c^2 + eps)
