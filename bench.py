@@ -290,8 +290,8 @@ def main(argv=None):
     ap.add_argument("--no-skewed", action="store_true")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library runs the "
+              "layer on one GPU and does not shard it across GPUs.", file=sys.stderr)
         return 2
 
     if args.copy_probe_mib > 0:
