@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null required pointer, out-of-range or inconsistent value */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid request outside what this build implements        */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request outside what the library implements      */
   MOE_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than required          */
   MOE_ERR_HIP = 4,          /* a HIP launch or runtime call failed (see moe_last_hip_error) */
   MOE_ERR_INTERNAL = 5      /* unexpected internal failure                              */
