@@ -521,14 +521,15 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     if (stats && !std::isfinite(opts->aux_alpha)) return MOE_ERR_INVALID_ARG;
     bool events = false;
     for (int i = 0; opts != nullptr && i < 8; ++i) events = events || opts->stage_events[i] != nullptr;
-    // few rows per expert: the routed and shared experts stream their weights in one
-    // launch per stage (bf16 activations only)
+    // few rows per expert: weight-streaming GEMMs (bf16 activations only)
     const int adt = cfg->act_dtype;
     const bool decode = !a8 && moe::decode_gemm_applies(up_r, adt) && moe::decode_gemm_applies(dn_r, adt) &&
                         (!shared || (moe::decode_gemm_applies(up_s, adt) &&
                                      moe::decode_gemm_applies(dn_s, adt)));
-    // shared experts on a second stream, unless the stages are being timed one by one
-    const bool fork = shared && !decode && !events;
+    // shared experts on a second stream from the start, where they overlap the routing,
+    // unless the stages are being timed one by one (then, in decode, the routed and shared
+    // experts stream their weights in one launch per stage)
+    const bool fork = shared && !events;
     hipStream_t side = nullptr;
     hipEvent_t fork_ev = nullptr, join = nullptr;
     if (fork) {
@@ -585,16 +586,18 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     }
     mark(2);
     if (decode) {
+      const bool with_shared = shared && !fork;
       if (e == hipSuccess)
         e = moe::launch_decode_gemm(up_r, moe::Stage::Up, cfg->act, cfg->weight_dtype, stream,
-                                    shared ? &up_s : nullptr);
+                                    with_shared ? &up_s : nullptr);
       mark(3);
       mark(4);
       if (e == hipSuccess)
         e = moe::launch_decode_gemm(dn_r, moe::Stage::Down, cfg->act, cfg->weight_dtype, stream,
-                                    shared ? &dn_s : nullptr);
+                                    with_shared ? &dn_s : nullptr);
       mark(5);
       mark(6);
+      if (fork && e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
     } else if (fork) {
       // routed GEMMs here, shared GEMMs on the side stream since the start of the forward
       if (e == hipSuccess)
