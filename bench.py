@@ -120,6 +120,41 @@ class Runner:
         wall = time.perf_counter() - t0
         return a.elapsed_time(b) / steps, wall
 
+    def step_distribution(self, steps, warmup):
+        """Each of K forwards bracketed by its own event pair: median, p10, p90 and mean of
+        the per-step times (ms).  The event records add a few microseconds per step."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            self.moe.forward(self.cfg, self.w, self.x, self.out, self.ws)
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+                "p90": float(np.percentile(t, 90)), "mean": float(t.mean()), "steps": steps}
+
+    def rotated_timed(self, weight_sets, steps, warmup):
+        """K forwards that cycle through several device copies of the same weights, so that
+        no step finds the previous step's weights in the 256 MB Infinity Cache; one event
+        pair around all K."""
+        torch = self.torch
+        n = len(weight_sets)
+        for i in range(warmup):
+            self.moe.forward(self.cfg, weight_sets[i % n], self.x, self.out, self.ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            self.moe.forward(self.cfg, weight_sets[i % n], self.x, self.out, self.ws)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     def backward_timed(self, steps, warmup):
         """One forward, then K moe_backward calls on its workspace (all weight, router and
         input gradients), bracketed by one event pair."""
@@ -236,9 +271,9 @@ def kernel_source_digest(names=GEMM_SOURCES):
     return h.hexdigest()
 
 
-def profiled_traffic(name, sources=GEMM_SOURCES):
-    """HBM bytes per launch recorded in profiles/<name> (from rocprofv3 FETCH_SIZE and
-    WRITE_SIZE runs), or None when the file is absent or the kernel sources changed since."""
+def profiled_value(name, key, sources=GEMM_SOURCES):
+    """A figure recorded in profiles/<name> (from rocprofv3 counter runs), or None when the
+    file is absent or the kernel sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -251,9 +286,71 @@ def profiled_traffic(name, sources=GEMM_SOURCES):
     if fields.get("kernel_source_sha256") != kernel_source_digest(sources):
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def profiled_traffic(name, sources=GEMM_SOURCES):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE runs, calibrated by a plain copy)."""
+    return profiled_value(name, "traffic_bytes_per_launch", sources)
+
+
+def only_kernel(workload, which, steps, warmup):
+    """One grouped-GEMM launch of the workload repeated alone (for counter runs, where every
+    matrix-core dispatch of the process is then this launch): the routing and permutation
+    are computed once through moe_route / moe_permute, then K launches of the chosen stage
+    through moe_grouped_gemm, bracketed by one event pair."""
+    import torch
+    import sparse_mixture_experts_gemm_amd as moe
+    import workloads as W
+    s = W.SHAPES[workload]
+    run = Runner(s, W.make_layer(s))
+    cfg, w = run.cfg, run.w
+    T, k, E = s.T, s.k, s.E
+    dev = "cuda"
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.route(cfg, run.x, w.tensors["router"], w.tensors["logit_bias"], None, None, idx, tw)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pt = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    pw = torch.empty(T * k, dtype=torch.float32, device=dev)
+    moe.permute(cfg, idx, tw, counts, offsets, pt, sp, pw, run.ws)
+    adt = torch.int16 if s.act_dtype == "bf16" else torch.float32
+    SI = s.S * s.I
+    h_r = torch.zeros((T * k, s.I), dtype=adt, device=dev)
+    h_s = torch.zeros((T, max(SI, 1)), dtype=adt, device=dev)
+    y_r = torch.empty((T * k, s.d), dtype=adt, device=dev)
+    y_s = torch.empty((T, s.d), dtype=adt, device=dev)
+    R, SH = moe.MOE_EXPERTS_ROUTED, moe.MOE_EXPERTS_SHARED
+    calls = {
+        "up_routed": lambda: moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, R, run.x, pt, offsets, T * k, w, None, h_r),
+        "down_routed": lambda: moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, R, h_r, None, offsets, T * k, w, pw, y_r),
+        "up_shared": lambda: moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, SH, run.x, None, None, T, w, None, h_s),
+        "down_shared": lambda: moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, SH, h_s, None, None, T, w, None, y_s),
+    }
+    # real h rows for the down projections
+    calls["up_routed"]()
+    if s.S > 0:
+        calls["up_shared"]()
+    f = calls[which]
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        f()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    fl = stage_flops(s, T)[which]
+    print(json.dumps({"workload": workload, "kernel": which, "steps": steps, "warmup": warmup,
+                      "ms_per_launch": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                      "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}))
+    return 0
 
 
 def copy_probe(mib):
@@ -281,6 +378,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--only-kernel", default="",
+                    choices=["", "up_routed", "down_routed", "up_shared", "down_shared"],
+                    help="only time this grouped-GEMM launch of the workload (counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
@@ -296,6 +396,8 @@ def main(argv=None):
 
     if args.copy_probe_mib > 0:
         return copy_probe(args.copy_probe_mib)
+    if args.only_kernel:
+        return only_kernel(args.workload, args.only_kernel, args.steps, args.warmup)
 
     import torch
     import workloads as W
@@ -307,6 +409,7 @@ def main(argv=None):
     T = shape.T
     fl = stage_flops(shape, T)
     total_flops = sum(fl.values())
+    step_dist = run.step_distribution(args.steps, args.warmup)
     stage_ms = run.staged(args.steps, args.warmup)
     # the dominant kernel (the routed up projection), bracketed by its own two events
     dom = "up_routed"
@@ -331,18 +434,49 @@ def main(argv=None):
                    "weights": shape.weight_dtype},
         "layer_tflops": total_flops / (step_ms * 1e-3) / 1e12,
         "layer_mfma_frac": total_flops / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "step_ms_per_step_events": step_dist,
         "stage_ms_with_events": stage_ms,
         "roofline": {"kernel": "grouped GEMM, routed up projection (SwiGLU epilogue)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": profiled_traffic(f"traffic_up_routed_{shape.name}.txt"),
-                     "kernel_ms": dom_ms, "algorithmic_tflop": fl[dom] / 1e12},
+                     "kernel_ms": dom_ms, "algorithmic_tflop": fl[dom] / 1e12,
+                     "mfma_busy_frac": profiled_value(f"counters_up_routed_{shape.name}.txt",
+                                                      "mfma_busy_frac")},
     }
+    if shape.name == "fusionllm_bf16":
+        # the routed down projection, the kernel furthest below its roofline
+        dn_ms = run.staged(args.steps, args.warmup, stages=[4, 5])["down_routed"]
+        res["down_routed"] = {"kernel_ms": dn_ms,
+                              "tflops": fl["down_routed"] / (dn_ms * 1e-3) / 1e12,
+                              "frac": fl["down_routed"] / (dn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "traffic": profiled_traffic(f"traffic_down_routed_{shape.name}.txt"),
+                              "algorithmic_bytes": (shape.T * shape.k * (shape.I + shape.d) * 2
+                                                    + shape.E * shape.d * shape.I * 2),
+                              "mfma_busy_frac": profiled_value(
+                                  f"counters_down_routed_{shape.name}.txt", "mfma_busy_frac")}
+        # the tiny fp32 layer: latency-bound, reported in microseconds
+        tshape = W.SHAPES["tiny_fp32"]
+        trun = Runner(tshape, W.make_layer(tshape))
+        t_ms, _ = trun.timed(args.steps, args.warmup)
+        res["tiny"] = {"workload": tshape.name, "us_per_step": t_ms * 1e3,
+                       "us_per_step_events": {k: (v * 1e3 if k != "steps" else v) for k, v in
+                                              trun.step_distribution(args.steps, args.warmup).items()},
+                       "tokens_per_s": tshape.T / (t_ms * 1e-3)}
+        del trun
     if not args.no_decode:
         dshape = W.SHAPES["decode_bf16"]
         dlay = W.make_layer(dshape)
         drun = Runner(dshape, dlay, weights=run.w)     # same weights as the prefill layer
-        d_ms, _ = drun.timed(args.steps, args.warmup)
+        d_ms_same, _ = drun.timed(args.steps, args.warmup)
+        # two more device copies of the weights: consecutive steps read different copies,
+        # so the 1.28 GB a step streams cannot come from the 256 MB Infinity Cache
+        copies = [drun.w] + [run.moe.Weights(**{n: (None if t is None else t.clone())
+                                                 for n, t in drun.w.tensors.items()})
+                             for _ in range(2)]
+        d_ms = drun.rotated_timed(copies, args.steps, args.warmup)
+        del copies
+        d_dist = drun.step_distribution(args.steps, args.warmup)
         d_graph_ms = drun.graph_timed(args.steps, args.warmup)
         d_stage = drun.staged(args.steps, args.warmup)
         d_up_ms = drun.staged(args.steps, args.warmup, stages=[2, 3])["up_routed"]
@@ -352,10 +486,14 @@ def main(argv=None):
         # routed experts and of the shared experts in one launch
         up_bytes = (touched + dshape.S) * 2 * dshape.d * dshape.I * 2 + dshape.T * dshape.d * 2
         res["decode"] = {"workload": dshape.name, "tokens": dshape.T, "ms_per_step": d_ms,
+                         "weights": "3 device copies, rotated every step",
                          "tokens_per_s": dshape.T / (d_ms * 1e-3),
                          "algorithmic_bytes": nbytes, "experts_touched": touched,
                          "hbm_GBps": nbytes / (d_ms * 1e-3) / 1e9,
                          "hbm_frac": nbytes / (d_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "same_weights_ms_per_step": d_ms_same,
+                         "same_weights_hbm_frac": nbytes / (d_ms_same * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "step_ms_per_step_events": d_dist,
                          "graph_replay_ms_per_step": d_graph_ms,
                          "graph_replay_hbm_frac": nbytes / (d_graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                          "stage_ms_with_events": d_stage,
@@ -435,7 +573,10 @@ def main(argv=None):
             f_ms, _ = frun.timed(max(5, args.steps // 4), args.warmup)
             up_ms = frun.staged(max(5, args.steps // 4), args.warmup, stages=[2, 3])["up_routed"]
             ffl = stage_flops(fshape, fshape.T)
+            lfl = sum(ffl.values())
             f8[name] = {"ms_per_step": f_ms, "tokens_per_s": fshape.T / (f_ms * 1e-3),
+                        "layer_tflops": lfl / (f_ms * 1e-3) / 1e12,
+                        "layer_frac_of_bf16_peak": lfl / (f_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                         "up_routed_ms": up_ms,
                         "up_routed_tflops": ffl["up_routed"] / (up_ms * 1e-3) / 1e12}
         up_a8 = f8["fp8a_relu2"]["up_routed_tflops"]

@@ -188,8 +188,10 @@ moe_status moe_load_stats(const moe_config* cfg, const float* scores, const int3
  *   perm_weight[p] topk_w of permuted row p (optional: both topk_w and perm_weight
  *                  NULL, or both set)                                    [T*k]
  * All int32/fp32 device buffers.  ws: at least moe_workspace_size bytes.  Every row of
- * topk_idx must hold k distinct experts in [0, E) (as moe_route produces); ids outside
- * [0, E) are skipped, duplicates within a row give an unspecified permutation.
+ * topk_idx should hold k distinct experts in [0, E) (as moe_route produces).  An id
+ * outside [0, E) (e.g. -1 padding) is skipped: it gets no row, is not counted, and its
+ * slot_pos is -1, so moe_combine skips it.  Duplicates within a row give an unspecified
+ * permutation.
  * Source: token routing to experts and per-expert batching ("MoE 数学" section and the
  * expert-parallel paragraph of "大模型工程（一）"; "批处理策略" of "开源混合架构大模型技术解析"). */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_idx, const float* topk_w,
@@ -247,10 +249,13 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
  * moe_rmsnorm_route (w->norm_gamma) and the experts read the normalised rows (kept in ws);
  * with cfg->residual, out[t] also adds x[t], after the expert outputs (fp32 sum).
  * With shared experts and more rows than the one-launch decode path takes, the shared
- * GEMMs run on a second stream that the library keeps per device (default priority,
- * created on first use): it waits for everything queued on `stream` before the call,
- * and `stream` waits for it before the combine, so the call is ordered on `stream` as a
- * whole.  Stage events (moe_forward_ex) switch this off. */
+ * GEMMs run on a second stream that the library keeps per (device, caller stream)
+ * (default priority, created on first use with its events, kept until the process ends):
+ * it waits for everything queued on `stream` before the call, and `stream` waits for it
+ * before the combine, so the call is ordered on `stream` as a whole, also under graph
+ * capture.  Calls on different caller streams never share a side stream; after 32 caller
+ * streams on one device, further ones run the shared GEMMs on `stream` itself.  Stage
+ * events (moe_forward_ex) switch the second stream off. */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -308,6 +313,7 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
  *     dw = 0 but keep their place in S); sigmoid ds s (1 - s), or softmax through all E
  *     logits; d_router = dl^T x, d_logit_bias = sum_t dl, dx += dl W_r;
  *   residual: dx += dout.
+ * The shared experts' chain runs on the side stream of moe_forward (same rules).
  * Supported: act_dtype and weight_dtype MOE_BF16, no pre_norm, no fp8_act, route_scale != 0
  * (else MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARG).  dout [T, d] bf16.  Weight gradients
  * accumulate in fp32 over the tokens in a fixed order; the result is deterministic.

@@ -13,8 +13,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "decode.hip",
            "stats.hip", "quant.hip", "backward.hip"]
-EXTRA_FLAGS = os.environ.get("MOE_EXTRA_HIPCC_FLAGS", "").split()
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIPCC = "/opt/rocm/bin/hipcc"
 
 FLAGS = [
     "-std=c++17", "-O3", "--offload-arch=gfx950", "-fPIC", "-x", "hip",
@@ -27,7 +26,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -44,26 +44,55 @@ moe_status current_cus(int* cus) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// A second stream per device for the shared experts, which do not depend on the routing:
-// their GEMMs overlap routing, permutation and the routed GEMMs.  Created on first use
-// (default priority, non-blocking) and kept until the process ends.
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxDevices];
+// A second stream for the shared experts, which do not depend on the routing: their GEMMs
+// overlap routing, permutation and the routed GEMMs.  One side stream (default priority,
+// non-blocking) with its own fork / join events is kept per (device, caller stream), created
+// on first use and kept until the process ends, so calls on different caller streams (or
+// under graph capture on one of them) never share a side stream.  Calls on the same caller
+// stream share its entry: they are ordered by that stream, and an event re-recorded by a
+// later call on it only makes an earlier call's wait more conservative.  Past
+// kMaxSideStreams caller streams per device, the shared experts run on the caller's stream.
+constexpr int kMaxSideStreams = 32;
+constexpr int kSideEvents = 3;   // fork, intermediate join, final join
 
-moe_status side_stream(hipStream_t* out) {
+struct SideEntry {
+  hipStream_t caller;
+  hipStream_t side;
+  hipEvent_t ev[kSideEvents];
+};
+
+std::mutex g_side_mu;
+SideEntry g_side[kMaxDevices][kMaxSideStreams];
+int g_side_n[kMaxDevices];
+
+// *out = the entry of (current device, caller), or null when the table is full.
+moe_status side_entry(hipStream_t caller, const SideEntry** out) {
+  *out = nullptr;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
   if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_side_mu);
-  if (g_side[dev] == nullptr) {
-    e = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking);
-    if (e != hipSuccess) {
-      g_side[dev] = nullptr;
-      return hip_status(e);
+  for (int i = 0; i < g_side_n[dev]; ++i) {
+    if (g_side[dev][i].caller == caller) {
+      *out = &g_side[dev][i];
+      return MOE_OK;
     }
   }
-  *out = g_side[dev];
+  if (g_side_n[dev] == kMaxSideStreams) return MOE_OK;
+  SideEntry ent{};
+  ent.caller = caller;
+  e = hipStreamCreateWithFlags(&ent.side, hipStreamNonBlocking);
+  for (int i = 0; e == hipSuccess && i < kSideEvents; ++i)
+    e = hipEventCreateWithFlags(&ent.ev[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    for (int i = 0; i < kSideEvents; ++i)
+      if (ent.ev[i] != nullptr) (void)hipEventDestroy(ent.ev[i]);
+    if (ent.side != nullptr) (void)hipStreamDestroy(ent.side);
+    return hip_status(e);
+  }
+  g_side[dev][g_side_n[dev]] = ent;
+  *out = &g_side[dev][g_side_n[dev]++];
   return MOE_OK;
 }
 
@@ -529,19 +558,15 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     // shared experts on a second stream from the start, where they overlap the routing,
     // unless the stages are being timed one by one (then, in decode, the routed and shared
     // experts stream their weights in one launch per stage)
-    const bool fork = shared && !events;
-    hipStream_t side = nullptr;
-    hipEvent_t fork_ev = nullptr, join = nullptr;
-    if (fork) {
-      st = side_stream(&side);
+    const SideEntry* side_ent = nullptr;
+    if (shared && !events) {
+      st = side_entry(stream, &side_ent);
       if (st != MOE_OK) return st;
-      hipError_t ce = hipEventCreateWithFlags(&fork_ev, hipEventDisableTiming);
-      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&join, hipEventDisableTiming);
-      if (ce != hipSuccess) {
-        if (fork_ev != nullptr) (void)hipEventDestroy(fork_ev);
-        return hip_status(ce);
-      }
     }
+    const bool fork = side_ent != nullptr;
+    hipStream_t side = fork ? side_ent->side : nullptr;
+    hipEvent_t fork_ev = fork ? side_ent->ev[0] : nullptr;
+    hipEvent_t join = fork ? side_ent->ev[2] : nullptr;
     moe::RouteParams rp = route_params(cfg);
     rp.select_bias = w->select_bias;
     if (pre) {
@@ -630,12 +655,6 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
                               shared ? at(cv.y_shared) : nullptr, cfg->residual ? x : nullptr,
                               out, stream);
     mark(7);
-    if (fork) {
-      // both events have been waited on or are pending in the streams: their resources
-      // are released once they complete
-      (void)hipEventDestroy(fork_ev);
-      (void)hipEventDestroy(join);
-    }
     return hip_status(e);
   } catch (...) {
     return MOE_ERR_INTERNAL;
@@ -716,21 +735,22 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     // its GEMMs overlap the routed ones, and its weight gradients, bound by the MFMAs,
     // share the CUs with the routed weight gradients, bound by their fp32 stores.  The main
     // stream waits for its dx rows before the combine and for all of it at the end.
-    hipStream_t side = stream;
-    hipEvent_t fork_ev = nullptr, dxs_ev = nullptr, join = nullptr;
+    const SideEntry* side_ent = nullptr;
     if (shared) {
-      st = side_stream(&side);
+      st = side_entry(stream, &side_ent);
       if (st != MOE_OK) return st;
-      hipError_t ce = hipEventCreateWithFlags(&fork_ev, hipEventDisableTiming);
-      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&dxs_ev, hipEventDisableTiming);
-      if (ce == hipSuccess) ce = hipEventCreateWithFlags(&join, hipEventDisableTiming);
-      if (ce != hipSuccess) {
-        for (hipEvent_t ev : {fork_ev, dxs_ev, join})
-          if (ev != nullptr) (void)hipEventDestroy(ev);
-        return hip_status(ce);
+    }
+    // without a side stream of its own (table full) the chain runs on the caller's stream
+    const bool fork = side_ent != nullptr;
+    hipStream_t side = fork ? side_ent->side : stream;
+    hipEvent_t fork_ev = fork ? side_ent->ev[0] : nullptr;
+    hipEvent_t dxs_ev = fork ? side_ent->ev[1] : nullptr;
+    hipEvent_t join = fork ? side_ent->ev[2] : nullptr;
+    if (shared) {
+      if (fork) {
+        e = hipEventRecord(fork_ev, stream);
+        if (ok()) e = hipStreamWaitEvent(side, fork_ev, 0);
       }
-      e = hipEventRecord(fork_ev, stream);
-      if (ok()) e = hipStreamWaitEvent(side, fork_ev, 0);
       // 1. the shared W2 stacked [S][d][I] is not one [d][S I] matrix: a transposed copy
       //    [S I][d] for its data gradient (the routed and the other weights are read as
       //    stored)
@@ -752,7 +772,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       dxs.K = nab * SI; dxs.kblock = nab * SI; dxs.w_down = w->sh_gate; dxs.w_up = w->sh_up;
       dxs.trb_split = SI; dxs.out = at(bc.dx_s);
       if (ok()) e = moe::launch_down_trb(dxs, cus, side);
-      if (ok()) e = hipEventRecord(dxs_ev, side);
+      if (fork && ok()) e = hipEventRecord(dxs_ev, side);
       // 7. weight gradients
       if (grads->d_sh_down != nullptr)
         wg(dout, d, 0, h_s, SI, 0, nullptr, 1, T, d, SI, I, grads->d_sh_down, side);
@@ -760,7 +780,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
         wg(at(bc.dab_s), nab * SI, 0, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_gate, side);
       if (swiglu && grads->d_sh_up != nullptr)
         wg(at(bc.dab_s), 2 * SI, SI, x, d, 0, nullptr, 1, T, SI, d, d, grads->d_sh_up, side);
-      if (ok()) e = hipEventRecord(join, side);
+      if (fork && ok()) e = hipEventRecord(join, side);
     }
     // 2. dh = (w dout) W2 (routed rows gathered from dout; W2 [E][d][I] is [K][N])
     moe::GemmParams g{};
@@ -792,7 +812,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     if (ok() && (grads->d_router != nullptr || grads->d_logit_bias != nullptr))
       e = moe::launch_router_wgrad(T, d, E, x, dl, grads->d_router, grads->d_logit_bias, at(bc.rg), stream);
     // 6. dx = dl W_r + experts (+ dout)
-    if (shared && ok()) e = hipStreamWaitEvent(stream, dxs_ev, 0);
+    if (fork && ok()) e = hipStreamWaitEvent(stream, dxs_ev, 0);
     if (ok())
       e = moe::launch_dx_combine(T, d, E, k, dl, w->router, at(bc.dxp_r), slot_pos,
                                  shared ? at(bc.dx_s) : nullptr, cfg->residual ? dout : nullptr,
@@ -814,13 +834,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
         wg(at(bc.dab_r), 2 * I, I, at(bc.x_perm), d, 0, offsets, E, Tk, I, d, d, grads->d_w_up,
            stream);
     }
-    if (shared) {
+    if (fork) {
       // also after an error: the side stream's work is ordered before what follows
       const hipError_t we = hipStreamWaitEvent(stream, join, 0);
       if (ok()) e = we;
-      // every event has been waited on or is pending in a stream: its resources are
-      // released once it completes
-      for (hipEvent_t ev : {fork_ev, dxs_ev, join}) (void)hipEventDestroy(ev);
     }
     return hip_status(e);
   } catch (...) {

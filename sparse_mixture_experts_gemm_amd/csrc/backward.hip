@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 
 // Gradient of each routing weight: dw[t, j] = dout[t] . y_hat[p], with y_hat = y[p] / w[t, j]
 // the expert's unweighted output (y is the forward's weighted output); 0 for dropped slots.
+// A selected expert whose weight is exactly 0 (its score underflowed to 0) gets dw = 0:
+// y_hat is then unknown, but dw only reaches the logits multiplied by that score (and the
+// score's own gradient by s (1 - s) or the softmax Jacobian, both 0 at s = 0), so 0 is exact.
 // One wave per slot, fixed-order sum.
 __global__ __launch_bounds__(256) void routing_weight_grad_kernel(
     int Tk, int k, int d, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y,
@@ -105,7 +108,10 @@ __global__ __launch_bounds__(256) void routing_weight_grad_kernel(
     }
   }
   acc = wave_sum_f(acc);
-  if (lane == 0) dw[q] = acc / topk_w[q];
+  if (lane == 0) {
+    const float wq = topk_w[q];
+    dw[q] = wq != 0.0f ? acc / wq : 0.0f;
+  }
 }
 
 // Logit gradients of one token per wave (lane = expert): the routing weights w_j = c s_j /

@@ -317,8 +317,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         const int lc = (lane % 32) ^ ((kr & 3) << 2);                    // logical chunk
         int n = tc.n_tile * BN + lc * 8;
         n = n < N ? n : 0;
-        src[i] = static_cast<const unsigned char*>(p.w_down) +
-                 ((size_t)tc.seg * p.trb_split * N + (size_t)kr * N + n) * 2;
+        // byte offset inside a 64-row block of the [K][N] matrix; the block's base
+        // (first or second matrix) is chosen per slice
+        src[i] = reinterpret_cast<const unsigned char*>(((size_t)kr * N + n) * 2);
       } else if (!is_b[i]) {
         const int row = q * (1024 / AROW) + lane / CPR_A;
         const int srow = gather ? s_arow[j & 1][row] : seg_row(tc, row);
@@ -365,21 +366,23 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
     const uint32_t st = lds_base + (uint32_t)(ist * ST_BYTES);
     const size_t aoff = (size_t)k0 * ESZ_A;
     const size_t koff = (size_t)(k0 / p.kblock) * N * p.kblock + (k0 % p.kblock);
-    ptrdiff_t boff = FP8 ? koff : koff * 2;
+    const size_t boff = FP8 ? koff : koff * 2;
+    // TRB: rows k0 .. of the segment's first matrix, or (k0 >= trb_split) of its second one
+    const unsigned char* tbase = nullptr;
     if (TRB) {
-      // rows k0 .. of the first matrix, or (k0 >= trb_split) of the second one
-      const ptrdiff_t nb = (ptrdiff_t)N * 2;
-      if (k0 < p.trb_split) {
-        boff = (ptrdiff_t)k0 * nb;
-      } else {
-        boff = (static_cast<const unsigned char*>(p.w_up) - static_cast<const unsigned char*>(p.w_down)) +
-               ((ptrdiff_t)src_seg * (K - 2 * p.trb_split) + (k0 - p.trb_split)) * nb;
-      }
+      const size_t nb = (size_t)N * 2;
+      const int ks = K - p.trb_split;   // rows of the second matrix per segment
+      tbase = k0 < p.trb_split
+                  ? static_cast<const unsigned char*>(p.w_down) + ((size_t)src_seg * p.trb_split + k0) * nb
+                  : static_cast<const unsigned char*>(p.w_up) +
+                        ((size_t)src_seg * ks + (k0 - p.trb_split)) * nb;
     }
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
-      dma16(st + (uint32_t)(q * 1024), src[i] + (is_b[i] ? boff : aoff));
+      const unsigned char* a = (TRB && is_b[i]) ? tbase + reinterpret_cast<size_t>(src[i])
+                                                : src[i] + (is_b[i] ? boff : aoff);
+      dma16(st + (uint32_t)(q * 1024), a);
     }
     ++ikt;
     ist = ist + 1 == NSTAGE ? 0 : ist + 1;
@@ -828,23 +831,13 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 // tiles even for routed segments of ~400 rows, where a third of the last m-tile is
 // padding: the larger tile halves the L2 and LDS traffic per MFMA), else 128 x 256.
 // Each configuration is (BM, BN, waves, LDS stages, workgroups per CU).
-#ifndef MOE_CFG_NARROW_UP
 #define MOE_CFG_NARROW_UP 128, 256, 8, 3, 1
-#endif
-#ifndef MOE_CFG_NARROW_DOWN
 #define MOE_CFG_NARROW_DOWN 128, 256, 8, 3, 1
-#endif
-#ifndef MOE_CFG_WIDE
 #define MOE_CFG_WIDE 256, 256, 8, 2, 1
-#endif
 
 // e4m3 activations: 128-byte slices of 128 K values (two MFMA steps), the bf16 ring depths
-#ifndef MOE_CFG_NARROW_A8
 #define MOE_CFG_NARROW_A8 128, 256, 8, 3, 1
-#endif
-#ifndef MOE_CFG_WIDE_A8
 #define MOE_CFG_WIDE_A8 256, 256, 8, 2, 1
-#endif
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
           bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>

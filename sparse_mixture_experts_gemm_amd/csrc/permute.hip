@@ -114,7 +114,10 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int ca
     if (ok) {
       for (int j = 0; j < k; ++j) {
         const int e = idx[(size_t)t * k + j];
-        if ((unsigned)e >= (unsigned)E) continue;
+        if ((unsigned)e >= (unsigned)E) {   // skipped id: no row, like a dropped slot
+          slot_pos[(size_t)t * k + j] = -1;
+          continue;
+        }
         const int rank = run[e] + __popcll(mask[e] & below);
         if (rank < capacity) {
           const int pos = koff[e] + rank;

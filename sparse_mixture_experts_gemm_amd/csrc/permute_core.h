@@ -94,7 +94,10 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, c
       for (int j = 0; j < 8; ++j) {
         if (j >= k) break;
         const int e = sidx[t * k + j];
-        if ((unsigned)e >= (unsigned)E) continue;
+        if ((unsigned)e >= (unsigned)E) {   // skipped id: no row, like a dropped slot
+          slot_pos[(size_t)t * k + j] = -1;
+          continue;
+        }
         const int rank = pl.run[wave][e] + __popcll(pl.mask[wave][e] & below);
         if (rank < capacity) {
           const int pos = pl.koff[e] + rank;

@@ -96,6 +96,35 @@ def test_backward_matches_oracle(name):
         assert diff <= TOL * scale, field
 
 
+def test_backward_with_a_selected_expert_of_zero_weight():
+    """Expert 3's logit is offset by -200, so its fp32 sigmoid score (and weight) is exactly
+    0, and a selection-only bias of +1000 makes every token pick it anyway.  The exact
+    gradient is finite (that weight's gradient enters the logits only multiplied by the
+    score); every gradient must match the fp64 oracle, whose score is ~1e-87, not 0."""
+    s = W.small_shape(T=200, d=256, E=16, k=4, G=1, Gk=1, S=1, I=128, select_bias_std=0.5,
+                      seed=69)
+    lay = W.make_layer(s, cache=False)
+    lay.logit_bias = np.zeros(s.E, np.float32)
+    lay.logit_bias[3] = -200.0
+    lay.select_bias = lay.select_bias.copy()
+    lay.select_bias[3] = 1000.0
+    cfg, wts, ws, x, dout, dout_np, grads, bws, gpu_idx = run_backward(s, lay)
+    assert (gpu_idx == 3).any(axis=1).all()
+    off = (s.T * s.k * 4 + 255) // 256 * 256        # topk_w follows topk_idx in the workspace
+    tw = ws[off: off + s.T * s.k * 4].view(torch.float32).cpu().numpy().reshape(s.T, s.k)
+    assert np.all(tw[gpu_idx == 3] == 0.0)
+    idx = checked_selection(s, lay, gpu_idx)
+    ref = O.backward.moe_backward(lay, O.decode_bf16(dout_np), idx=idx)
+    for field, t in grads.items():
+        want = ref[NAMES[field]]
+        got = act_to_f64(t, "bf16") if field == "dx" else t.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), field
+        scale = np.max(np.abs(want))
+        diff = np.max(np.abs(got - want))
+        print(f"zero-weight {field}: max|d|/max|ref| = {diff / scale:.3e}")
+        assert diff <= TOL * scale, field
+
+
 def test_backward_is_deterministic_and_untouched_experts_get_zero():
     s = W.small_shape(T=12, d=128, E=32, k=2, G=1, Gk=1, S=1, I=64, seed=67)
     lay = W.make_layer(s, cache=False)

@@ -1,13 +1,17 @@
 """GPU parity of every libmoe entry point against the fp64 CPU oracle.
 
-All inputs come from the seeded generator (workloads) or from the oracle; nothing the GPU
-computes is fed to the oracle.  Bars:
+All inputs come from the seeded generator (workloads) or from the oracle; the only GPU
+values handed to the oracle are the fp32 router scores and the selected experts, and
+only after the parity protocol has checked them.  Bars:
 * selection (moe_select on shared fp32 scores) and permutation: bit-exact;
-* routing by moe_route: GPU scores within 1e-5 of the oracle's fp64 scores; indices
-  identical for every token whose fp64 decision margins exceed 1e-5 (a smaller margin is
-  below the fp32 score error, so either choice is correct: those tokens are checked for
-  validity instead and kept out of output comparisons when their selection differs);
-* float outputs: max|delta| <= 2e-2 max|ref| (bf16) and <= 1e-4 max|ref| (fp32).
+* routing by moe_route: GPU scores within 1e-5 of the oracle's fp64 scores, and the
+  oracle's selection applied to the GPU's own fp32 scores equal to the GPU's indices for
+  every token, bit for bit; against the free-running fp64 oracle the indices are
+  identical wherever the fp64 decision margin exceeds 1e-5 (a smaller margin is below
+  the fp32 score error, so either choice is correct: those tokens are checked for
+  validity instead);
+* float outputs: every row, max|delta| <= 2e-2 max|ref| (bf16) and <= 1e-4 max|ref|
+  (fp32), against the oracle run under the GPU's checked routing.
 """
 import numpy as np
 import pytest
@@ -238,6 +242,15 @@ ROUTE_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
 def test_route_matches_oracle(name):
+    """The routing protocol on moe_route's own output:
+    (1) its fp32 scores against the oracle's fp64 scores;
+    (2) the oracle's selection applied to those fp32 scores equals the GPU's indices for
+        every token, bit for bit (cases without a selection bias, whose keys the kernel
+        does not export), and the weights are the renormalised GPU scores within one ulp
+        of their fp32 value;
+    (3) against the free-running fp64 oracle: identical indices wherever the fp64 decision
+        margin exceeds the fp32 score error; closer tokens must still be a valid top-k
+        within that margin (informational count printed)."""
     s = shape_of(name)
     lay = layer_of(name)
     cfg = config(s)
@@ -249,18 +262,37 @@ def test_route_matches_oracle(name):
               to_dev(lay.select_bias), scores, idx, w)
     torch.cuda.synchronize()
     r = O.route(lay)
-    g_sc = scores.cpu().numpy().astype(np.float64)
+    sc32 = scores.cpu().numpy()
+    g_sc = sc32.astype(np.float64)
     assert np.max(np.abs(g_sc - r["scores"])) <= 1e-5
     g_idx = idx.cpu().numpy()
+    g_w = w.cpu().numpy()
+    if lay.select_bias is None:
+        own = O.select_experts(sc32, s.k, s.G, s.Gk, s.n_g)
+        bad = np.nonzero((own != g_idx).any(axis=1))[0]
+        assert bad.size == 0, f"{bad.size} tokens differ from the oracle's selection on the GPU scores, first {bad[:8]}"
+        # renormalisation in fp32 steps: the k selected scores summed in slot order, one
+        # division, one product with route_scale
+        sel = np.take_along_axis(sc32, g_idx.astype(np.int64), axis=1)
+        tot = np.zeros(T, np.float32)
+        for j in range(s.k):
+            tot = (tot + sel[:, j]).astype(np.float32)
+        ref_w = (sel / tot[:, None]).astype(np.float32) if s.renormalize else sel
+        ref_w = (ref_w * np.float32(s.route_scale)).astype(np.float32).astype(np.float64)
+        ulp = np.spacing(np.abs(ref_w).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(g_w.astype(np.float64) - ref_w) <= ulp), \
+            np.max(np.abs(g_w.astype(np.float64) - ref_w) / ulp)
     mar = margins(r["keys"], s)
     clear = mar > MARGIN
     assert np.array_equal(g_idx[clear], r["idx"][clear])
     # near-tie tokens: the GPU's pick must still be a valid top-k within the margin
     for t in np.nonzero(~clear)[0]:
         assert valid_within_margin(g_idx[t], r["keys"][t], s), (t, g_idx[t], r["idx"][t])
-    assert (~clear).sum() <= max(4, T // 200)
+    differ = int((g_idx != r["idx"]).any(axis=1).sum())
+    print(f"{name}: {differ} of {T} tokens route differently from the free-running fp64 "
+          f"oracle ({int((~clear).sum())} within the fp32 margin)")
     same = (g_idx == r["idx"]).all(axis=1)
-    assert np.allclose(w.cpu().numpy()[same], r["w"][same], rtol=1e-5, atol=1e-6)
+    assert np.allclose(g_w[same], r["w"][same], rtol=1e-5, atol=1e-6)
 
 
 # ----------------------------------------------------------------------------- pre-norm routing
@@ -417,6 +449,46 @@ def test_permute_edge_cases(T, E, k, pattern):
         idx = np.tile(np.arange(k, dtype=np.int32)[::-1], (T, 1))
     w = rng.random((T, k)).astype(np.float32)
     _check_permute(T, E, k, idx, w)
+
+
+@pytest.mark.parametrize("T", [300, 3000])
+def test_permute_skips_out_of_range_ids_and_combine_ignores_them(T):
+    """Padding ids (-1 and E) in topk_idx get no row and slot_pos -1, on the one-launch
+    (T <= 1024) and the two-launch path; the expected maps come from Python's sorted() of
+    the valid (expert, token, slot) triples.  moe_combine then sums only the valid slots."""
+    E, k, d = 16, 4, 64
+    rng = np.random.default_rng(T + 7)
+    idx = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    pad = rng.random((T, k)) < 0.2
+    idx[pad] = np.where(rng.random(int(pad.sum())) < 0.5, -1, E).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    cfg = moe.make_config(T, d, E, k, I=64)
+    ws = workspace(cfg)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pt = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    sp = torch.full((T * k,), 12345, dtype=torch.int32, device="cuda")
+    pw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    moe.permute(cfg, to_dev(idx), to_dev(w), counts, offsets, pt, sp, pw, ws)
+    torch.cuda.synchronize()
+    triples = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k) if 0 <= idx[t, j] < E)
+    exp_sp = np.full(T * k, -1, np.int32)
+    for p, (_, t, j) in enumerate(triples):
+        exp_sp[t * k + j] = p
+    exp_counts = np.array([sum(1 for q in triples if q[0] == e) for e in range(E)], np.int32)
+    rows = len(triples)
+    assert np.array_equal(counts.cpu().numpy(), exp_counts)
+    assert np.array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(exp_counts)]))
+    assert np.array_equal(pt.cpu().numpy()[:rows], np.array([t for (_, t, _) in triples], np.int32))
+    assert np.array_equal(sp.cpu().numpy(), exp_sp)
+    assert np.array_equal(pw.cpu().numpy()[:rows], np.array([w[t, j] for (_, t, j) in triples], np.float32))
+    y = W.random_act((T * k, d), seed=81, dtype="bf16")
+    out = act_empty((T, d), "bf16")
+    moe.combine(cfg, to_dev(y), sp, None, out)
+    torch.cuda.synchronize()
+    ref = O.combine(O.decode_act(y, "bf16"), exp_sp, None, k)
+    got = act_to_f64(out, "bf16")
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
 
 
 # ----------------------------------------------------------------------------- grouped GEMMs
@@ -660,32 +732,37 @@ def run_forward(name):
     return s, lay, cfg, wts, ws, x, out, gpu_idx
 
 
+def check_forward_routing(s, lay, gpu_idx, x=None, margin=MARGIN):
+    """The forward's routing against the free-running oracle: every token identical as a
+    set of experts, except near ties (fp64 margin below ``margin``), which must still be a
+    valid top-k within it.  Returns the number of tokens routed differently."""
+    full = O.route(lay, x=x)
+    mar = margins(full["keys"], s)
+    same = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, full["idx"])])
+    assert np.all(same | (mar <= margin)), "routing differs away from a near tie"
+    if margin == MARGIN:
+        for t in np.nonzero(~same)[0]:
+            assert valid_within_margin(gpu_idx[t], full["keys"][t], s)
+    return int((~same).sum())
+
+
 @pytest.mark.parametrize("name", FORWARD_CASES)
 def test_forward_matches_oracle(name):
+    """Every output row of the forward against the oracle forward run under the GPU's
+    checked routing (parity protocol step 4; with a capacity this is the only comparison
+    possible, since dropped slots depend on the whole batch's routing)."""
     s, lay, cfg, wts, ws, x, out, gpu_idx = run_forward(name)
-    rows = sample_tokens(s.T, n=128, seed=4)
+    differ = check_forward_routing(s, lay, gpu_idx)
+    ref = O.moe_forward(lay, idx=gpu_idx)
     if s.capacity_factor is not None:
-        # which slots a capacity drops depends on the whole batch's routing: check the GPU
-        # routing of every token against the oracle, then compare the outputs under it
-        full = O.route(lay)
-        mar_all = margins(full["keys"], s)
-        same_all = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, full["idx"])])
-        assert np.all(same_all | (mar_all <= MARGIN)), "routing differs away from a near tie"
-        for t in np.nonzero(~same_all)[0]:
-            assert valid_within_margin(gpu_idx[t], full["keys"][t], s)
-        ref = O.moe_forward(lay, tokens=rows, idx=gpu_idx)
-        same = np.ones(len(rows), dtype=bool)
         assert (~ref["kept"]).any() or s.capacity_factor >= 1.0
-    else:
-        ref = O.moe_forward(lay, tokens=rows)
-        same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
-        mar = margins(ref["keys"], s)
-        assert np.all(same | (mar <= MARGIN)), "routing differs away from a near tie"
-    got = act_to_f64(out, s.act_dtype)[rows]
-    diff = np.max(np.abs(got[same] - ref["out"][same]))
-    scale = np.max(np.abs(ref["out"][same]))
-    print(f"{name}: max|d|/max|ref| = {diff / scale:.3e} over {same.sum()} rows")
-    assert diff <= TOL[s.act_dtype] * scale
+    got = act_to_f64(out, s.act_dtype)
+    err = np.abs(got - ref["out"]).max(axis=1)
+    scale = np.max(np.abs(ref["out"]))
+    print(f"{name}: max|d|/max|ref| = {err.max() / scale:.3e} over all {s.T} rows "
+          f"({differ} near-tie tokens routed differently from the free-running oracle)")
+    bad = np.nonzero(err > TOL[s.act_dtype] * scale)[0]
+    assert bad.size == 0, f"{bad.size} rows off, first {bad[:8]}"
 
 
 PRENORM_FORWARD_CASES = PRENORM_CASES + ["small_prenorm_a8"]
@@ -694,9 +771,9 @@ PRENORM_FORWARD_CASES = PRENORM_CASES + ["small_prenorm_a8"]
 @pytest.mark.parametrize("name", PRENORM_FORWARD_CASES)
 def test_forward_prenorm_matches_oracle(name):
     """The pre-norm layer step: routing identical to moe_rmsnorm_route on the same input,
-    the oracle's own routing except at near ties of the pre-norm step, and the output of
-    every agreeing sampled row within TOL * max|MoE part| + half an ulp of the output (the
-    final rounding of a sum that includes the residual x)."""
+    the oracle's own routing except at near ties of the pre-norm step, and every output row
+    (against the oracle run under the GPU's checked routing) within TOL * max|MoE part| +
+    half an ulp of the output (the final rounding of a sum that includes the residual x)."""
     s, lay, cfg, wts, ws, x, out, gpu_idx = run_forward(name)
     idx = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
     w = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
@@ -705,25 +782,16 @@ def test_forward_prenorm_matches_oracle(name):
                       to_dev(lay.select_bias), x_norm, None, idx, w)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), gpu_idx)
-    rows = sample_tokens(s.T, n=128, seed=5)
-    if s.capacity_factor is not None:
-        full = O.route(lay, x=O.normalized_input(lay))
-        same_all = np.array([set(a.tolist()) == set(b.tolist()) for a, b in zip(gpu_idx, full["idx"])])
-        assert np.all(same_all | (margins(full["keys"], s) <= PRENORM_MARGIN))
-        ref = O.moe_forward(lay, tokens=rows, idx=gpu_idx)
-        same = np.ones(len(rows), dtype=bool)
-    else:
-        ref = O.moe_forward(lay, tokens=rows)
-        same = np.array([set(gpu_idx[t].tolist()) == set(ref["idx"][i].tolist()) for i, t in enumerate(rows)])
-        assert np.all(same | (margins(ref["keys"], s) <= PRENORM_MARGIN))
-    got = act_to_f64(out, s.act_dtype)[rows]
-    xr = O.decode_act(lay.x[rows], s.act_dtype)
+    check_forward_routing(s, lay, gpu_idx, x=O.normalized_input(lay), margin=PRENORM_MARGIN)
+    ref = O.moe_forward(lay, idx=gpu_idx)
+    got = act_to_f64(out, s.act_dtype)
+    xr = O.decode_act(lay.x, s.act_dtype)
     moe_part = ref["out"] - (xr if s.residual else 0.0)
-    scale = np.max(np.abs(moe_part[same]))
+    scale = np.max(np.abs(moe_part))
     bound = TOL[s.act_dtype] * scale + 0.5 * _ulp(np.maximum(np.abs(got), np.abs(ref["out"])), s.act_dtype)
-    err = np.abs(got - ref["out"])[same]
-    print(f"{name}: max|d|/max|moe part| = {np.max(err) / scale:.3e} over {same.sum()} rows")
-    assert np.all(err <= bound[same])
+    err = np.abs(got - ref["out"])
+    print(f"{name}: max|d|/max|moe part| = {np.max(err) / scale:.3e} over all {s.T} rows")
+    assert np.all(err <= bound)
 
 
 @pytest.mark.parametrize("name", ["balance_bf16", "small_f32"])

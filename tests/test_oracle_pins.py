@@ -386,6 +386,70 @@ def test_permute_empty_experts_and_single_token():
     assert perm_token.tolist() == [0, 0] and slot_pos.tolist() == [1, 0]
 
 
+# ----------------------------------------------------------------------------- combine
+def _combine_case(with_shared, drop):
+    """Per-slot values v[t, j] (distinct powers-of-two sums, exact in fp64) laid out in
+    expert-major order by Python's sorted() of (expert, token, slot), optionally with a
+    capacity of one row per expert (later slots of an expert dropped, slot_pos -1), and
+    the expected per-token result written out with pure-Python loops."""
+    T, k, E, d = 7, 3, 5, 4
+    rng = np.random.default_rng(91)
+    idx = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    v = {(t, j): [float(2 ** (t + 8 * j)) + c / 8.0 for c in range(d)] for t in range(T) for j in range(k)}
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k))
+    seen, rows, slot_pos = {}, [], [-1] * (T * k)
+    for e, t, j in pairs:
+        seen[e] = seen.get(e, 0) + 1
+        if drop and seen[e] > 1:
+            continue
+        slot_pos[t * k + j] = len(rows)
+        rows.append(v[(t, j)])
+    # a row that no slot points at: picking it up (e.g. through index -1) shows
+    rows.append([1e6] * d)
+    y_perm = np.array(rows, dtype=np.float64)
+    y_sh = np.array([[float(-(c + 1) * (t + 1)) for c in range(d)] for t in range(T)]) if with_shared else None
+    expect = []
+    for t in range(T):
+        acc = [0.0] * d
+        for j in range(k):
+            if slot_pos[t * k + j] < 0:
+                continue
+            acc = [a + b for a, b in zip(acc, v[(t, j)])]
+        if with_shared:
+            acc = [a + b for a, b in zip(acc, y_sh[t].tolist())]
+        expect.append(acc)
+    return y_perm, np.array(slot_pos, np.int32), y_sh, k, np.array(expect), drop
+
+
+@pytest.mark.parametrize("with_shared,drop", [(True, False), (False, False), (True, True), (False, True)])
+def test_combine_brute_force(with_shared, drop):
+    """out[t] = sum of the kept slots' expert outputs + the shared row: per-token loops
+    over (token, slot) pairs laid out by sorted(), with dropped slots skipped."""
+    y_perm, slot_pos, y_sh, k, expect, drop = _combine_case(with_shared, drop)
+    assert (slot_pos < 0).any() == drop
+    got = O.combine(y_perm, slot_pos, y_sh, k)
+    assert np.array_equal(got, expect)
+
+
+def test_combine_inverts_the_permutation_of_the_oracle():
+    """Round trip: rows laid out by O.permute (itself pinned by sorted()) and summed back by
+    O.combine give each token the sum of its own k values, with or without a capacity."""
+    rng = np.random.default_rng(92)
+    T, E, k, d = 50, 8, 3, 5
+    idx = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    vals = rng.standard_normal((T, k, d))
+    for cap in (None, 10):
+        _, offsets, perm_token, slot_pos = O.permute(idx, E, cap)
+        kept = (slot_pos >= 0).reshape(T, k)
+        y = np.zeros((int(offsets[-1]), d))
+        flat = vals.reshape(T * k, d)
+        y[slot_pos[slot_pos >= 0]] = flat[slot_pos >= 0]
+        got = O.combine(y, slot_pos, None, k)
+        want = np.array([sum((vals[t, j] for j in range(k) if kept[t, j]), np.zeros(d)) for t in range(T)])
+        assert np.allclose(got, want, rtol=1e-14, atol=1e-14)
+        assert cap is None or (~kept).any()
+
+
 # ----------------------------------------------------------------------------- selection bias
 def _with_bias(lay, b):
     lay.select_bias = None if b is None else np.asarray(b, np.float32)
@@ -763,7 +827,8 @@ def _swapped_ffn(x, w1, w3, w2, act):
                                       "biased_weights", "keep_last_at_capacity",
                                       "truncating_quantiser", "layernorm_centering",
                                       "eps_outside_root", "sum_not_mean", "no_residual",
-                                      "double_rounding"])
+                                      "double_rounding", "combine_no_shared",
+                                      "combine_dropped_as_last_row", "combine_slot_major"])
 def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
     """Each mutation is a plausible slip in the oracle; the named pin must then fail."""
     if mutation == "swap_gate_up":
@@ -872,5 +937,25 @@ def test_planted_oracle_mistakes_are_caught(monkeypatch, mutation):
             return h @ w2[:, ::-1].T                      # wrong column order of W2
         monkeypatch.setattr(O.moe_oracle, "expert_ffn", bad_ffn)
         check = test_single_expert_equals_dense_swiglu_ffn
+    elif mutation == "combine_no_shared":
+        orig = O.moe_oracle.combine
+        monkeypatch.setattr(O, "combine", lambda y, sp, ysh, k: orig(y, sp, None, k))
+        check = lambda: test_combine_brute_force(True, False)
+    elif mutation == "combine_dropped_as_last_row":
+        # a dropped slot (-1) gathers the last row instead of being skipped
+        def bad(y, sp, ysh, k):
+            y = np.asarray(y, np.float64)
+            out = y[np.asarray(sp, np.int64).reshape(-1, k)].sum(axis=1)
+            return out if ysh is None else out + np.asarray(ysh, np.float64)
+        monkeypatch.setattr(O, "combine", bad)
+        check = lambda: test_combine_brute_force(False, True)
+    elif mutation == "combine_slot_major":
+        # slot_pos read as [k, T] instead of [T, k]
+        orig = O.moe_oracle.combine
+        def bad(y, sp, ysh, k):
+            sp = np.asarray(sp).reshape(k, -1).T.reshape(-1)
+            return orig(y, sp, ysh, k)
+        monkeypatch.setattr(O, "combine", bad)
+        check = test_combine_inverts_the_permutation_of_the_oracle
     with pytest.raises(AssertionError):
         check()
