@@ -287,17 +287,6 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(
 // 16-column group, and two loads (rows 0-3, 4-7) give each lane its 8 rows.  16-byte chunks
 // are XOR-swizzled by 4 (row & 3), which puts the four rows read together in different bank
 // windows.  Rows past the segment's end and columns past M or N read a zero row.
-__device__ __forceinline__ void dma16_wg(uint32_t lds_base, const void* src) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds_base), "v"(src)
-      : "memory");
-}
 
 constexpr int kWgBK = 64;
 __device__ const uint16_t kZeroRow[256] = {};   // source of rows and columns out of range
@@ -354,7 +343,7 @@ __global__ __launch_bounds__(WAVES * 64) void wgrad_kernel(WgradParams p) {
       const bool ok = rr < nrows && dcol_ok[i];
       const size_t ld = dis_b[i] ? (size_t)p.ldb : (size_t)p.lda;
       const uint16_t* src = ok ? dbase[i] + (size_t)(r0 + rr) * ld : kZeroRow;
-      dma16_wg(st + (uint32_t)((wave * NDMA + i) * 1024), src);
+      lds_dma16(st + (uint32_t)((wave * NDMA + i) * 1024), src);
     }
   };
   // transposing operand load: 8 rows (k) of column base + (lane % 32) in two halves

@@ -105,6 +105,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (the LDS base is
+// taken from M0; no VGPR is written).  The caller waits with vmcnt before reading the LDS.
+// An LDS-DMA load that reads M0 needs one wait state after the scalar write of M0 (a gfx9
+// hazard that the compiler cannot see inside inline assembly): the s_nop provides it.  M0
+// is restored afterwards.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* src) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(src)
+      : "memory");
+}
+
 // Logical workgroup -> XCD-contiguous order.  Workgroups are dispatched round-robin over
 // the 8 XCDs (workgroup b runs on XCD b % 8), so map workgroup b to a slot such that each
 // XCD walks a contiguous range of logical tiles and its L2 sees their shared operands.

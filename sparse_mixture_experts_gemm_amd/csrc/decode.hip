@@ -31,19 +31,6 @@ constexpr int kLdsMaxK = 2048;        // activation rows staged in LDS up to thi
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane (no VGPR written).
-__device__ __forceinline__ void dma16_dec(uint32_t lds_base, const void* src) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds_base), "v"(src)
-      : "memory");
-}
-
 __device__ __forceinline__ void widen16(uint4 q, bf16x8& lo, bf16x8& hi) {
   bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
   bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
@@ -188,7 +175,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void dec_gemm_kernel(DecSet first, 
         int srow = row0 + m;
         if (p.row_index != nullptr) srow = p.row_index[srow];
         const uint16_t* src = a_base + (size_t)srow * K + (size_t)(blk * 64 + (lane ^ (m & 15))) * 8;
-        dma16_dec((uint32_t)__builtin_amdgcn_readfirstlane((int)(a_lds_base + (uint32_t)(m * K * 2 + blk * 1024))),
+        lds_dma16((uint32_t)__builtin_amdgcn_readfirstlane((int)(a_lds_base + (uint32_t)(m * K * 2 + blk * 1024))),
                   src);
       }
     }

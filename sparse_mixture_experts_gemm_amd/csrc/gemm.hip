@@ -30,72 +30,15 @@
 // tile are in flight while the current tile's epilogue runs.  Within a slice, scheduling
 // directives place the LDS reads of the next K-step between the MFMAs of the current one.
 #include "common.h"
+#include "gemm_core.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace moe {
 
 namespace {
 
-constexpr int kGroupM = 8;   // m-tiles walked together per n-tile inside a large segment
-
-// Builds, in LDS, the first tile index of every segment and its row range.  Run by
-// wave 0; nseg <= 64.
-__device__ void build_schedule(const GemmParams& p, int BM, int NT, int* s_tile0, int* s_row0,
-                               int* s_rows) {
-  const int lane = threadIdx.x;
-  if (lane < 64) {
-    int row0 = 0, rows = 0, tiles = 0;
-    if (lane < p.nseg) {
-      if (p.offsets != nullptr) {
-        row0 = p.offsets[lane];
-        rows = p.offsets[lane + 1] - row0;
-      } else {
-        row0 = 0;
-        rows = p.rows;
-      }
-      tiles = ((rows + BM - 1) / BM) * NT;
-    }
-    int incl = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane < p.nseg) {
-      s_tile0[lane + 1] = incl;
-      s_row0[lane] = row0;
-      s_rows[lane] = rows;
-    }
-    if (lane == 0) s_tile0[0] = 0;
-  }
-}
-
-struct TileCoord {
-  int seg, m_tile, n_tile, row0, rows;
-};
-
-__device__ __forceinline__ TileCoord decode_tile(int L, int nseg, int BM, int NT,
-                                                 const int* s_tile0, const int* s_row0,
-                                                 const int* s_rows) {
-  int lo = 0, hi = nseg - 1;  // last segment with s_tile0[seg] <= L
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_tile0[mid] <= L) lo = mid; else hi = mid - 1;
-  }
-  TileCoord c;
-  c.seg = lo;
-  c.row0 = s_row0[lo];
-  c.rows = s_rows[lo];
-  const int u = L - s_tile0[lo];
-  const int mt = (c.rows + BM - 1) / BM;
-  const int grp = u / (kGroupM * NT);
-  const int first_m = grp * kGroupM;
-  const int gm = min(kGroupM, mt - first_m);
-  const int r = u - grp * kGroupM * NT;
-  c.m_tile = first_m + r % gm;
-  c.n_tile = r / gm;
-  return c;
-}
 
 // ------------------------------------------------------------------------------------
 // bf16 activations, bf16 or e4m3 weights, MFMA 32x32x16.
@@ -120,68 +63,12 @@ __device__ __forceinline__ TileCoord decode_tile(int L, int nseg, int BM, int NT
 // (column) l % 32 and MFMA row 8 * (i / 4) + 4 * (l / 32) + i % 4.  LDS row r of a 32-row
 // weight block holds weight row perm32(r) of the block, which makes that element feature
 // 16 * (l / 32) + i: a lane's 16 values are consecutive features of one token.
-__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
-__device__ __forceinline__ int perm32(int r) { return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3); }
-
-// 16 bytes per lane from global memory into LDS at lds_base + 16 * lane.  No VGPR is
-// written; the caller waits with vmcnt before reading the LDS.
-__device__ __forceinline__ void dma16(uint32_t lds_base, const void* src) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds_base), "v"(src)
-      : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] = 7 | lgkmcnt[11:8] = 15 | vmcnt[5:4] << 14
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x8 widen_e4m3x8(uint2 q) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// 16 consecutive fp32 values (scaled by the per-feature factors when given) -> 16 bf16 at
-// dst (32-byte aligned), as two 16-byte stores.
-__device__ __forceinline__ void store16_bf16(void* dst, const float (&v)[16]) {
-  uint4 lo, hi;
-  lo.x = pack_bf16x2(v[0], v[1]);   lo.y = pack_bf16x2(v[2], v[3]);
-  lo.z = pack_bf16x2(v[4], v[5]);   lo.w = pack_bf16x2(v[6], v[7]);
-  hi.x = pack_bf16x2(v[8], v[9]);   hi.y = pack_bf16x2(v[10], v[11]);
-  hi.z = pack_bf16x2(v[12], v[13]); hi.w = pack_bf16x2(v[14], v[15]);
-  uint4* d = static_cast<uint4*>(dst);
-  d[0] = lo;
-  d[1] = hi;
-}
-
-__device__ __forceinline__ void load16_f32(const float* src, float (&v)[16]) {
-  const float4* s4 = reinterpret_cast<const float4*>(src);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 t = s4[q];
-    v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-  }
-}
 
 // Tile shapes: 256 x 256 when the problem gives every CU at least two such tiles, else
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   // K values per slice: 64 (128-byte bf16 rows), or 128 e4m3 bytes with e4m3 activations
@@ -218,6 +105,12 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   auto swz_a = [](int r) { return swz8(r); };                        // A rows (128 bytes)
   auto swz_b8 = [](int r) { return swz4(r); };                       // 64-byte e4m3 B rows
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
+  // SPLIT: the two wave rows queue their loads of the next slice at different times, the
+  // first row before its MFMAs, the second half-way through them, so that on every SIMD one
+  // wave multiplies while the other waits for the address unit to take its loads.  Loads
+  // are then queued outside the barrier-synchronised points, so the path that stages
+  // gathered rows with a barrier (short K on a deeper ring) must not be taken.
+  static_assert(!SPLIT || (NSTAGE == 2 && !A8), "staggered loads: 2-stage ring, bf16 activations");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
 
   __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
@@ -382,7 +275,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       const int q = wave * NDMA + i;
       const unsigned char* a = (TRB && is_b[i]) ? tbase + reinterpret_cast<size_t>(src[i])
                                                 : src[i] + (is_b[i] ? boff : aoff);
-      dma16(st + (uint32_t)(q * 1024), a);
+      lds_dma16(st + (uint32_t)(q * 1024), a);
     }
     ++ikt;
     ist = ist + 1 == NSTAGE ? 0 : ist + 1;
@@ -426,8 +319,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   int wave_rows = rows_of_wave(tc);
   int j = 0, kt = 0, cst = 0;      // tile, k-slice and ring stage being multiplied
   int j3 = 0;                      // j mod 3
+  const bool late_loads = SPLIT && wm == 1;   // this wave queues its loads half-way
   for (int g = 0; g < nslices; ++g) {
-    if (g + NSTAGE - 1 < nslices) issue_next();
+    if (g + NSTAGE - 1 < nslices && !late_loads) issue_next();
     if (FOLD && kt > 0 && ((kt * BK) % p.kblock) == 0) {
       // the next K block belongs to another shared expert: fold the finished block
       // with its per-channel scales
@@ -532,27 +426,28 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         }
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
       }
-    } else if (wave_rows > 0) {
-      load_frags(0, af[0], bfr[0]);
-      __builtin_amdgcn_s_setprio(1);
+    } else {
+      // K-steps [k0, k1) of the slice: the LDS reads of step ks + 1 run behind the MFMAs of
+      // step ks, placed one by one between them by scheduling directives (left to itself
+      // the compiler issues some of them just before their first use)
+      auto mfma_steps = [&](auto k0_tag, auto k1_tag) {
+        constexpr int K0 = decltype(k0_tag)::value, K1 = decltype(k1_tag)::value;
+        if (K0 == 0) load_frags(0, af[0], bfr[0]);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+        for (int ks = K0; ks < K1; ++ks) {
+          if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
-                                                                  acc[fm][fn], 0, 0, 0);
-      }
-      {
-        // instruction order for the scheduler: the LDS reads of K-step ks + 1 interleaved
-        // one by one with the MFMAs of step ks, so that they land while it multiplies
-        // (left to itself it issues some of them just before their first use)
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
+                                                                    acc[fm][fn], 0, 0, 0);
+        }
         constexpr int NDS = FM + (TRB ? 2 : 1) * FN, NMF = FM * FN;
         constexpr int NPAIR = NDS < NMF ? NDS : NMF;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = K0; ks < K1; ++ks) {
           if (ks + 1 < BK / 16) {
 #pragma unroll
             for (int i = 0; i < NPAIR; ++i) {
@@ -565,6 +460,18 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
             __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
           }
         }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using IH = std::integral_constant<int, BK / 32>;
+      using IE = std::integral_constant<int, BK / 16>;
+      if (!SPLIT) {
+        if (wave_rows > 0) mfma_steps(I0{}, IE{});
+      } else {
+        // a wave whose rows are all padding still queues its loads
+        if (wave_rows > 0) mfma_steps(I0{}, IH{});
+        __builtin_amdgcn_s_setprio(0);
+        if (late_loads && g + NSTAGE - 1 < nslices) issue_next();
+        if (wave_rows > 0) mfma_steps(IH{}, IE{});
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -840,9 +747,9 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #define MOE_CFG_WIDE_A8 256, 256, 8, 2, 1
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true, bool SPLIT = false>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB, KBLK>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB, KBLK, SPLIT>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -867,7 +774,7 @@ hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
       if (p.kblock == p.K)
         return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, false>(p, num_cus, s);
     } else {
-      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
+      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, true, !FP8>(p, num_cus, s);
     }
   }
   if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_NARROW_UP, STAGE, ACT, FP8>(p, num_cus, s);
