@@ -774,7 +774,7 @@ hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
       if (p.kblock == p.K)
         return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, false>(p, num_cus, s);
     } else {
-      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, true, !FP8>(p, num_cus, s);
+      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, true, false>(p, num_cus, s);
     }
   }
   if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_NARROW_UP, STAGE, ACT, FP8>(p, num_cus, s);
