@@ -259,6 +259,20 @@ moe_status moe_combine(const moe_config* cfg, const void* y_perm, const int32_t*
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same layer with no
+ * workspace argument and no allocation of any kind.  Its workspace is a 64 MiB array that
+ * the library holds on every device it runs on until the process ends (moe_workspace_size
+ * at most 64 MiB, e.g. T <= 1024 tokens at d = 2048, E = 64, k = 6, S = 4, I = 1536; a
+ * larger config returns MOE_ERR_WORKSPACE before anything is enqueued).  Every launch,
+ * shared experts included, runs on `stream` (no side stream).  Every call on a device
+ * shares that device's array: calls that overlap on one device (on different streams, or
+ * from different threads without ordering) race; calls ordered on one stream do not.
+ * Nothing in the array needs to start at zero: each byte a kernel reads was written
+ * earlier in the same call.  Arguments, results and errors as moe_forward. */
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x,
+                               void* out, hipStream_t stream);
+
 /* Options of moe_forward_ex. */
 typedef struct {
   /* Events recorded on `stream` at the stage boundaries of the forward (NULL entries are

@@ -16,7 +16,7 @@ __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
     "workspace_size", "route", "rmsnorm_route", "select", "load_stats", "permute",
     "quantize_rows",
-    "grouped_gemm", "combine", "forward", "backward_workspace_size", "backward", "GRAD_FIELDS",
+    "grouped_gemm", "combine", "forward", "forward_noalloc", "backward_workspace_size", "backward", "GRAD_FIELDS",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
     "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
@@ -32,7 +32,8 @@ MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
 EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_rmsnorm_route", "moe_select",
                     "moe_load_stats",
                     "moe_permute", "moe_quantize_rows", "moe_grouped_gemm", "moe_combine",
-                    "moe_forward", "moe_forward_ex", "moe_backward_workspace_size", "moe_backward",
+                    "moe_forward", "moe_forward_ex", "moe_forward_noalloc",
+                    "moe_backward_workspace_size", "moe_backward",
                     "moe_status_string", "moe_last_hip_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -125,6 +126,7 @@ def lib():
             "moe_quantize_rows": [cfgp, vp, i32, i32, vp, vp, vp],
             "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
             "moe_forward_ex": [cfgp, wp, vp, vp, vp, sz, vp, ctypes.POINTER(_OptsC)],
+            "moe_forward_noalloc": [cfgp, wp, vp, vp, vp],
             "moe_backward_workspace_size": [cfgp, ctypes.POINTER(sz)],
             "moe_backward": [cfgp, wp, vp, vp, vp, sz, ctypes.POINTER(_GradsC), vp, sz, vp],
             "moe_last_hip_error": [],
@@ -261,6 +263,13 @@ def forward(cfg, weights: Weights, x, out, ws, ws_bytes=None, stream=None, stage
     _check(lib().moe_forward_ex(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x), _ptr(out),
                                 _ptr(ws), nb, _stream(stream), ctypes.byref(opts)),
            "moe_forward_ex")
+
+
+def forward_noalloc(cfg, weights: Weights, x, out, stream=None):
+    """The whole layer on the library's own per-device workspace (moe_forward_noalloc: no
+    allocation; moe_workspace_size(cfg) at most 64 MiB)."""
+    _check(lib().moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(x),
+                                     _ptr(out), _stream(stream)), "moe_forward_noalloc")
 
 
 def backward_workspace_size(cfg: Config) -> int:

@@ -301,6 +301,37 @@ moe_status gemm_params(const moe_config* c, moe_stage stage, moe_expert_set set,
   return MOE_OK;
 }
 
+// Workspace of moe_forward_noalloc, for callers that cannot allocate device memory: one
+// array per device (the code object's own storage, held until the process ends), shared by
+// every call on that device.  Host code never passes `scratch` itself to a kernel or a copy:
+// in host code the name stands for a host-side shadow, not a device address.  The device
+// address is taken once per device with hipGetSymbolAddress (with that device current) and
+// kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// *out = the device address of the current device's scratch array.
+moe_status device_scratch(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (ptr == nullptr) return MOE_ERR_INTERNAL;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,9 +520,11 @@ moe_status moe_quantize_rows(const moe_config* cfg, const void* a, int32_t rows,
   }
 }
 
-moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
-                          void* ws, size_t ws_bytes, hipStream_t stream,
-                          const moe_forward_opts* opts) {
+// The forward of moe_forward_ex on a given workspace.  allow_side = false keeps every launch
+// on `stream` (no side stream or event is created or used).
+static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, const void* x,
+                               void* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                               const moe_forward_opts* opts, bool allow_side) {
   try {
     moe_status st = check_config(cfg);
     if (st != MOE_OK) return st;
@@ -559,7 +592,7 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const voi
     // unless the stages are being timed one by one (then, in decode, the routed and shared
     // experts stream their weights in one launch per stage)
     const SideEntry* side_ent = nullptr;
-    if (shared && !events) {
+    if (shared && !events && allow_side) {
       st = side_entry(stream, &side_ent);
       if (st != MOE_OK) return st;
     }
@@ -845,9 +878,31 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   }
 }
 
+moe_status moe_forward_ex(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
+                          void* ws, size_t ws_bytes, hipStream_t stream,
+                          const moe_forward_opts* opts) {
+  return forward_impl(cfg, w, x, out, ws, ws_bytes, stream, opts, true);
+}
+
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, void* out,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   return moe_forward_ex(cfg, w, x, out, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x,
+                               void* out, hipStream_t stream) {
+  try {
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (carve(cfg).total > kScratchBytes) return MOE_ERR_WORKSPACE;
+    if (cfg->num_tokens == 0) return MOE_OK;
+    void* scratch_ptr = nullptr;
+    st = device_scratch(&scratch_ptr);
+    if (st != MOE_OK) return st;
+    return forward_impl(cfg, w, x, out, scratch_ptr, kScratchBytes, stream, nullptr, false);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
 }
 
 }  // extern "C"
