@@ -256,7 +256,7 @@ def cpu_baseline(lay, n_tokens, min_seconds=10.0):
                       f"(routing, all expert FFNs, combine), {dt:.1f} s wall"}
 
 
-GEMM_SOURCES = ["gemm.hip", "common.h", "internal.h", "api.cpp"]
+GEMM_SOURCES = ["gemm.hip", "gemm_core.h", "common.h", "internal.h", "api.cpp"]
 DECODE_SOURCES = ["decode.hip", "common.h", "internal.h", "api.cpp"]
 
 

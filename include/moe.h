@@ -23,9 +23,12 @@
  *     (MOE_F32 or MOE_BF16); weight_dtype applies to the expert weights (MOE_F32 with
  *     MOE_F32 activations; MOE_BF16 or MOE_FP8_E4M3 with MOE_BF16 activations).
  *   - Limits: 1 <= E <= 64, 1 <= k <= E, E % G == 0, 1 <= Gk <= G, k <= Gk*E/G,
- *     n_g in {1, 2} and n_g <= E/G; dim and inter_dim multiples of 64 (bf16/e4m3) or
- *     of 16 (fp32); num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned; sizes whose
- *     element offsets exceed 2^31 - 1 are MOE_ERR_UNSUPPORTED.
+ *     n_g in {1, 2} and n_g <= E/G; dim and inter_dim multiples of 8 (bf16 weights), of
+ *     16 (e4m3 weights, and fp32); with fp8_act dim a multiple of 128 and inter_dim of 64;
+ *     moe_backward needs multiples of 64.  Multiples of 64 take the tiled MFMA kernels,
+ *     other sizes a kernel built for the tails (moe_gemm_kernel_path tells which);
+ *     num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned; sizes whose element
+ *     offsets exceed 2^31 - 1 are MOE_ERR_UNSUPPORTED.
  *     Violations return MOE_ERR_INVALID_ARG (bad values) or MOE_ERR_UNSUPPORTED
  *     (valid but not implemented).
  *   - Calls are re-entrant; calls that share output or workspace buffers on the same
@@ -160,7 +163,11 @@ moe_status moe_rmsnorm_route(const moe_config* cfg, const void* x, const float* 
 
 /* The selection step of moe_route alone, on given fp32 scores [T, E] and optional
  * selection keys [T, E] (NULL: the scores are the keys).  Every value must be finite and
- * >= 0, as sigmoid and softmax values are.  Same outputs and tie rules. */
+ * >= 0, as sigmoid and softmax values are.  Same outputs and tie rules.
+ * Source: top-k over the gate scores with the selected weights renormalised (the MoEBlock
+ * listing and section "MoE 数学：路由、容量与平衡详解" of "大模型工程（一）：Transformer 到
+ * MoE"); the group limit of section "混合专家（MoE）" of the FusionLLM training-framework
+ * page ("组限制路由", groups ranked by the sum of their n_g best scores). */
 moe_status moe_select(const moe_config* cfg, const float* scores, const float* keys,
                       int32_t* topk_idx, float* topk_w, hipStream_t stream);
 
@@ -233,6 +240,28 @@ moe_status moe_grouped_gemm(const moe_config* cfg, moe_stage stage, moe_expert_s
                             const void* a, const int32_t* row_index, const int32_t* offsets,
                             int32_t rows, const moe_weights* w, const float* row_weight,
                             void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel family that moe_grouped_gemm (and moe_forward) runs for one stage and expert set
+ * of `rows` rows (host only, no HIP call):
+ *   MOE_GEMM_PATH_TILED   MFMA kernel on LDS-staged 64-wide K-slices (dim and inter_dim
+ *                         multiples of 64; the fast path of the prefill shapes);
+ *   MOE_GEMM_PATH_DECODE  weight-streaming kernel for few rows per expert;
+ *   MOE_GEMM_PATH_TAIL    MFMA kernel on directly loaded operands, for a K or N that is a
+ *                         multiple of 8 (bf16) or 16 (e4m3) but not of 64;
+ *   MOE_GEMM_PATH_F32     fp32 activations and weights;
+ *   MOE_GEMM_PATH_FP8_ACT e4m3 x e4m3 up projection (cfg->fp8_act).
+ * The choice depends only on cfg, stage, set and rows.  MOE_ERR_INVALID_ARG / _UNSUPPORTED
+ * as moe_grouped_gemm for the config.  Source: the grouped GEMM after routing, section
+ * "融合内核" of the FusionLLM training-framework page. */
+typedef enum {
+  MOE_GEMM_PATH_TILED = 0,
+  MOE_GEMM_PATH_DECODE = 1,
+  MOE_GEMM_PATH_TAIL = 2,
+  MOE_GEMM_PATH_F32 = 3,
+  MOE_GEMM_PATH_FP8_ACT = 4
+} moe_gemm_path;
+moe_status moe_gemm_kernel_path(const moe_config* cfg, moe_stage stage, moe_expert_set set,
+                                int32_t rows, int32_t* path);
 
 /* out[t] = sum_{j<k} y_perm[slot_pos[t*k+j]] + y_shared[t], summed in that fixed order in
  * fp32, rounded to act_dtype; slots with slot_pos < 0 (dropped) are skipped.

@@ -16,7 +16,8 @@ __all__ = [
     "MoeError", "LibraryMissing", "Config", "Weights", "lib", "library_path", "make_config",
     "workspace_size", "route", "rmsnorm_route", "select", "load_stats", "permute",
     "quantize_rows",
-    "grouped_gemm", "combine", "forward", "forward_noalloc", "backward_workspace_size", "backward", "GRAD_FIELDS",
+    "grouped_gemm", "gemm_kernel_path", "combine", "forward", "forward_noalloc",
+    "backward_workspace_size", "backward", "GRAD_FIELDS",
     "status_string", "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_SCORE_SOFTMAX",
     "MOE_SCORE_SIGMOID", "MOE_ACT_SWIGLU", "MOE_ACT_RELU2", "MOE_STAGE_UP", "MOE_STAGE_DOWN",
     "MOE_EXPERTS_ROUTED", "MOE_EXPERTS_SHARED", "EXPORTED_SYMBOLS",
@@ -28,10 +29,13 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_RELU2 = 0, 1
 MOE_STAGE_UP, MOE_STAGE_DOWN = 0, 1
 MOE_EXPERTS_ROUTED, MOE_EXPERTS_SHARED = 0, 1
+MOE_GEMM_PATH_TILED, MOE_GEMM_PATH_DECODE, MOE_GEMM_PATH_TAIL, MOE_GEMM_PATH_F32, \
+    MOE_GEMM_PATH_FP8_ACT = range(5)
 
 EXPORTED_SYMBOLS = ["moe_workspace_size", "moe_route", "moe_rmsnorm_route", "moe_select",
                     "moe_load_stats",
-                    "moe_permute", "moe_quantize_rows", "moe_grouped_gemm", "moe_combine",
+                    "moe_permute", "moe_quantize_rows", "moe_grouped_gemm",
+                    "moe_gemm_kernel_path", "moe_combine",
                     "moe_forward", "moe_forward_ex", "moe_forward_noalloc",
                     "moe_backward_workspace_size", "moe_backward",
                     "moe_status_string", "moe_last_hip_error"]
@@ -123,6 +127,7 @@ def lib():
             "moe_permute": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_grouped_gemm": [cfgp, i32, i32, vp, vp, vp, i32, wp, vp, vp, vp, sz, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp],
+            "moe_gemm_kernel_path": [cfgp, i32, i32, i32, ctypes.POINTER(i32)],
             "moe_quantize_rows": [cfgp, vp, i32, i32, vp, vp, vp],
             "moe_forward": [cfgp, wp, vp, vp, vp, sz, vp],
             "moe_forward_ex": [cfgp, wp, vp, vp, vp, sz, vp, ctypes.POINTER(_OptsC)],
@@ -222,6 +227,14 @@ def permute(cfg, topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_w
     _check(lib().moe_permute(ctypes.byref(cfg), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
                              _ptr(offsets), _ptr(perm_token), _ptr(slot_pos), _ptr(perm_weight),
                              _ptr(ws), nb, _stream(stream)), "moe_permute")
+
+
+def gemm_kernel_path(cfg, stage, expert_set, rows) -> int:
+    """Kernel family of one grouped-GEMM stage (moe_gemm_kernel_path; host only)."""
+    path = ctypes.c_int32(-1)
+    _check(lib().moe_gemm_kernel_path(ctypes.byref(cfg), int(stage), int(expert_set), int(rows),
+                                      ctypes.byref(path)), "moe_gemm_kernel_path")
+    return path.value
 
 
 def grouped_gemm(cfg, stage, expert_set, a, row_index, offsets, rows, weights: Weights,

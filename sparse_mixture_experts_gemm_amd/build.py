@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "decode.hip",
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_tail.hip", "combine.hip", "decode.hip",
            "stats.hip", "quant.hip", "backward.hip"]
 HIPCC = "/opt/rocm/bin/hipcc"
 

@@ -121,13 +121,17 @@ moe_status check_config(const moe_config* c) {
   if (E > 64) return MOE_ERR_UNSUPPORTED;
   if (c->fp8_act && (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_FP8_E4M3))
     return MOE_ERR_UNSUPPORTED;
-  if (c->fp8_act && c->dim % 128 != 0) return MOE_ERR_UNSUPPORTED;   // 128-byte K-slices
+  // e4m3 activations: 128-byte K-slices of the up projection, 64-wide output tiles
+  if (c->fp8_act && (c->dim % 128 != 0 || c->inter_dim % 64 != 0)) return MOE_ERR_UNSUPPORTED;
   if (c->act_dtype == MOE_F32) {
     if (c->weight_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
     if (c->dim % 16 != 0 || c->inter_dim % 16 != 0) return MOE_ERR_UNSUPPORTED;
   } else {
+    // 16-byte rows of operands: 8 bf16 values, or 16 e4m3 weights (multiples of 64 take
+    // the tiled kernels, other multiples the tail kernel of gemm_tail.hip)
     if (c->weight_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
-    if (c->dim % 64 != 0 || c->inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    const int q = c->weight_dtype == MOE_FP8_E4M3 ? 16 : 8;
+    if (c->dim % q != 0 || c->inter_dim % q != 0) return MOE_ERR_UNSUPPORTED;
   }
   const long long Tk = (long long)c->num_tokens * c->top_k;
   if (Tk > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
@@ -249,6 +253,7 @@ moe_status check_backward_config(const moe_config* c) {
   if (!std::isfinite(c->route_scale) || c->route_scale == 0.0f) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_BF16 || c->pre_norm || c->fp8_act)
     return MOE_ERR_UNSUPPORTED;
+  if (c->dim % 64 != 0 || c->inter_dim % 64 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -873,6 +878,38 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
       if (ok()) e = we;
     }
     return hip_status(e);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_gemm_kernel_path(const moe_config* cfg, moe_stage stage, moe_expert_set set,
+                                int32_t rows, int32_t* path) {
+  try {
+    if (path == nullptr || rows < 0) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    if (stage != MOE_STAGE_UP && stage != MOE_STAGE_DOWN) return MOE_ERR_INVALID_ARG;
+    if (set != MOE_EXPERTS_ROUTED && set != MOE_EXPERTS_SHARED) return MOE_ERR_INVALID_ARG;
+    const bool routed = set == MOE_EXPERTS_ROUTED;
+    if (!routed && cfg->num_shared == 0) return MOE_ERR_INVALID_ARG;
+    // the shape fields of the launch parameters (pointers only as markers: never read)
+    static const int32_t marker = 0;
+    const int I_eff = routed ? cfg->inter_dim : cfg->num_shared * cfg->inter_dim;
+    moe::GemmParams g{};
+    g.offsets = routed ? &marker : nullptr;
+    g.nseg = routed ? cfg->num_experts : 1;
+    g.rows = rows;
+    const bool up = stage == MOE_STAGE_UP;
+    g.N = up ? I_eff : cfg->dim;
+    g.K = up ? cfg->dim : I_eff;
+    g.kblock = up ? cfg->dim : cfg->inter_dim;
+    if (up && cfg->fp8_act) *path = MOE_GEMM_PATH_FP8_ACT;
+    else if (cfg->act_dtype == MOE_F32) *path = MOE_GEMM_PATH_F32;
+    else if (moe::tail_gemm_applies(g)) *path = MOE_GEMM_PATH_TAIL;
+    else if (moe::decode_gemm_applies(g, cfg->act_dtype)) *path = MOE_GEMM_PATH_DECODE;
+    else *path = MOE_GEMM_PATH_TILED;
+    return MOE_OK;
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

@@ -341,7 +341,7 @@ hipError_t launch_dec(const GemmParams& p, const GemmParams* p2, hipStream_t s) 
 
 bool decode_gemm_applies(const GemmParams& p, int act_dtype) {
   if (act_dtype != MOE_BF16) return false;
-  if (p.K % kStepK != 0 || p.kblock % kStepK != 0) return false;
+  if (p.K % kStepK != 0 || p.kblock % kStepK != 0 || p.N % 64 != 0) return false;
   // few rows per segment: streaming the weights dominates
   if (p.offsets != nullptr) return (long long)p.rows <= 32LL * p.nseg;
   return p.rows <= 128;

@@ -829,6 +829,7 @@ hipError_t launch_grouped_gemm(const GemmParams& p, Stage stage, int act, int ac
     return launch_f32<1, MOE_ACT_SWIGLU>(p, num_cus, s);
   }
   const bool fp8 = weight_dtype == MOE_FP8_E4M3;
+  if (tail_gemm_applies(p)) return launch_tail_gemm(p, stage, act, weight_dtype, num_cus, s);
   if (decode_gemm_applies(p, act_dtype)) return launch_decode_gemm(p, stage, act, weight_dtype, s);
   if (up) {
     if (fp8) return relu2 ? launch_mfma<0, MOE_ACT_RELU2, true>(p, num_cus, s)

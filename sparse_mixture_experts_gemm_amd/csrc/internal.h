@@ -91,6 +91,12 @@ hipError_t launch_up_backward(const GemmParams& p, int act, int num_cus, hipStre
 // forward weights as they are.
 hipError_t launch_down_trb(const GemmParams& p, int num_cus, hipStream_t s);
 
+// Grouped GEMM for K, kblock or N off the 64-element grid (multiples of 8; bf16
+// activations, bf16 or e4m3 weights): operands straight from global memory, 64 x 64 tiles.
+bool tail_gemm_applies(const GemmParams& p);
+hipError_t launch_tail_gemm(const GemmParams& p, Stage stage, int act, int weight_dtype,
+                            int num_cus, hipStream_t s);
+
 // Weight-streaming variant of the grouped GEMM for few rows per segment.  `second`, when
 // given, is a second segment set (e.g. the shared experts) run in the same launch.
 bool decode_gemm_applies(const GemmParams& p, int act_dtype);

@@ -154,7 +154,9 @@ constexpr int kNormLdsDim = 4096;
 constexpr int kNormRowBytes = kNormLdsDim * 2 + 16;
 constexpr int kPartBytes = kRouteWaves * kRouteTok * 64 * 4;
 
-template <int NORM>
+// KTAIL: d is not a multiple of 32 (a multiple of 8): one more K-step, whose 8-element
+// groups past d read zeros.  With KTAIL false the code is that of a 32-aligned d.
+template <int NORM, bool KTAIL>
 __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
                                                           const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ wr,
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
   const float row_r = NORM == 2 ? s_inv_rms[m] : 0.0f;
   const unsigned char* lds_row = smem + m * kNormRowBytes;
   auto load_a = [&](int kk) -> uint4 {
-    if (!row_ok) return make_uint4(0, 0, 0, 0);
+    if (!row_ok || (KTAIL && kk >= p.d)) return make_uint4(0, 0, 0, 0);
     if (NORM == 1) return *reinterpret_cast<const uint4*>(lds_row + kk * 2);
     const uint4 v = *reinterpret_cast<const uint4*>(xrow + kk);
     return NORM == 2 ? norm_bf16x8(v, row_r, p.norm_gamma + kk) : v;
@@ -251,11 +253,12 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
 #pragma unroll
   for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = p.d >> 5;
+  const int nsteps = KTAIL ? (p.d + 31) >> 5 : p.d >> 5;
   auto load_b = [&](int kk, int n) -> uint4 {
     const int e = n * 16 + m;
-    return (n < ntiles && e < p.E) ? *reinterpret_cast<const uint4*>(wr + (size_t)e * p.d + kk)
-                                   : make_uint4(0, 0, 0, 0);
+    return (n < ntiles && e < p.E && (!KTAIL || kk < p.d))
+               ? *reinterpret_cast<const uint4*>(wr + (size_t)e * p.d + kk)
+               : make_uint4(0, 0, 0, 0);
   };
   int st = wave;
   for (; st + 3 * kRouteWaves < nsteps; st += 4 * kRouteWaves) {
@@ -357,8 +360,12 @@ hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, cons
   const bool norm = p.norm_gamma != nullptr;
   if (act_dtype == MOE_BF16) {
     dim3 grid((p.T + kRouteTok - 1) / kRouteTok);
-    auto kern = !norm ? route_bf16_kernel<0>
-                      : (p.d <= kNormLdsDim ? route_bf16_kernel<1> : route_bf16_kernel<2>);
+    const int nm = !norm ? 0 : (p.d <= kNormLdsDim ? 1 : 2);
+    auto kern = (p.d & 31) == 0
+                    ? (nm == 0 ? route_bf16_kernel<0, false>
+                               : nm == 1 ? route_bf16_kernel<1, false> : route_bf16_kernel<2, false>)
+                    : (nm == 0 ? route_bf16_kernel<0, true>
+                               : nm == 1 ? route_bf16_kernel<1, true> : route_bf16_kernel<2, true>);
     hipLaunchKernelGGL(kern, grid, dim3(64 * kRouteWaves), 0, s, p,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(router),
                        bias, scores, idx, w);

@@ -72,12 +72,15 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
 @pytest.mark.parametrize("bad,status", [
     (dict(k=0), 1), (dict(k=65, E=64), 1), (dict(E=60, G=8), 1), (dict(Gk=9), 1),
     (dict(k=17, Gk=2), 1), (dict(n_g=3), 1), (dict(E=64, G=64, Gk=6, n_g=2), 1),
-    (dict(T=-1), 1), (dict(d=0), 1), (dict(E=128, G=8, k=6), 2), (dict(d=2000), 2),
-    (dict(I=1000), 2), (dict(act_dtype="f32", weight_dtype="bf16"), 2),
+    (dict(T=-1), 1), (dict(d=0), 1), (dict(E=128, G=8, k=6), 2), (dict(d=2004), 2),
+    (dict(I=1004), 2), (dict(weight_dtype="e4m3", d=2056), 2),   # 8 | d but not 16 (e4m3)
+    (dict(weight_dtype="e4m3", I=1544), 2), (dict(act_dtype="f32", weight_dtype="f32", d=40), 2),
+    (dict(act_dtype="f32", weight_dtype="bf16"), 2),
     (dict(act_dtype="bf16", weight_dtype="f32"), 2),
     (dict(capacity_factor=float("nan")), 1),
     (dict(fp8_act=True), 2),                       # e4m3 activations need e4m3 weights
     (dict(fp8_act=True, weight_dtype="e4m3", d=192), 2),   # ... and 128-byte K-slices
+    (dict(fp8_act=True, weight_dtype="e4m3", I=1552), 2),  # ... and 64-wide output tiles
     (dict(pre_norm=True, norm_eps=float("nan")), 1), (dict(norm_eps=-1e-6), 1),
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
@@ -139,7 +142,8 @@ def test_backward_arguments_are_checked_on_the_host(lib):
     assert call(c, w, g, nb=n - 1) == 3                     # backward workspace too small
     assert call(c, w, g, x=fake + 2) == 2                   # misaligned
     for bad, status in [(dict(weight_dtype="e4m3"), 2), (dict(act_dtype="f32", weight_dtype="f32"), 2),
-                        (dict(pre_norm=True), 2), (dict(route_scale=0.0), 1)]:
+                        (dict(pre_norm=True), 2), (dict(route_scale=0.0), 1),
+                        (dict(d=2000), 2), (dict(I=1000), 2)]:   # the backward's 64-grid
         cb = cfg(T=64, **bad)
         nn = ctypes.c_size_t(0)
         assert lib.moe_backward_workspace_size(ctypes.byref(cb), ctypes.byref(nn)) == status
@@ -216,3 +220,38 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(moe.LibraryMissing):
         moe.workspace_size(cfg())
+
+
+@pytest.mark.parametrize("over,stage,expert_set,rows,path", [
+    # the FusionLLM layer at 4096 tokens: every stage on the tiled MFMA kernel
+    (dict(), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 4096 * 6, moe.MOE_GEMM_PATH_TILED),
+    (dict(), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, 4096 * 6, moe.MOE_GEMM_PATH_TILED),
+    (dict(), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_SHARED, 4096, moe.MOE_GEMM_PATH_TILED),
+    (dict(), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_SHARED, 4096, moe.MOE_GEMM_PATH_TILED),
+    (dict(weight_dtype="e4m3"), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 16384 * 6,
+     moe.MOE_GEMM_PATH_TILED),
+    # 64 tokens: weight streaming
+    (dict(T=64), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 64 * 6, moe.MOE_GEMM_PATH_DECODE),
+    (dict(T=64), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_SHARED, 64, moe.MOE_GEMM_PATH_DECODE),
+    # off the 64-element grid: the tail kernel, for either stage
+    (dict(d=200, I=136), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 4096 * 6, moe.MOE_GEMM_PATH_TAIL),
+    (dict(d=2048, I=136), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_SHARED, 4096, moe.MOE_GEMM_PATH_TAIL),
+    (dict(d=208, I=144, weight_dtype="e4m3"), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, 64 * 6,
+     moe.MOE_GEMM_PATH_TAIL),
+    (dict(act_dtype="f32", weight_dtype="f32"), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 100,
+     moe.MOE_GEMM_PATH_F32),
+    (dict(weight_dtype="e4m3", fp8_act=True), moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, 100,
+     moe.MOE_GEMM_PATH_FP8_ACT),
+    (dict(weight_dtype="e4m3", fp8_act=True), moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, 4096 * 6,
+     moe.MOE_GEMM_PATH_TILED),
+])
+def test_gemm_kernel_path(lib, over, stage, expert_set, rows, path):
+    assert moe.gemm_kernel_path(cfg(**over), stage, expert_set, rows) == path
+
+
+def test_gemm_kernel_path_rejects_bad_arguments(lib):
+    p = ctypes.c_int32(-1)
+    assert lib.moe_gemm_kernel_path(ctypes.byref(cfg()), 0, 0, 10, None) == 1
+    assert lib.moe_gemm_kernel_path(ctypes.byref(cfg()), 2, 0, 10, ctypes.byref(p)) == 1
+    assert lib.moe_gemm_kernel_path(ctypes.byref(cfg(S=0)), 0, 1, 10, ctypes.byref(p)) == 1
+    assert lib.moe_gemm_kernel_path(ctypes.byref(cfg(d=2004)), 0, 0, 10, ctypes.byref(p)) == 2

@@ -86,6 +86,19 @@ SMALL = {
     "biased_prenorm": W.small_shape(T=333, d=256, E=32, k=4, G=8, Gk=3, n_g=2, S=1, I=128,
                                     select_bias_std=0.7, capacity_factor=1.0, pre_norm=True,
                                     residual=True, seed=49),
+    # dim and inter_dim off the 64-element grid (multiples of 8 for bf16, of 16 for e4m3
+    # weights): the router's K tail and the tail grouped GEMM
+    "tail_bf16": W.small_shape(T=300, d=200, E=16, k=4, G=4, Gk=2, S=2, I=136, seed=60),
+    "tail_e4m3": W.small_shape(T=250, d=208, E=8, k=2, G=2, Gk=1, S=2, I=144,
+                               weight_dtype="e4m3", seed=61),
+    "tail_relu2_e4m3": W.small_shape(T=190, d=208, E=8, k=3, G=1, Gk=1, S=1, I=176,
+                                     act="relu2", weight_dtype="e4m3", seed=62),
+    "tail_d_only": W.small_shape(T=200, d=200, E=8, k=2, G=2, Gk=1, S=1, I=128, seed=63),
+    "tail_i_only": W.small_shape(T=200, d=256, E=8, k=2, G=2, Gk=1, S=3, I=72, seed=64),
+    # several tail tiles per workgroup
+    "tail_multi": W.small_shape(T=16384, d=200, E=8, k=4, G=1, Gk=1, S=1, I=136, seed=65),
+    "tail_prenorm": W.small_shape(T=150, d=200, E=16, k=4, G=4, Gk=2, S=1, I=136,
+                                  pre_norm=True, residual=True, seed=66),
 }
 
 
@@ -237,7 +250,7 @@ def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
 # ----------------------------------------------------------------------------- route
 ROUTE_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                "small_swiglu", "small_f32", "single_token", "topk1_nogroups", "balance_bf16",
-               "biased_softmax_f32", "biased_groups_n2"]
+               "biased_softmax_f32", "biased_groups_n2", "tail_bf16", "tail_e4m3"]
 
 
 @pytest.mark.parametrize("name", ROUTE_CASES)
@@ -298,7 +311,7 @@ def test_route_matches_oracle(name):
 # ----------------------------------------------------------------------------- pre-norm routing
 PRENORM_CASES = ["prenorm_bf16", "prenorm_decode_bf16", "small_prenorm_bf16",
                  "small_prenorm_noresid", "small_prenorm_f32", "biased_prenorm", "prenorm_d4096",
-                 "prenorm_d4160"]
+                 "prenorm_d4160", "tail_prenorm"]
 # A normalised value that differs from the oracle's by one ulp moves a logit by about
 # |W_r| * ulp (~1e-4 here); decisions closer than this are near ties of the pre-norm step.
 PRENORM_MARGIN = 1e-3
@@ -499,7 +512,8 @@ def _dense(lay, which, e, shared=False):
 
 
 GEMM_CASES = ["small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32", "tiny_fp32",
-              "single_token", "fusionllm_bf16", "fp8_relu2"]
+              "single_token", "fusionllm_bf16", "fp8_relu2", "tail_bf16", "tail_e4m3",
+              "tail_relu2_e4m3", "tail_d_only", "tail_i_only"]
 
 
 @pytest.mark.parametrize("name", GEMM_CASES)
@@ -715,7 +729,8 @@ FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "f
                  "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
                  "single_token", "topk1_nogroups", "balance_bf16", "biased_softmax_f32",
                  "biased_groups_n2", "fp8a_relu2", "small_a8_swiglu", "multi_tile_a8_relu2",
-                 "all_experts"]
+                 "all_experts", "tail_bf16", "tail_e4m3", "tail_relu2_e4m3", "tail_d_only",
+                 "tail_i_only", "tail_multi"]
 
 
 def run_forward(name):
