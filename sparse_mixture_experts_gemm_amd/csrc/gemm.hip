@@ -68,7 +68,7 @@ namespace {
 // 128 x 256.  Eight waves (two per SIMD) per workgroup, so one wave's LDS and barrier waits
 // are covered by its partner's MFMAs.
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true, bool SPLIT = false>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
 __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) {
   constexpr int NTHR = WAVES * 64;
   // K values per slice: 64 (128-byte bf16 rows), or 128 e4m3 bytes with e4m3 activations
@@ -105,12 +105,6 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   auto swz_a = [](int r) { return swz8(r); };                        // A rows (128 bytes)
   auto swz_b8 = [](int r) { return swz4(r); };                       // 64-byte e4m3 B rows
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
-  // SPLIT: the two wave rows queue their loads of the next slice at different times, the
-  // first row before its MFMAs, the second half-way through them, so that on every SIMD one
-  // wave multiplies while the other waits for the address unit to take its loads.  Loads
-  // are then queued outside the barrier-synchronised points, so the path that stages
-  // gathered rows with a barrier (short K on a deeper ring) must not be taken.
-  static_assert(!SPLIT || (NSTAGE == 2 && !A8), "staggered loads: 2-stage ring, bf16 activations");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
 
   __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
@@ -190,7 +184,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   for (int i = 0; i < NDMA; ++i) is_b[i] = wave * NDMA + i >= A_DMA;
   int src_seg = 0;   // segment of the tile being loaded (TRB: offset of the second matrix)
 
-  auto set_sources = [&](int j) {
+  auto set_sources = [&](int j) __attribute__((always_inline)) {
     const TileCoord tc = tile_at(j);
     if (gather && !prefetch) {
       // short K: the rows of tile j are gathered here, at the cost of draining the loads
@@ -249,7 +243,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   // next slice to request: tile ij, k-slice ikt, ring stage ist
   int ij = 0, ikt = 0, ist = 0;
   set_sources(0);
-  auto issue_next = [&]() {
+  auto issue_next = [&]() __attribute__((always_inline)) {
     if (ikt == nk) {
       ikt = 0;
       ++ij;
@@ -275,7 +269,7 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       const int q = wave * NDMA + i;
       const unsigned char* a = (TRB && is_b[i]) ? tbase + reinterpret_cast<size_t>(src[i])
                                                 : src[i] + (is_b[i] ? boff : aoff);
-      lds_dma16(st + (uint32_t)(q * 1024), a);
+      lds_dma16((uint32_t)__builtin_amdgcn_readfirstlane((int)(st + (uint32_t)(q * 1024))), a);
     }
     ++ikt;
     ist = ist + 1 == NSTAGE ? 0 : ist + 1;
@@ -319,9 +313,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   int wave_rows = rows_of_wave(tc);
   int j = 0, kt = 0, cst = 0;      // tile, k-slice and ring stage being multiplied
   int j3 = 0;                      // j mod 3
-  const bool late_loads = SPLIT && wm == 1;   // this wave queues its loads half-way
   for (int g = 0; g < nslices; ++g) {
-    if (g + NSTAGE - 1 < nslices && !late_loads) issue_next();
+    if (g + NSTAGE - 1 < nslices) issue_next();
     if (FOLD && kt > 0 && ((kt * BK) % p.kblock) == 0) {
       // the next K block belongs to another shared expert: fold the finished block
       // with its per-channel scales
@@ -462,17 +455,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         }
       };
       using I0 = std::integral_constant<int, 0>;
-      using IH = std::integral_constant<int, BK / 32>;
       using IE = std::integral_constant<int, BK / 16>;
-      if (!SPLIT) {
-        if (wave_rows > 0) mfma_steps(I0{}, IE{});
-      } else {
-        // a wave whose rows are all padding still queues its loads
-        if (wave_rows > 0) mfma_steps(I0{}, IH{});
-        __builtin_amdgcn_s_setprio(0);
-        if (late_loads && g + NSTAGE - 1 < nslices) issue_next();
-        if (wave_rows > 0) mfma_steps(IH{}, IE{});
-      }
+      if (wave_rows > 0) mfma_steps(I0{}, IE{});
     }
     __builtin_amdgcn_s_setprio(0);
 
@@ -747,9 +731,9 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(GemmParams p) {
 #define MOE_CFG_WIDE_A8 256, 256, 8, 2, 1
 
 template <int BM, int BN, int WAVES, int NSTAGE, int OCC, int STAGE, int ACT, bool FP8,
-          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true, bool SPLIT = false>
+          bool A8 = false, bool BWD = false, bool TRB = false, bool KBLK = true>
 hipError_t launch_cfg(const GemmParams& p, int num_cus, hipStream_t s) {
-  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB, KBLK, SPLIT>),
+  hipLaunchKernelGGL((gg_mfma_kernel<BM, BN, WAVES, NSTAGE, OCC, STAGE, ACT, FP8, A8, BWD, TRB, KBLK>),
                      dim3(num_cus * OCC), dim3(WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -774,7 +758,7 @@ hipError_t launch_mfma(const GemmParams& p, int num_cus, hipStream_t s) {
       if (p.kblock == p.K)
         return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, false>(p, num_cus, s);
     } else {
-      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8, false, false, false, true, false>(p, num_cus, s);
+      return launch_cfg<MOE_CFG_WIDE, STAGE, ACT, FP8>(p, num_cus, s);
     }
   }
   if constexpr (STAGE == 0) return launch_cfg<MOE_CFG_NARROW_UP, STAGE, ACT, FP8>(p, num_cus, s);
