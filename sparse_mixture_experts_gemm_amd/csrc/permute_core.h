@@ -1,7 +1,6 @@
-// Single-workgroup permutation of (token, slot) pairs whose expert ids are already in LDS.
-// Used by the small-batch permutation and by the small-batch route kernel, which selects
-// the experts itself and permutes in the same launch.  Order: expert ascending, then token
-// ascending (see permute.hip).
+// Single-workgroup permutation of (token, slot) pairs whose expert ids are already in LDS,
+// used by the small-batch permutation of permute.hip.  Order: expert ascending, then token
+// ascending.
 #pragma once
 #include "common.h"
 

@@ -504,6 +504,58 @@ def test_permute_skips_out_of_range_ids_and_combine_ignores_them(T):
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
 
 
+def _ws_maps(ws, T, k, E):
+    """topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight from the head of
+    a forward workspace (each array 256-byte aligned, in that order; moe_forward's layout)."""
+    out, off = [], 0
+    for n, dt in ((T * k, torch.int32), (T * k, torch.float32), (E, torch.int32),
+                  (E + 1, torch.int32), (T * k, torch.int32), (T * k, torch.int32),
+                  (T * k, torch.float32)):
+        out.append(ws[off: off + 4 * n].view(dt).cpu().numpy().copy())
+        off += (4 * n + 255) // 256 * 256
+    return out
+
+
+@pytest.mark.parametrize("name,T", [("decode_bf16", 1), ("decode_bf16", 17), ("decode_bf16", 64),
+                                    ("fusionllm_bf16", 128), ("biased_groups_n2", 100),
+                                    ("tail_bf16", 77), ("small_relu2_e4m3", 128)])
+def test_small_batch_forward_routes_and_permutes_like_the_separate_calls(name, T):
+    """The routing (indices, weights) and permutation maps that moe_forward leaves in its
+    workspace for a small batch equal those of moe_route followed by moe_permute on the same
+    input, bit for bit (selection bias, capacity and a dim off the 32-grid included)."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    wts = weights(lay)
+    x = to_dev(lay.x)[:T].contiguous()
+    cfg = config(s, T=T)
+    ws = workspace(cfg)
+    out = act_empty((T, s.d), s.act_dtype)
+    moe.forward(cfg, wts, x, out, ws)
+    torch.cuda.synchronize()
+    fused = _ws_maps(ws, T, s.k, s.E)
+    k, E = s.k, s.E
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.route(cfg, x, wts.tensors["router"], wts.tensors["logit_bias"], wts.tensors["select_bias"],
+              None, idx, tw)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pt = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    moe.permute(cfg, idx, tw, counts, offsets, pt, sp, pw, workspace(cfg))
+    torch.cuda.synchronize()
+    rows = int(offsets[-1].item())
+    sep = [idx.cpu().numpy().reshape(-1), tw.cpu().numpy().reshape(-1), counts.cpu().numpy(),
+           offsets.cpu().numpy(), pt.cpu().numpy(), sp.cpu().numpy(), pw.cpu().numpy()]
+    names = ["topk_idx", "topk_w", "counts", "offsets", "perm_token", "slot_pos", "perm_weight"]
+    for nm, a, b in zip(names, fused, sep):
+        if nm in ("perm_token", "perm_weight"):
+            a, b = a[:rows], b[:rows]
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b), nm
+
+
 # ----------------------------------------------------------------------------- grouped GEMMs
 def _dense(lay, which, e, shared=False):
     s = lay.shape
