@@ -28,7 +28,8 @@
  *     moe_backward needs multiples of 64.  Multiples of 64 take the tiled MFMA kernels,
  *     other sizes a kernel built for the tails (moe_gemm_kernel_path tells which);
  *     num_tokens >= 0 (0 is a no-op); pointers 16-byte aligned; sizes whose element
- *     offsets exceed 2^31 - 1 are MOE_ERR_UNSUPPORTED.
+ *     offsets exceed 2^31 - 1 (T*k*max(dim, inter_dim), T*S*inter_dim, E*dim*inter_dim,
+ *     S*inter_dim*dim) are MOE_ERR_UNSUPPORTED.
  *     Violations return MOE_ERR_INVALID_ARG (bad values) or MOE_ERR_UNSUPPORTED
  *     (valid but not implemented).
  *   - Calls are re-entrant; calls that share output or workspace buffers on the same

@@ -136,10 +136,12 @@ moe_status check_config(const moe_config* c) {
   const long long Tk = (long long)c->num_tokens * c->top_k;
   if (Tk > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   if ((long long)c->num_shared * c->inter_dim > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
-  // the kernels index activations and one expert's weights with 32-bit element offsets
+  // the kernels index activations and one expert's weights (the stacked shared experts
+  // count as one) with 32-bit element offsets, or byte offsets below 4 GB
   const long long widest = c->dim > c->inter_dim ? c->dim : c->inter_dim;
   if (Tk * widest > INT_MAX || (long long)c->num_tokens * c->num_shared * c->inter_dim > INT_MAX ||
-      (long long)c->num_experts * c->dim * c->inter_dim > INT_MAX)
+      (long long)c->num_experts * c->dim * c->inter_dim > INT_MAX ||
+      (long long)c->num_shared * c->inter_dim * c->dim > INT_MAX)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

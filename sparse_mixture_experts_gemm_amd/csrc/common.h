@@ -123,6 +123,30 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_base, const void* src) {
       : "memory");
 }
 
+// As lds_dma16, reading from base + off: `base` is the same for every lane of the wave (it
+// is passed in scalar registers), `off` is this lane's byte offset (below 4 GB).
+__device__ __forceinline__ void lds_dma16_off(uint32_t lds_base, const void* base, uint32_t off) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_base), "v"(off), "s"(base)
+      : "memory");
+}
+
+// A pointer that the caller knows to be the same in every lane, made visibly uniform (the
+// first lane's value) so that it can live in scalar registers.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const void* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return reinterpret_cast<const unsigned char*>(((unsigned long long)hi << 32) | lo);
+}
+
 // Logical workgroup -> XCD-contiguous order.  Workgroups are dispatched round-robin over
 // the 8 XCDs (workgroup b runs on XCD b % 8), so map workgroup b to a slot such that each
 // XCD walks a contiguous range of logical tiles and its L2 sees their shared operands.

@@ -25,7 +25,11 @@
 // XCD-contiguous order: workgroup b runs on XCD b % 8, and each XCD takes a contiguous range
 // of (expert, n-tile, m-tile) tiles so that tiles sharing an expert's weights share that
 // XCD's L2; the slot-to-tile map rotates by one per step, so that every workgroup alternates
-// an expert's full and padded m-tiles and the two stay in step over the same weights.  The
+// an expert's full and padded m-tiles and the two stay in step over the same weights.  A
+// tile's K-loop is compiled once per count of the wave's 32-row blocks that hold rows of the
+// segment, so the padded rows of an expert's last m-tile cost neither LDS reads nor MFMAs.
+// Every DMA reads from a base address that is the same over the wave (scalar registers)
+// plus a 32-bit offset per lane, which keeps the address registers few.  The
 // K-slices of a workgroup's consecutive tiles form one stream, so the loads of the next
 // tile are in flight while the current tile's epilogue runs.  Within a slice, scheduling
 // directives place the LDS reads of the next K-step between the MFMAs of the current one.
@@ -106,6 +110,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   auto swz_b8 = [](int r) { return swz4(r); };                       // 64-byte e4m3 B rows
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
+  // forward bf16-activation tiles: per-tile copies of the K-loop for 0 .. FM live row blocks
+  constexpr bool SPEC = !A8 && !BWD && !TRB && !FP8;
+  static_assert(!SPEC || FM == 2 || FM == 4, "row-block specialisation");
 
   __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
   __shared__ int s_tile0[65], s_row0[64], s_rows[64];
@@ -178,11 +185,16 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   }
 
   // ---- sources of every DMA this lane takes part in, for the tile being loaded
-  const unsigned char* src[NDMA];
+  // (a base address that is the same for the whole wave, held in scalar registers, and this
+  // lane's 32-bit byte offset from it: an activation matrix and one segment's weights stay
+  // below 4 GB)
+  const unsigned char* sbase[NDMA];
+  uint32_t soff[NDMA];
   bool is_b[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) is_b[i] = wave * NDMA + i >= A_DMA;
   int src_seg = 0;   // segment of the tile being loaded (TRB: offset of the second matrix)
+  constexpr int ESZ_B = FP8 ? 1 : 2;
 
   auto set_sources = [&](int j) __attribute__((always_inline)) {
     const TileCoord tc = tile_at(j);
@@ -192,8 +204,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       if (tid < BM) s_arow[j & 1][tid] = p.row_index[seg_row(tc, tid)];
       __syncthreads();
     }
-    const size_t seg_off = (size_t)tc.seg * N * K;   // weight elements per segment
-    src_seg = tc.seg;
+    src_seg = __builtin_amdgcn_readfirstlane(tc.seg);
+    const size_t seg_off = (size_t)src_seg * N * K;   // weight elements per segment
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
@@ -206,11 +218,13 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         n = n < N ? n : 0;
         // byte offset inside a 64-row block of the [K][N] matrix; the block's base
         // (first or second matrix) is chosen per slice
-        src[i] = reinterpret_cast<const unsigned char*>(((size_t)kr * N + n) * 2);
+        sbase[i] = nullptr;
+        soff[i] = (uint32_t)(((size_t)kr * N + n) * 2);
       } else if (!is_b[i]) {
         const int row = q * (1024 / AROW) + lane / CPR_A;
         const int srow = gather ? s_arow[j & 1][row] : seg_row(tc, row);
-        src[i] = a_base + (size_t)srow * K * ESZ_A + (size_t)(((lane % CPR_A) ^ swz_a(row)) * 16);
+        sbase[i] = a_base;
+        soff[i] = (uint32_t)((size_t)srow * K * ESZ_A + (size_t)(((lane % CPR_A) ^ swz_a(row)) * 16));
       } else {
         const int qb = q - A_DMA;
         const int n = (FP8 && !A8) ? qb * B_RPD + lane / 4 : qb * B_RPD + lane / 8;   // LDS row
@@ -232,10 +246,10 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
           wb = p.w_down;
         }
         wrow = wrow < N ? wrow : 0;
-        const size_t e = seg_off + (size_t)wrow * p.kblock;
-        src[i] = static_cast<const unsigned char*>(wb) +
-                 (A8    ? e + ((lane & 7) ^ swz8(n)) * 16
-                  : FP8 ? e + ((lane & 3) ^ swz_b8(n)) * 16 : (e + ((lane & 7) ^ swz8(n)) * 8) * 2);
+        // the rows of one DMA lie in one 32-row block, so all its lanes read one matrix
+        sbase[i] = uniform_ptr(static_cast<const unsigned char*>(wb) + seg_off * ESZ_B);
+        soff[i] = (uint32_t)((size_t)wrow * p.kblock * ESZ_B +
+                             (FP8 && !A8 ? ((lane & 3) ^ swz_b8(n)) : ((lane & 7) ^ swz8(n))) * 16);
       }
     }
   };
@@ -267,29 +281,19 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int q = wave * NDMA + i;
-      const unsigned char* a = (TRB && is_b[i]) ? tbase + reinterpret_cast<size_t>(src[i])
-                                                : src[i] + (is_b[i] ? boff : aoff);
-      lds_dma16((uint32_t)__builtin_amdgcn_readfirstlane((int)(st + (uint32_t)(q * 1024))), a);
+      const unsigned char* base = (TRB && is_b[i]) ? tbase : sbase[i] + (is_b[i] ? boff : aoff);
+      lds_dma16_off((uint32_t)__builtin_amdgcn_readfirstlane((int)(st + (uint32_t)(q * 1024))), base,
+                    soff[i]);
     }
     ++ikt;
     ist = ist + 1 == NSTAGE ? 0 : ist + 1;
   };
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int a = 0; a < FM; ++a)
-#pragma unroll
-    for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
   // e4m3 DOWN over several weight-scale blocks of K (the stacked shared experts): the
   // finished blocks are folded into a second accumulator set.  KBLK = false: one block
   // (p.kblock == K, checked by the launcher), the scale is applied in the epilogue only.
   constexpr bool FOLD = FP8 && STAGE == 1 && KBLK;
   constexpr int TFM = FOLD ? FM : 1, TFN = FOLD ? FN : 1;
-  f32x16 acc_tot[TFM][TFN];
-#pragma unroll
-  for (int a = 0; a < TFM; ++a)
-#pragma unroll
-    for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
 
   // prologue: slices 0 .. NSTAGE-2 in flight, slice 0 landed
 #pragma unroll
@@ -313,315 +317,343 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   int wave_rows = rows_of_wave(tc);
   int j = 0, kt = 0, cst = 0;      // tile, k-slice and ring stage being multiplied
   int j3 = 0;                      // j mod 3
-  for (int g = 0; g < nslices; ++g) {
-    if (g + NSTAGE - 1 < nslices) issue_next();
-    if (FOLD && kt > 0 && ((kt * BK) % p.kblock) == 0) {
-      // the next K block belongs to another shared expert: fold the finished block
-      // with its per-channel scales
-      const int blk = (kt * BK) / p.kblock - 1;
+  int g = 0;                       // slice of the workgroup's sequence being multiplied
+  // The nk slices of one tile.  NF: how many of the wave's 32-row blocks hold rows of the
+  // segment; the others are padding, neither multiplied nor stored.  NF is fixed for the
+  // whole tile, so that each specialised copy of the loop keeps its own accumulators and
+  // none of them is live where the copies meet.
+  auto run_tile = [&](auto nf_tag) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
+    f32x16 acc[FM][FN];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
-        float sc[16];
-        if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
-        else {
+    for (int a = 0; a < FM; ++a)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-        }
+      for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
+    f32x16 acc_tot[TFM][TFN];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
+    for (int a = 0; a < TFM; ++a)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc_tot[fm % TFM][fn % TFN][i] += sc[i] * acc[fm][fn][i];
-          acc[fm][fn] = f32x16{};
-        }
-      }
-    }
-    const unsigned char* A = lds + cst * ST_BYTES;
-    const unsigned char* B = A + A_BYTES;
-    // operand fragments of K-step ks + 1 are read from LDS while the MFMAs of step ks run
-    bf16x8 af[2][FM], bfr[2][FN];
-    auto load_frags = [&](int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
-      const int c = ks * 2 + (lane >> 5);
+      for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
+    for (int islice = 0; islice < nk; ++islice, ++g) {
+      if (g + NSTAGE - 1 < nslices) issue_next();
+      if (FOLD && kt > 0 && ((kt * BK) % p.kblock) == 0) {
+        // the next K block belongs to another shared expert: fold the finished block
+        // with its per-channel scales
+        const int blk = (kt * BK) / p.kblock - 1;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = wm * WTM + fm * 32 + (lane & 31);
-        a[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
-      }
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+          float sc[16];
+          if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
+          else {
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int row = wn * WTN + fn * 32 + (lane & 31);
-        if (TRB) {
-          typedef short v4s __attribute__((ext_vector_type(4)));
-          const int g = lane >> 4, jj = lane & 15, q4 = jj & 3;
-          const int col = wn * WTN + fn * 32 + 16 * (q4 & 1) + 8 * (g & 1) + 4 * (q4 >> 1);
-          v4s v[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int kr = ks * 16 + 8 * (g >> 1) + 4 * h + (jj >> 2);
-            const int addr = kr * (BN * 2) + ((((col >> 3) ^ ((kr & 3) << 2)) << 4) | ((col & 7) << 1));
-            v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s*)(B + addr));
+            for (int i = 0; i < 16; ++i) sc[i] = 0.f;
           }
-          b[fn] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-              v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]});
-        } else if (!FP8) {
-          b[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
-        } else {
-          const uint2 q = *reinterpret_cast<const uint2*>(
-              B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
-          b[fn] = widen_e4m3x8(q);
-        }
-      }
-    };
-    // a wave whose rows of the tile are all past the end of the segment (the upper half
-    // of an expert's last 256-row tile) skips its LDS reads and MFMAs
-    if (A8) {
-      if (wave_rows > 0) {
-        // two 32x32x64 e4m3 MFMA steps per block and slice: in step ks, lane half h holds K
-        // bytes [64 ks + 32 h, + 32) of its row in both operands (logical chunks 4 ks + 2 h
-        // and 4 ks + 2 h + 1); the operands of step 1 are read while step 0 multiplies
-        typedef int v8i __attribute__((ext_vector_type(8)));
-        const int h = lane >> 5;
-        auto frag8 = [&](const unsigned char* base, int row, int ks) {
-          const int z = swz8(row), c0 = 4 * ks + 2 * h;
-          const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ z) << 4));
-          const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ z) << 4));
-          return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        };
-        // B fragments of both steps and the A fragments of step 0 first; each A fragment of
-        // step 1 is read into its register once step 0's MFMAs of that fragment are issued
-        v8i a8[FM], b8[2][FN];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) b8[ks][fn] = frag8(B, wn * WTN + fn * 32 + (lane & 31), ks);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 0);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  b8[ks][fn], a8[fm], acc[fm][fn], 0, 0, 0, 127, 0, 127);
-            if (ks == 0) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 1);
+            for (int i = 0; i < 16; ++i) acc_tot[fm % TFM][fn % TFN][i] += sc[i] * acc[fm][fn][i];
+            acc[fm][fn] = f32x16{};
           }
         }
-        // instruction order: the two reads of A fragment fm of step 1 right after step 0's
-        // MFMAs of fm
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * FN + 2 * FM, 0);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
       }
-    } else {
-      // K-steps [k0, k1) of the slice: the LDS reads of step ks + 1 run behind the MFMAs of
-      // step ks, placed one by one between them by scheduling directives (left to itself
-      // the compiler issues some of them just before their first use)
-      auto mfma_steps = [&](auto k0_tag, auto k1_tag) {
-        constexpr int K0 = decltype(k0_tag)::value, K1 = decltype(k1_tag)::value;
-        if (K0 == 0) load_frags(0, af[0], bfr[0]);
-        __builtin_amdgcn_s_setprio(1);
+      const unsigned char* A = lds + cst * ST_BYTES;
+      const unsigned char* B = A + A_BYTES;
+      // operand fragments of K-step ks + 1 are read from LDS while the MFMAs of step ks run
+      bf16x8 af[2][FM], bfr[2][FN];
+      auto load_frags = [&](int ks, bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+        const int c = ks * 2 + (lane >> 5);
 #pragma unroll
-        for (int ks = K0; ks < K1; ++ks) {
-          if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
-                                                                    acc[fm][fn], 0, 0, 0);
+        for (int fm = 0; fm < NF; ++fm) {
+          const int row = wm * WTM + fm * 32 + (lane & 31);
+          a[fm] = *reinterpret_cast<const bf16x8*>(A + row * AROW + ((c ^ sw) << 4));
         }
-        constexpr int NDS = FM + (TRB ? 2 : 1) * FN, NMF = FM * FN;
-        constexpr int NPAIR = NDS < NMF ? NDS : NMF;
 #pragma unroll
-        for (int ks = K0; ks < K1; ++ks) {
-          if (ks + 1 < BK / 16) {
+        for (int fn = 0; fn < FN; ++fn) {
+          const int row = wn * WTN + fn * 32 + (lane & 31);
+          if (TRB) {
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            const int g = lane >> 4, jj = lane & 15, q4 = jj & 3;
+            const int col = wn * WTN + fn * 32 + 16 * (q4 & 1) + 8 * (g & 1) + 4 * (q4 >> 1);
+            v4s v[2];
 #pragma unroll
-            for (int i = 0; i < NPAIR; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int h = 0; h < 2; ++h) {
+              const int kr = ks * 16 + 8 * (g >> 1) + 4 * h + (jj >> 2);
+              const int addr = kr * (BN * 2) + ((((col >> 3) ^ ((kr & 3) << 2)) << 4) | ((col & 7) << 1));
+              v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4s*)(B + addr));
             }
-            if (NMF > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NPAIR, 0);
-            if (NDS > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NPAIR, 0);
+            b[fn] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]});
+          } else if (!FP8) {
+            b[fn] = *reinterpret_cast<const bf16x8*>(B + row * BROW + ((c ^ sw) << 4));
           } else {
-            __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+            const uint2 q = *reinterpret_cast<const uint2*>(
+                B + row * BROW + ((ks ^ swz4(row)) << 4) + ((lane >> 5) << 3));
+            b[fn] = widen_e4m3x8(q);
           }
         }
       };
-      using I0 = std::integral_constant<int, 0>;
-      using IE = std::integral_constant<int, BK / 16>;
-      if (wave_rows > 0) mfma_steps(I0{}, IE{});
-    }
-    __builtin_amdgcn_s_setprio(0);
-
-    if (kt == nk - 1) {
-      // ---- epilogue of tile j while the next tile's first slices are in flight
-      int pf_row = 0;
-      float pf_w = 0.f;
-      const bool pf = prefetch && j + 2 < ntiles && tid < BM;
-      if (pf) {
-        const int sr = seg_row(tile_at(j + 2), tid);
-        if (gather) pf_row = p.row_index[sr];
-        if (has_rw) pf_w = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
-      }
-      if (has_rw && !prefetch) {
-        // short K: this tile's row weights are staged here (buffer j3 was last read by the
-        // epilogue three tiles ago)
-        if (tid < BM) {
-          const int sr = seg_row(tc, tid);
-          s_rw[j3][tid] = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
-        }
-        __syncthreads();
-      }
-      const int m0 = tc.m_tile * BM;
-      // every load of the epilogue is issued before its first store, so that the waits
-      // for them do not also wait for stores
-      if (STAGE == 0) {
-        constexpr int FH = SWIGLU ? FN / 2 : FN;
-        float ra[FM];   // e4m3 activations: the scale of each lane's A row
+      // rows past the end of the segment (the padding of an expert's last m-tile) are not
+      // multiplied: in the specialised copies only the wave's first NF 32-row blocks are
+      // read and multiplied; otherwise a wave whose rows are all padding skips its LDS
+      // reads and MFMAs
+      if (A8) {
+        if (wave_rows > 0) {
+          // two 32x32x64 e4m3 MFMA steps per block and slice: in step ks, lane half h holds K
+          // bytes [64 ks + 32 h, + 32) of its row in both operands (logical chunks 4 ks + 2 h
+          // and 4 ks + 2 h + 1); the operands of step 1 are read while step 0 multiplies
+          typedef int v8i __attribute__((ext_vector_type(8)));
+          const int h = lane >> 5;
+          auto frag8 = [&](const unsigned char* base, int row, int ks) {
+            const int z = swz8(row), c0 = 4 * ks + 2 * h;
+            const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ z) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ z) << 4));
+            return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          };
+          // B fragments of both steps and the A fragments of step 0 first; each A fragment of
+          // step 1 is read into its register once step 0's MFMAs of that fragment are issued
+          v8i a8[FM], b8[2][FN];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) ra[fm] = (A8 && has_rw) ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
-        float sg[FH][16], su[FH][16];
-        if (FP8) {
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) b8[ks][fn] = frag8(B, wn * WTN + fn * 32 + (lane & 31), ks);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 0);
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    b8[ks][fn], a8[fm], acc[fm][fn], 0, 0, 0, 127, 0, 127);
+              if (ks == 0) a8[fm] = frag8(A, wm * WTM + fm * 32 + (lane & 31), 1);
+            }
+          }
+          // instruction order: the two reads of A fragment fm of step 1 right after step 0's
+          // MFMAs of fm
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * FN + 2 * FM, 0);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            __builtin_amdgcn_sched_group_barrier(0x008, FN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+        }
+      } else {
+        // K-steps [k0, k1) of the slice: the LDS reads of step ks + 1 run behind the MFMAs of
+        // step ks, placed one by one between them by scheduling directives (left to itself
+        // the compiler issues some of them just before their first use)
+        auto mfma_steps = [&](auto k0_tag, auto k1_tag) {
+          constexpr int K0 = decltype(k0_tag)::value, K1 = decltype(k1_tag)::value;
+          if (K0 == 0) load_frags(0, af[0], bfr[0]);
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ks = K0; ks < K1; ++ks) {
+            if (ks + 1 < BK / 16) load_frags(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+            for (int fm = 0; fm < NF; ++fm)
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][fn], af[ks & 1][fm],
+                                                                      acc[fm][fn], 0, 0, 0);
+          }
+          constexpr int NDS = NF + (TRB ? 2 : 1) * FN, NMF = NF * FN;
+          constexpr int NPAIR = NDS < NMF ? NDS : NMF;
+#pragma unroll
+          for (int ks = K0; ks < K1; ++ks) {
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+              for (int i = 0; i < NPAIR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              }
+              if (NMF > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NPAIR, 0);
+              if (NDS > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, NDS - NPAIR, 0);
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+            }
+          }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using IE = std::integral_constant<int, BK / 16>;
+        if constexpr (SPEC) {
+          if constexpr (NF > 0) mfma_steps(I0{}, IE{});
+        } else if (wave_rows > 0) {
+          mfma_steps(I0{}, IE{});
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+
+      if (kt == nk - 1) {
+        // ---- epilogue of tile j while the next tile's first slices are in flight
+        int pf_row = 0;
+        float pf_w = 0.f;
+        const bool pf = prefetch && j + 2 < ntiles && tid < BM;
+        if (pf) {
+          const int sr = seg_row(tile_at(j + 2), tid);
+          if (gather) pf_row = p.row_index[sr];
+          if (has_rw) pf_w = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
+        }
+        if (has_rw && !prefetch) {
+          // short K: this tile's row weights are staged here (buffer j3 was last read by the
+          // epilogue three tiles ago)
+          if (tid < BM) {
+            const int sr = seg_row(tc, tid);
+            s_rw[j3][tid] = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
+          }
+          __syncthreads();
+        }
+        const int m0 = tc.m_tile * BM;
+        // every load of the epilogue is issued before its first store, so that the waits
+        // for them do not also wait for stores
+        if (STAGE == 0) {
+          constexpr int FH = SWIGLU ? FN / 2 : FN;
+          float ra[FM];   // e4m3 activations: the scale of each lane's A row
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) ra[fm] = (A8 && has_rw) ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
+          float sg[FH][16], su[FH][16];
+          if (FP8) {
+#pragma unroll
+            for (int fh = 0; fh < FH; ++fh) {
+              const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
+                                      : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
+              const int hc = hcol < N ? hcol : 0;
+              load16_f32(p.s_gate + (size_t)tc.seg * N + hc, sg[fh]);
+              if (SWIGLU) load16_f32(p.s_up + (size_t)tc.seg * N + hc, su[fh]);
+            }
+          }
 #pragma unroll
           for (int fh = 0; fh < FH; ++fh) {
             const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
                                     : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
-            const int hc = hcol < N ? hcol : 0;
-            load16_f32(p.s_gate + (size_t)tc.seg * N + hc, sg[fh]);
-            if (SWIGLU) load16_f32(p.s_up + (size_t)tc.seg * N + hc, su[fh]);
-          }
-        }
+            if (hcol >= N) continue;
+            if (BWD) {
 #pragma unroll
-        for (int fh = 0; fh < FH; ++fh) {
-          const int hcol = SWIGLU ? tc.n_tile * (BN / 2) + wn * (WTN / 2) + fh * 32 + 16 * fhalf
-                                  : tc.n_tile * BN + wn * WTN + fh * 32 + 16 * fhalf;
-          if (hcol >= N) continue;
-          if (BWD) {
+              for (int fm = 0; fm < FM; ++fm) {
+                const int r = m0 + wm * WTM + fm * 32 + col_in;
+                if (r >= tc.rows) continue;
+                const size_t row = (size_t)(tc.row0 + r);
+                // dh of these 16 features (bf16)
+                const uint4* dsrc = reinterpret_cast<const uint4*>(
+                    static_cast<const uint16_t*>(p.dact) + row * N + hcol);
+                const uint4 d0 = dsrc[0], d1 = dsrc[1];
+                const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                float da[16], db[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const float dh = bf16_bits_to_f32((i & 1) ? (dw[i >> 1] >> 16) : (dw[i >> 1] & 0xffffu));
+                  const float a = acc[fm][fh][i];
+                  if (SWIGLU) {
+                    const float b = acc[fm][fh + FN / 2][i];
+                    const float sig = 1.0f / (1.0f + __expf(-a));
+                    da[i] = dh * b * (sig * (1.0f + a * (1.0f - sig)));   // silu'(a)
+                    db[i] = dh * (a * sig);                                // silu(a)
+                  } else {
+                    da[i] = dh * 2.0f * fmaxf(a, 0.f);
+                  }
+                }
+                uint16_t* o = static_cast<uint16_t*>(p.out) + row * (SWIGLU ? 2 * N : N);
+                store16_bf16(o + hcol, da);
+                if (SWIGLU) store16_bf16(o + N + hcol, db);
+              }
+              continue;
+            }
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
               const int r = m0 + wm * WTM + fm * 32 + col_in;
               if (r >= tc.rows) continue;
-              const size_t row = (size_t)(tc.row0 + r);
-              // dh of these 16 features (bf16)
-              const uint4* dsrc = reinterpret_cast<const uint4*>(
-                  static_cast<const uint16_t*>(p.dact) + row * N + hcol);
-              const uint4 d0 = dsrc[0], d1 = dsrc[1];
-              const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-              float da[16], db[16];
+              float h[16];
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
-                const float dh = bf16_bits_to_f32((i & 1) ? (dw[i >> 1] >> 16) : (dw[i >> 1] & 0xffffu));
-                const float a = acc[fm][fh][i];
                 if (SWIGLU) {
-                  const float b = acc[fm][fh + FN / 2][i];
-                  const float sig = 1.0f / (1.0f + __expf(-a));
-                  da[i] = dh * b * (sig * (1.0f + a * (1.0f - sig)));   // silu'(a)
-                  db[i] = dh * (a * sig);                                // silu(a)
+                  const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
+                  const float uv = FP8 ? acc[fm][fh + FN / 2][i] * (su[fh][i] * ra[fm]) : acc[fm][fh + FN / 2][i];
+                  h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
                 } else {
-                  da[i] = dh * 2.0f * fmaxf(a, 0.f);
+                  const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
+                  const float rr = fmaxf(gv, 0.f);
+                  h[i] = rr * rr;
                 }
               }
-              uint16_t* o = static_cast<uint16_t*>(p.out) + row * (SWIGLU ? 2 * N : N);
-              store16_bf16(o + hcol, da);
-              if (SWIGLU) store16_bf16(o + N + hcol, db);
+              store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + hcol, h);
             }
-            continue;
+          }
+        } else {
+          float rw[FM];
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) rw[fm] = has_rw ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
+          if (FP8) {
+            const int blk = nblk_k - 1;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+              float sc[16];
+              if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
+              else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+              }
+#pragma unroll
+              for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                  acc[fm][fn][i] = acc_tot[fm % TFM][fn % TFN][i] + sc[i] * acc[fm][fn][i];
+            }
           }
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) {
             const int r = m0 + wm * WTM + fm * 32 + col_in;
             if (r >= tc.rows) continue;
-            float h[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              if (SWIGLU) {
-                const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
-                const float uv = FP8 ? acc[fm][fh + FN / 2][i] * (su[fh][i] * ra[fm]) : acc[fm][fh + FN / 2][i];
-                h[i] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-              } else {
-                const float gv = FP8 ? acc[fm][fh][i] * (sg[fh][i] * ra[fm]) : acc[fm][fh][i];
-                const float rr = fmaxf(gv, 0.f);
-                h[i] = rr * rr;
-              }
+            for (int fn = 0; fn < FN; ++fn) {
+              const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
+              if (col >= N) continue;
+              float y[16];
+#pragma unroll
+              for (int i = 0; i < 16; ++i) y[i] = rw[fm] * acc[fm][fn][i];
+              store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + col, y);
             }
-            store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + hcol, h);
           }
+        }
+        // stores and loads may retire out of order with respect to each other: drain all
+        wait_vmcnt<0>();
+        if (pf) {
+          if (gather) s_arow[j & 1][tid] = pf_row;   // tile j + 2 has the parity of tile j
+          if (has_rw) s_rw[j3 == 0 ? 2 : j3 - 1][tid] = pf_w;   // (j + 2) mod 3
+        }
+        ++j;
+        j3 = j3 == 2 ? 0 : j3 + 1;
+        kt = 0;
+        if (j < ntiles) {
+          tc = tile_at(j);
+          wave_rows = rows_of_wave(tc);
         }
       } else {
-        float rw[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) rw[fm] = has_rw ? s_rw[j3][wm * WTM + fm * 32 + col_in] : 1.f;
-        if (FP8) {
-          const int blk = nblk_k - 1;
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
-            float sc[16];
-            if (col < N) load16_f32(p.s_down + ((size_t)tc.seg * nblk_k + blk) * N + col, sc);
-            else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                acc[fm][fn][i] = acc_tot[fm % TFM][fn % TFN][i] + sc[i] * acc[fm][fn][i];
-          }
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int r = m0 + wm * WTM + fm * 32 + col_in;
-          if (r >= tc.rows) continue;
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int col = tc.n_tile * BN + wn * WTN + fn * 32 + 16 * fhalf;
-            if (col >= N) continue;
-            float y[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[i] = rw[fm] * acc[fm][fn][i];
-            store16_bf16(static_cast<uint16_t*>(p.out) + (size_t)(tc.row0 + r) * N + col, y);
-          }
-        }
+        ++kt;
+        // slice g + 1 must have landed; younger slices may stay in flight
+        const int younger = min(NSTAGE - 2, nslices - 2 - g);
+        if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
+        else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
+        else wait_vmcnt<0>();
       }
-#pragma unroll
-      for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = f32x16{};
-#pragma unroll
-      for (int a = 0; a < TFM; ++a)
-#pragma unroll
-        for (int b = 0; b < TFN; ++b) acc_tot[a][b] = f32x16{};
-      // stores and loads may retire out of order with respect to each other: drain all
-      wait_vmcnt<0>();
-      if (pf) {
-        if (gather) s_arow[j & 1][tid] = pf_row;   // tile j + 2 has the parity of tile j
-        if (has_rw) s_rw[j3 == 0 ? 2 : j3 - 1][tid] = pf_w;   // (j + 2) mod 3
-      }
-      ++j;
-      j3 = j3 == 2 ? 0 : j3 + 1;
-      kt = 0;
-      if (j < ntiles) {
-        tc = tile_at(j);
-        wave_rows = rows_of_wave(tc);
-      }
-    } else {
-      ++kt;
-      // slice g + 1 must have landed; younger slices may stay in flight
-      const int younger = min(NSTAGE - 2, nslices - 2 - g);
-      if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
-      else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
-      else wait_vmcnt<0>();
+      cst = cst + 1 == NSTAGE ? 0 : cst + 1;
+      __syncthreads();
     }
-    cst = cst + 1 == NSTAGE ? 0 : cst + 1;
-    __syncthreads();
+  };
+  while (g < nslices) {
+    if constexpr (SPEC) {
+      const int nf = wave_rows <= 0 ? 0 : min(FM, (wave_rows + 31) / 32);
+      if (nf == FM) run_tile(std::integral_constant<int, FM>{});
+      else if (nf <= 0) run_tile(std::integral_constant<int, 0>{});
+      else if (nf == 1) run_tile(std::integral_constant<int, 1>{});
+      else if (nf == 2) run_tile(std::integral_constant<int, (FM > 2 ? 2 : 1)>{});
+      else run_tile(std::integral_constant<int, (FM > 3 ? 3 : 1)>{});
+    } else {
+      run_tile(std::integral_constant<int, FM>{});
+    }
   }
 }
 

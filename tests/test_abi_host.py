@@ -82,6 +82,8 @@ def test_workspace_size_is_the_sum_of_the_stages(lib):
     (dict(fp8_act=True, weight_dtype="e4m3", d=192), 2),   # ... and 128-byte K-slices
     (dict(fp8_act=True, weight_dtype="e4m3", I=1552), 2),  # ... and 64-wide output tiles
     (dict(pre_norm=True, norm_eps=float("nan")), 1), (dict(norm_eps=-1e-6), 1),
+    # the stacked shared experts' weights past 2^31 - 1 elements
+    (dict(T=64, E=8, G=8, Gk=2, k=2, S=64, d=4096, I=8192), 2),
 ])
 def test_invalid_configs_are_rejected_on_the_host(lib, bad, status):
     c = cfg(**bad)
