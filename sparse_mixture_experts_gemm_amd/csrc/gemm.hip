@@ -488,7 +488,8 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
       __builtin_amdgcn_s_setprio(0);
 
       if (kt == nk - 1) {
-        // ---- epilogue of tile j while the next tile's first slices are in flight
+        // ---- tile j's last slice: the per-row data of tile j + 2, the barrier, then the
+        // epilogue of tile j while the next tile's first slices are in flight
         int pf_row = 0;
         float pf_w = 0.f;
         const bool pf = prefetch && j + 2 < ntiles && tid < BM;
@@ -497,6 +498,16 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
           if (gather) pf_row = p.row_index[sr];
           if (has_rw) pf_w = p.row_weight[A8 && gather ? p.row_index[sr] : sr];
         }
+        // slice g + 1 and the loads above have landed; no store is in flight
+        wait_vmcnt<0>();
+        if (pf) {
+          if (gather) s_arow[j & 1][tid] = pf_row;   // tile j + 2 has the parity of tile j
+          if (has_rw) s_rw[j3 == 0 ? 2 : j3 - 1][tid] = pf_w;   // (j + 2) mod 3
+        }
+        cst = cst + 1 == NSTAGE ? 0 : cst + 1;
+        __syncthreads();
+        // The epilogue runs behind the barrier, so its stores complete while the next slice
+        // is multiplied; the next slice's wait (a full one on the 2-stage ring) covers them.
         if (has_rw && !prefetch) {
           // short K: this tile's row weights are staged here (buffer j3 was last read by the
           // epilogue three tiles ago)
@@ -618,12 +629,6 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
             }
           }
         }
-        // stores and loads may retire out of order with respect to each other: drain all
-        wait_vmcnt<0>();
-        if (pf) {
-          if (gather) s_arow[j & 1][tid] = pf_row;   // tile j + 2 has the parity of tile j
-          if (has_rw) s_rw[j3 == 0 ? 2 : j3 - 1][tid] = pf_w;   // (j + 2) mod 3
-        }
         ++j;
         j3 = j3 == 2 ? 0 : j3 + 1;
         kt = 0;
@@ -638,9 +643,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
         if (NSTAGE >= 4 && younger >= 2) wait_vmcnt<(NSTAGE >= 4 ? 2 * NDMA : 0)>();
         else if (NSTAGE >= 3 && younger >= 1) wait_vmcnt<(NSTAGE >= 3 ? NDMA : 0)>();
         else wait_vmcnt<0>();
+        cst = cst + 1 == NSTAGE ? 0 : cst + 1;
+        __syncthreads();
       }
-      cst = cst + 1 == NSTAGE ? 0 : cst + 1;
-      __syncthreads();
     }
   };
   while (g < nslices) {
