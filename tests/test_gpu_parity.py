@@ -662,6 +662,61 @@ def test_grouped_gemm_routed_every_row(name):
     assert bad_y.size == 0, f"down: {bad_y.size} rows off, first {bad_y[:8]}"
 
 
+# Segment sizes whose last tile ends at, and one row either side of, every 32-row block
+# boundary of a wave's rows (the tiled kernel runs one K-loop copy per count of live row
+# blocks), from one row to past a full tile, plus an empty segment.
+BLOCK_EDGE_ROWS = [0, 1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 161, 191,
+                   192, 193, 223, 224, 225, 255, 256, 257, 289, 320, 353, 384, 417, 448, 481, 512]
+
+
+@pytest.mark.parametrize("case", ["wide", "narrow"])
+def test_grouped_gemm_row_block_edges(case):
+    """Routed UP and DOWN GEMMs on segments sized to every 32-row block edge of a tile's last
+    m-tile, with gathered rows and routing weights; every output row against the oracle's
+    expert FFN.  "wide": d = 2048, I = 1024 and 512 more rows per segment, so both stages
+    take 256 x 256 tiles (four 32-row blocks per wave); "narrow": d = I = 256 and the
+    sizes as listed, 128 x 256 tiles (two blocks per wave)."""
+    wide = case == "wide"
+    sizes = [r + (512 if wide else 0) for r in BLOCK_EDGE_ROWS]
+    E = len(sizes)
+    d, I = (2048, 1024) if wide else (256, 256)
+    s = W.small_shape(T=4096, d=d, E=E, k=1, G=1, Gk=1, S=0, I=I, seed=67 if wide else 68)
+    lay = W.make_layer(s, cache=False)
+    wts = weights(lay)
+    cfg = config(s)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    rng = np.random.default_rng(69)
+    row_index = rng.integers(0, s.T, size=rows).astype(np.int32)
+    rw = rng.uniform(0.05, 1.0, size=rows).astype(np.float32)
+    h = act_empty((rows, I), s.act_dtype)
+    print(f"case {case}: {E} segments, {rows} rows", flush=True)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, to_dev(lay.x),
+                     to_dev(row_index), to_dev(offsets), rows, wts, None, h)
+    h_in = W.random_act((rows, I), seed=70, dtype=s.act_dtype, std=0.5)
+    y = act_empty((rows, d), s.act_dtype)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, to_dev(h_in), None,
+                     to_dev(offsets), rows, wts, to_dev(rw), y)
+    torch.cuda.synchronize()
+    got_h = act_to_f64(h, s.act_dtype)
+    got_y = act_to_f64(y, s.act_dtype)
+    x64 = O.decode_act(lay.x, s.act_dtype)
+    h64 = O.decode_act(h_in, s.act_dtype)
+    ref_h = np.zeros((rows, I))
+    ref_y = np.zeros((rows, d))
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            ref_h[a:b] = O.expert_up(x64[row_index[a:b]], *_dense(lay, "up", e), s.act)
+            ref_y[a:b] = rw[a:b].astype(np.float64)[:, None] * O.expert_down(h64[a:b], _dense(lay, "down", e))
+    eh = np.abs(got_h - ref_h).max(axis=1)
+    ey = np.abs(got_y - ref_y).max(axis=1)
+    bad_h = np.nonzero(eh > TOL[s.act_dtype] * np.max(np.abs(ref_h)))[0]
+    bad_y = np.nonzero(ey > TOL[s.act_dtype] * np.max(np.abs(ref_y)))[0]
+    assert bad_h.size == 0, f"up: {bad_h.size} rows off, first {bad_h[:8]}"
+    assert bad_y.size == 0, f"down: {bad_y.size} rows off, first {bad_y[:8]}"
+
+
 @pytest.mark.parametrize("name", ["small_swiglu", "small_relu2_e4m3", "small_f32", "fusionllm_bf16",
                                   "fp8_relu2", "multi_tile_swiglu", "short_k"])
 def test_grouped_gemm_shared(name):
