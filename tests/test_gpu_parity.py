@@ -99,6 +99,16 @@ SMALL = {
     "tail_multi": W.small_shape(T=16384, d=200, E=8, k=4, G=1, Gk=1, S=1, I=136, seed=65),
     "tail_prenorm": W.small_shape(T=150, d=200, E=16, k=4, G=4, Gk=2, S=1, I=136,
                                   pre_norm=True, residual=True, seed=66),
+    # ReLU^2 with bf16 weights on every GEMM family (tiled, weight-streaming, tail), and
+    # SwiGLU with e4m3 weights on the weight-streaming one
+    "small_relu2_bf16": W.small_shape(T=300, d=256, E=16, k=4, G=4, Gk=2, S=1, I=256,
+                                      act="relu2", seed=81),
+    "decode_relu2_bf16": W.small_shape(T=40, d=256, E=16, k=4, G=4, Gk=2, S=1, I=256,
+                                       act="relu2", seed=82),
+    "decode_swiglu_e4m3": W.small_shape(T=48, d=256, E=16, k=4, G=4, Gk=2, S=1, I=256,
+                                        weight_dtype="e4m3", seed=83),
+    "tail_relu2_bf16": W.small_shape(T=200, d=200, E=8, k=2, G=2, Gk=1, S=1, I=136,
+                                     act="relu2", seed=84),
 }
 
 
@@ -565,7 +575,8 @@ def _dense(lay, which, e, shared=False):
 
 GEMM_CASES = ["small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32", "tiny_fp32",
               "single_token", "fusionllm_bf16", "fp8_relu2", "tail_bf16", "tail_e4m3",
-              "tail_relu2_e4m3", "tail_d_only", "tail_i_only"]
+              "tail_relu2_e4m3", "tail_d_only", "tail_i_only", "small_relu2_bf16",
+              "decode_relu2_bf16", "decode_swiglu_e4m3", "tail_relu2_bf16"]
 
 
 @pytest.mark.parametrize("name", GEMM_CASES)
@@ -837,7 +848,8 @@ FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "f
                  "single_token", "topk1_nogroups", "balance_bf16", "biased_softmax_f32",
                  "biased_groups_n2", "fp8a_relu2", "small_a8_swiglu", "multi_tile_a8_relu2",
                  "all_experts", "tail_bf16", "tail_e4m3", "tail_relu2_e4m3", "tail_d_only",
-                 "tail_i_only", "tail_multi"]
+                 "tail_i_only", "tail_multi", "small_relu2_bf16", "decode_relu2_bf16",
+                 "decode_swiglu_e4m3", "tail_relu2_bf16"]
 
 
 def run_forward(name):
