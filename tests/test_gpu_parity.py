@@ -51,6 +51,10 @@ SMALL = {
     "multi_tile_wide": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512, seed=40),
     "multi_tile_wide_e4m3": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1, I=512,
                                           act="relu2", weight_dtype="e4m3", seed=52),
+    "multi_tile_wide_swiglu_e4m3": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1,
+                                                 I=512, weight_dtype="e4m3", seed=85),
+    "multi_tile_wide_relu2_bf16": W.small_shape(T=16384, d=512, E=8, k=4, G=1, Gk=1, S=1,
+                                                I=1024, act="relu2", seed=86),
     # selection-only expert bias: softmax gating (fp32) and n_g = 2 groups (bf16)
     "biased_softmax_f32": W.small_shape(T=257, d=128, E=16, k=3, score="softmax", G=1, Gk=1,
                                         S=0, I=64, act_dtype="f32", weight_dtype="f32",
@@ -634,7 +638,8 @@ def test_grouped_gemm_down_routed(name):
 
 
 @pytest.mark.parametrize("name", ["multi_tile_swiglu", "multi_tile_relu2_e4m3", "short_k",
-                                  "multi_tile_wide", "multi_tile_wide_e4m3"])
+                                  "multi_tile_wide", "multi_tile_wide_e4m3",
+                                  "multi_tile_wide_swiglu_e4m3", "multi_tile_wide_relu2_bf16"])
 def test_grouped_gemm_routed_every_row(name):
     """Up and down routed GEMMs with several tiles per workgroup, every output row checked."""
     s = shape_of(name)
