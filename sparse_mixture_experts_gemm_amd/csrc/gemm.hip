@@ -111,7 +111,9 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   static_assert(NDMA * (NSTAGE - 2) < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row when per-row data is staged");
   // forward bf16-activation tiles: per-tile copies of the K-loop for 0 .. FM live row blocks
-  constexpr bool SPEC = !A8 && !BWD && !TRB && !FP8;
+  // (with e4m3 weights, up projection only, and only for none, half or all of them: more
+  // copies spill registers, and the down projections measured no gain)
+  constexpr bool SPEC = !A8 && !BWD && !TRB && (!FP8 || STAGE == 0);
   static_assert(!SPEC || FM == 2 || FM == 4, "row-block specialisation");
 
   __shared__ __align__(1024) unsigned char lds[NSTAGE * ST_BYTES];
@@ -651,11 +653,17 @@ __global__ __launch_bounds__(WAVES * 64, OCC) void gg_mfma_kernel(GemmParams p) 
   while (g < nslices) {
     if constexpr (SPEC) {
       const int nf = wave_rows <= 0 ? 0 : min(FM, (wave_rows + 31) / 32);
-      if (nf == FM) run_tile(std::integral_constant<int, FM>{});
-      else if (nf <= 0) run_tile(std::integral_constant<int, 0>{});
-      else if (nf == 1) run_tile(std::integral_constant<int, 1>{});
-      else if (nf == 2) run_tile(std::integral_constant<int, (FM > 2 ? 2 : 1)>{});
-      else run_tile(std::integral_constant<int, (FM > 3 ? 3 : 1)>{});
+      if constexpr (FP8) {
+        if (nf > FM / 2) run_tile(std::integral_constant<int, FM>{});
+        else if (nf > 0) run_tile(std::integral_constant<int, FM / 2>{});
+        else run_tile(std::integral_constant<int, 0>{});
+      } else {
+        if (nf == FM) run_tile(std::integral_constant<int, FM>{});
+        else if (nf <= 0) run_tile(std::integral_constant<int, 0>{});
+        else if (nf == 1) run_tile(std::integral_constant<int, 1>{});
+        else if (nf == 2) run_tile(std::integral_constant<int, (FM > 2 ? 2 : 1)>{});
+        else run_tile(std::integral_constant<int, (FM > 3 ? 3 : 1)>{});
+      }
     } else {
       run_tile(std::integral_constant<int, FM>{});
     }
