@@ -1002,6 +1002,36 @@ def test_forward_is_deterministic(name):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("name", ["small_swiglu", "decode_bf16", "fusionllm_bf16"])
+def test_forwards_on_two_streams_match_serial(name):
+    """Two forwards on different inputs, enqueued together on two caller streams (each with
+    its own second stream for the shared experts), three times in a row, equal the same
+    forwards run one after the other, bit for bit."""
+    s = shape_of(name)
+    lay = layer_of(name)
+    wts = weights(lay)
+    cfg = config(s)
+    x1 = to_dev(lay.x)
+    x2 = torch.flip(x1, dims=[0]).contiguous()   # the same rows in reverse token order
+    refs = []
+    for x in (x1, x2):
+        out = act_empty((s.T, s.d), s.act_dtype)
+        moe.forward(cfg, wts, x, out, workspace(cfg))
+        refs.append(out)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [workspace(cfg), workspace(cfg)]
+    outs = [act_empty((s.T, s.d), s.act_dtype) for _ in range(2)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, x in enumerate((x1, x2)):
+            with torch.cuda.stream(streams[i]):
+                moe.forward(cfg, wts, x, outs[i], wss[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], refs[i]), f"{name}: stream {i}, repetition {rep}"
+
+
 def test_forward_error_paths_enqueue_nothing():
     s = shape_of("small_swiglu")
     lay = layer_of("small_swiglu")
