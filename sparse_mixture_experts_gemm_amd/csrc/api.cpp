@@ -636,7 +636,10 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
                                      cus, side);
-      if (e == hipSuccess) e = hipEventRecord(join, side);
+      // recorded also after an error, so that the wait on it below orders whatever the side
+      // stream took before the caller's next work (which may free the workspace)
+      const hipError_t re = hipEventRecord(join, side);
+      if (e == hipSuccess) e = re;
     }
     if (!pre) route();
     if (e == hipSuccess)
@@ -662,7 +665,6 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
                                     with_shared ? &dn_s : nullptr);
       mark(5);
       mark(6);
-      if (fork && e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
     } else if (fork) {
       // routed GEMMs here, shared GEMMs on the side stream since the start of the forward
       if (e == hipSuccess)
@@ -671,7 +673,6 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(dn_r, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
                                      cus, stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(stream, join, 0);
     } else {
       if (e == hipSuccess)
         e = moe::launch_grouped_gemm(up_r, moe::Stage::Up, cfg->act, adt, cfg->weight_dtype, cus,
@@ -689,6 +690,11 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
         e = moe::launch_grouped_gemm(dn_s, moe::Stage::Down, cfg->act, adt, cfg->weight_dtype,
                                      cus, stream);
       mark(6);
+    }
+    if (fork) {
+      // also after an error: the side stream's work is ordered before what follows
+      const hipError_t we = hipStreamWaitEvent(stream, join, 0);
+      if (e == hipSuccess) e = we;
     }
     if (e == hipSuccess)
       e = moe::launch_combine(T, cfg->dim, cfg->top_k, adt, at(cv.y_routed), slot_pos,
