@@ -933,6 +933,70 @@ def test_forward_prenorm_matches_oracle(name):
     assert np.all(err <= bound)
 
 
+def random_shape(seed):
+    """A seeded layer drawn from what the boundary accepts: any dtype pairing, activation,
+    scoring, grouping (n_g of 1 or 2), k up to the eligible experts, shared experts, a
+    capacity, a selection bias, the pre-norm step, tokens from 1 to 2500, and dim / inter
+    dim on their grids (multiples of 8 for bf16 weights, 16 for e4m3 or fp32, 128 / 64 with
+    e4m3 activations; half of them on the 64-element grid)."""
+    g = np.random.default_rng(7000 + seed)
+    kind = ("bf16", "e4m3", "f32", "a8")[seed % 4]
+    E = int(g.choice([4, 8, 16, 32, 64]))
+    G = int(g.choice([x for x in (1, 2, 4, 8) if E % x == 0]))
+    Gk = int(g.integers(1, G + 1))
+    n_g = int(g.choice([1, 2])) if E // G >= 2 else 1
+    k = int(g.integers(1, min(Gk * (E // G), 8) + 1))
+    if kind == "a8":
+        d, I = 128 * int(g.integers(1, 4)), 64 * int(g.integers(1, 7))
+    else:
+        # half of the layers on the 64-element grid of the tiled kernels
+        q = 64 if g.random() < 0.5 else (8 if kind == "bf16" else 16)
+        d, I = q * int(g.integers(-(-48 // q), 512 // q + 1)), q * int(g.integers(-(-32 // q), 384 // q + 1))
+    pre = bool(g.random() < 0.3)
+    return W.small_shape(
+        T=int(g.choice([1, 5, 33, 64, 100, 257, 600, 1100, 2500])), d=d, E=E, k=k, G=G, Gk=Gk,
+        n_g=n_g, S=int(g.integers(0, 3)), I=I, score=str(g.choice(["sigmoid", "softmax"])),
+        act=str(g.choice(["swiglu", "relu2"])),
+        act_dtype="f32" if kind == "f32" else "bf16",
+        weight_dtype={"bf16": "bf16", "f32": "f32"}.get(kind, "e4m3"), fp8_act=kind == "a8",
+        renormalize=bool(g.integers(0, 2)), route_scale=float(g.choice([1.0, 2.5])),
+        capacity_factor=float(g.choice([0.5, 1.0, 1.5])) if g.random() < 0.3 else None,
+        select_bias_std=0.5 if g.random() < 0.3 else None,
+        pre_norm=pre, residual=pre and bool(g.integers(0, 2)), seed=900 + seed)
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_forward_random_configs(seed):
+    """The whole forward on seeded random layers: routing against the free-running oracle
+    (identical away from near ties), every output row against the oracle run under the
+    GPU's routing, to the same bars as the fixed cases."""
+    s = random_shape(seed)
+    print(s)
+    lay = W.make_layer(s, cache=False)
+    cfg = config(s)
+    wts = weights(lay)
+    ws = workspace(cfg)
+    x = to_dev(lay.x)
+    out = act_empty((s.T, s.d), s.act_dtype)
+    moe.forward(cfg, wts, x, out, ws)
+    torch.cuda.synchronize()
+    gpu_idx = ws[: s.T * s.k * 4].view(torch.int32).cpu().numpy().reshape(s.T, s.k)
+    if s.pre_norm:
+        check_forward_routing(s, lay, gpu_idx, x=O.normalized_input(lay), margin=PRENORM_MARGIN)
+    else:
+        check_forward_routing(s, lay, gpu_idx)
+    ref = O.moe_forward(lay, idx=gpu_idx)
+    got = act_to_f64(out, s.act_dtype)
+    moe_part = ref["out"] - (O.decode_act(lay.x, s.act_dtype) if s.residual else 0.0)
+    scale = np.max(np.abs(moe_part))
+    bound = TOL[s.act_dtype] * scale
+    if s.residual:
+        bound = bound + 0.5 * _ulp(np.maximum(np.abs(got), np.abs(ref["out"])), s.act_dtype)
+    err = np.abs(got - ref["out"])
+    print(f"seed {seed}: max|d|/max|moe part| = {np.max(err) / max(scale, 1e-300):.3e}")
+    assert np.all(err <= bound)
+
+
 @pytest.mark.parametrize("name", ["balance_bf16", "small_f32"])
 def test_forward_load_stats_match_oracle(name):
     """The statistics moe_forward_ex writes for its own routing: f from the GPU routing
