@@ -358,8 +358,9 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
  *     logits; d_router = dl^T x, d_logit_bias = sum_t dl, dx += dl W_r;
  *   residual: dx += dout.
  * The shared experts' chain runs on the side stream of moe_forward (same rules).
- * Supported: act_dtype and weight_dtype MOE_BF16, no pre_norm, no fp8_act, route_scale != 0
- * (else MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARG).  dout [T, d] bf16.  Weight gradients
+ * Supported: act_dtype and weight_dtype MOE_BF16, dim and inter_dim multiples of 64, no
+ * pre_norm, no fp8_act, route_scale != 0 (else MOE_ERR_UNSUPPORTED / MOE_ERR_INVALID_ARG).
+ * dout [T, d] bf16.  Weight gradients
  * accumulate in fp32 over the tokens in a fixed order; the result is deterministic.
  * Source: the chain rule through the forward of moe_forward; the router gradient through
  * the logits follows item 4 of section "常见陷阱" of "大模型工程（一）：Transformer 到 MoE". */

@@ -96,6 +96,52 @@ def test_backward_matches_oracle(name):
         assert diff <= TOL * scale, field
 
 
+def random_backward_shape(seed):
+    """A seeded layer inside the backward's contract (bf16, dim and inter dim on the
+    64-grid, no pre-norm or e4m3 activations): any activation, scoring, grouping, k up to
+    the eligible experts, 0-2 shared experts, capacity, selection bias, residual, route
+    scale, and 1 to 2500 tokens."""
+    g = np.random.default_rng(8000 + seed)
+    E = int(g.choice([4, 8, 16, 32, 64]))
+    G = int(g.choice([x for x in (1, 2, 4, 8) if E % x == 0]))
+    Gk = int(g.integers(1, G + 1))
+    n_g = int(g.choice([1, 2])) if E // G >= 2 else 1
+    return W.small_shape(
+        T=int(g.choice([1, 5, 33, 64, 100, 257, 600, 1100, 2500])), d=64 * int(g.integers(1, 9)),
+        E=E, k=int(g.integers(1, min(Gk * (E // G), 8) + 1)), G=G, Gk=Gk, n_g=n_g,
+        S=int(g.integers(0, 3)), I=64 * int(g.integers(1, 7)),
+        score=str(g.choice(["sigmoid", "softmax"])), act=str(g.choice(["swiglu", "relu2"])),
+        renormalize=bool(g.integers(0, 2)), route_scale=float(g.choice([1.0, 2.5])),
+        capacity_factor=float(g.choice([0.5, 1.0, 1.5])) if g.random() < 0.3 else None,
+        select_bias_std=0.5 if g.random() < 0.3 else None, residual=bool(g.integers(0, 2)),
+        seed=950 + seed)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_backward_random_configs(seed):
+    """Every gradient on seeded random layers, against the fp64 backward oracle under the
+    forward's checked selection, at the bar of the fixed cases."""
+    s = random_backward_shape(seed)
+    print(s)
+    lay = W.make_layer(s, cache=False)
+    cfg, wts, ws, x, dout, dout_np, grads, bws, gpu_idx = run_backward(s, lay)
+    idx = checked_selection(s, lay, gpu_idx)
+    ref = O.backward.moe_backward(lay, O.decode_bf16(dout_np), idx=idx)
+    # k = 1 with renormalised weights: the weight c s / s is constant, so the router
+    # gradient is exactly zero and both sides hold rounding residue only
+    no_router_grad = s.renormalize and s.k == 1
+    for field, t in grads.items():
+        want = ref[NAMES[field]]
+        got = act_to_f64(t, "bf16") if field == "dx" else t.cpu().numpy().astype(np.float64)
+        scale = np.max(np.abs(want))
+        diff = np.max(np.abs(got - want))
+        print(f"seed {seed} {field}: max|d| = {diff:.3e}, max|ref| = {scale:.3e}")
+        if scale == 0 or (no_router_grad and field in ("d_router", "d_logit_bias")):
+            assert diff <= 1e-4, field     # an exactly zero gradient (also: every slot dropped)
+        else:
+            assert diff <= TOL * scale, field
+
+
 def test_backward_with_a_selected_expert_of_zero_weight():
     """Expert 3's logit is offset by -200, so its fp32 sigmoid score (and weight) is exactly
     0, and a selection-only bias of +1000 makes every token pick it anyway.  The exact
