@@ -478,6 +478,24 @@ def test_permute_edge_cases(T, E, k, pattern):
     _check_permute(T, E, k, idx, w)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_permute_random_bit_exact(seed):
+    """Seeded random routings (1 to 20000 tokens, 1 to 64 experts, k up to E, uniform or
+    Zipf-skewed expert popularity, with and without a capacity) on both the one-launch and
+    the two-launch path: every map bit-exact against the oracle's permutation."""
+    g = np.random.default_rng(5000 + seed)
+    T = int(g.choice([1, 2, 31, 64, 500, 1024, 1025, 3000, 20000]))
+    E = int(g.choice([1, 3, 8, 16, 33, 64]))
+    k = int(g.integers(1, min(E, 8) + 1))
+    logp = -float(g.choice([0.0, 1.2])) * np.log1p(np.arange(E))     # Zipf exponent 0 or 1.2
+    keys = logp[None, :] - np.log(-np.log(g.random((T, E))))          # Gumbel top-k
+    idx = np.argsort(-keys, axis=1)[:, :k].astype(np.int32)
+    w = g.random((T, k)).astype(np.float32)
+    cf = float(g.choice([0.0, 0.0, 0.25, 1.0, 1.5]))
+    print(f"T={T} E={E} k={k} capacity_factor={cf}")
+    _check_permute(T, E, k, idx, w, capacity_factor=cf)
+
+
 @pytest.mark.parametrize("T", [300, 3000])
 def test_permute_skips_out_of_range_ids_and_combine_ignores_them(T):
     """Padding ids (-1 and E) in topk_idx get no row and slot_pos -1, on the one-launch
