@@ -261,6 +261,40 @@ def test_select_bit_exact_on_tie_laden_scores(E, k, G, Gk, n_g):
     assert np.allclose(w.cpu().numpy()[ok], ref_w[ok], rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_select_random_bit_exact(seed):
+    """Seeded random selection problems: any E up to 64 with any group count dividing it,
+    Gk, n_g in {1, 2}, k up to the eligible experts, continuous or tie-laden (eighths)
+    scores, with or without separate selection keys, renormalised or scaled weights:
+    indices bit-exact against the oracle's selection, weights within 2e-6."""
+    g = np.random.default_rng(6000 + seed)
+    E = int(g.integers(1, 65))
+    G = int(g.choice([x for x in range(1, E + 1) if E % x == 0]))
+    Gk = int(g.integers(1, G + 1))
+    n_g = int(g.choice([1, 2])) if E // G >= 2 else 1
+    k = int(g.integers(1, Gk * (E // G) + 1))
+    T = int(g.choice([1, 7, 100, 1000, 5000]))
+    ties = bool(g.integers(0, 2))
+    draw = lambda: ((g.integers(0, 8, size=(T, E)) / 8.0) if ties else g.random((T, E))).astype(np.float32)
+    sc = draw()
+    # keys, like scores, are >= 0 (the selection's contract)
+    keys = ((sc + draw()) * np.float32(0.5)).astype(np.float32) if g.random() < 0.5 else None
+    renorm, scale = bool(g.integers(0, 2)), float(g.choice([1.0, 2.5]))
+    print(f"T={T} E={E} G={G} Gk={Gk} n_g={n_g} k={k} ties={ties} keys={keys is not None}")
+    cfg = moe.make_config(T, 64, E, k, G=G, Gk=Gk, n_g=n_g, I=64, renormalize=renorm,
+                          route_scale=scale)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.select(cfg, to_dev(sc), None if keys is None else to_dev(keys), idx, w)
+    torch.cuda.synchronize()
+    ref = O.select_experts(sc if keys is None else keys, k, G, Gk, n_g)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ref_w = O.routing_weights(sc.astype(np.float64), ref, renorm, scale)
+    ok = np.all(np.isfinite(ref_w), axis=1)        # a renormalised all-zero selection has no weights
+    assert np.allclose(w.cpu().numpy()[ok], ref_w[ok], rtol=2e-6, atol=1e-7)
+
+
 # ----------------------------------------------------------------------------- route
 ROUTE_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                "small_swiglu", "small_f32", "single_token", "topk1_nogroups", "balance_bf16",
