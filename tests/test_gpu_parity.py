@@ -312,8 +312,10 @@ def test_route_matches_oracle(name):
     (3) against the free-running fp64 oracle: identical indices wherever the fp64 decision
         margin exceeds the fp32 score error; closer tokens must still be a valid top-k
         within that margin (informational count printed)."""
-    s = shape_of(name)
-    lay = layer_of(name)
+    _check_route(shape_of(name), layer_of(name), name)
+
+
+def _check_route(s, lay, name):
     cfg = config(s)
     T = s.T
     scores = torch.empty((T, s.E), dtype=torch.float32, device="cuda")
@@ -354,6 +356,30 @@ def test_route_matches_oracle(name):
           f"oracle ({int((~clear).sum())} within the fp32 margin)")
     same = (g_idx == r["idx"]).all(axis=1)
     assert np.allclose(g_w[same], r["w"][same], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_route_random(seed):
+    """The routing protocol of moe_route on seeded random layers: bf16 or fp32, dim on or
+    off the 32-element K-step (up to 4160), any E up to 64 with any group count dividing
+    it, n_g in {1, 2}, k up to the eligible experts, sigmoid or softmax, a logit bias, a
+    selection-only bias, and 1 to 3000 tokens."""
+    g = np.random.default_rng(4000 + seed)
+    f32 = bool(g.random() < 0.3)
+    E = int(g.integers(2, 65))
+    G = int(g.choice([x for x in range(1, E + 1) if E % x == 0]))
+    Gk = int(g.integers(1, G + 1))
+    s = W.small_shape(
+        T=int(g.choice([1, 15, 16, 17, 300, 3000])),
+        d=(16 if f32 else 8) * int(g.integers(2, 4160 // (16 if f32 else 8) + 1)), E=E,
+        k=int(g.integers(1, min(Gk * (E // G), 8) + 1)), G=G, Gk=Gk,
+        n_g=int(g.choice([1, 2])) if E // G >= 2 else 1, S=0, I=64,
+        score=str(g.choice(["sigmoid", "softmax"])), renormalize=bool(g.integers(0, 2)),
+        route_scale=float(g.choice([1.0, 2.5])), act_dtype="f32" if f32 else "bf16",
+        weight_dtype="f32" if f32 else "bf16",
+        select_bias_std=0.5 if g.random() < 0.3 else None, seed=800 + seed)
+    print(s)
+    _check_route(s, W.make_layer(s, cache=False), f"seed {seed}")
 
 
 # ----------------------------------------------------------------------------- pre-norm routing
