@@ -811,6 +811,63 @@ def test_grouped_gemm_row_block_edges(case):
     assert bad_y.size == 0, f"down: {bad_y.size} rows off, first {bad_y[:8]}"
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_grouped_gemm_random_segments(seed):
+    """Routed UP (gathered rows) and DOWN (routing weights) on seeded random segment lists:
+    1 to 64 segments whose sizes mix empty, decode-sized and multi-tile ones; bf16, e4m3 or
+    fp32 weights; SwiGLU or ReLU^2; dim and inter dim on or off the 64-grid.  Every output
+    row against the oracle's expert FFN."""
+    g = np.random.default_rng(3000 + seed)
+    kind = ("bf16", "e4m3", "f32")[seed % 3]
+    q = 64 if g.random() < 0.5 else (8 if kind == "bf16" else 16)
+    d = q * int(g.integers(-(-64 // q), 384 // q + 1))
+    I = q * int(g.integers(-(-64 // q), 384 // q + 1))
+    E = int(g.integers(1, 65))
+    sizes = np.where(g.random(E) < 0.2, 0,
+                     np.where(g.random(E) < 0.4, g.integers(1, 40, E), g.integers(1, 1500, E)))
+    sizes = (sizes * min(1.0, 12000 / max(1, sizes.sum()))).astype(np.int64)
+    s = W.small_shape(T=2000, d=d, E=E, k=1, G=1, Gk=1, S=0, I=I,
+                      act=str(g.choice(["swiglu", "relu2"])),
+                      act_dtype="f32" if kind == "f32" else "bf16", weight_dtype=kind,
+                      seed=700 + seed)
+    lay = W.make_layer(s, cache=False)
+    wts = weights(lay)
+    cfg = config(s)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    print(f"{kind} {s.act} d={d} I={I} E={E} rows={rows} "
+          f"paths up/down {moe.gemm_kernel_path(cfg, 0, 0, rows)}/{moe.gemm_kernel_path(cfg, 1, 0, rows)}")
+    row_index = g.integers(0, s.T, size=max(rows, 1)).astype(np.int32)
+    rw = g.uniform(0.05, 1.0, size=max(rows, 1)).astype(np.float32)
+    h = act_empty((max(rows, 1), I), s.act_dtype)
+    y = act_empty((max(rows, 1), d), s.act_dtype)
+    h_in = W.random_act((max(rows, 1), I), seed=710 + seed, dtype=s.act_dtype, std=0.5)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_UP, moe.MOE_EXPERTS_ROUTED, to_dev(lay.x),
+                     to_dev(row_index), to_dev(offsets), rows, wts, None, h)
+    moe.grouped_gemm(cfg, moe.MOE_STAGE_DOWN, moe.MOE_EXPERTS_ROUTED, to_dev(h_in), None,
+                     to_dev(offsets), rows, wts, to_dev(rw), y)
+    torch.cuda.synchronize()
+    if rows == 0:
+        return
+    got_h = act_to_f64(h, s.act_dtype)[:rows]
+    got_y = act_to_f64(y, s.act_dtype)[:rows]
+    x64 = O.decode_act(lay.x, s.act_dtype)
+    h64 = O.decode_act(h_in, s.act_dtype)[:rows]
+    ref_h = np.zeros((rows, I))
+    ref_y = np.zeros((rows, d))
+    for e in range(E):
+        a, b = offsets[e], offsets[e + 1]
+        if b > a:
+            ref_h[a:b] = O.expert_up(x64[row_index[a:b]], *_dense(lay, "up", e), s.act)
+            ref_y[a:b] = rw[a:b].astype(np.float64)[:, None] * O.expert_down(h64[a:b], _dense(lay, "down", e))
+    eh = np.abs(got_h - ref_h).max(axis=1)
+    ey = np.abs(got_y - ref_y).max(axis=1)
+    bad_h = np.nonzero(eh > TOL[s.act_dtype] * np.max(np.abs(ref_h)))[0]
+    bad_y = np.nonzero(ey > TOL[s.act_dtype] * np.max(np.abs(ref_y)))[0]
+    assert bad_h.size == 0, f"up: {bad_h.size} rows off, first {bad_h[:8]}"
+    assert bad_y.size == 0, f"down: {bad_y.size} rows off, first {bad_y[:8]}"
+
+
 @pytest.mark.parametrize("name", ["small_swiglu", "small_relu2_e4m3", "small_f32", "fusionllm_bf16",
                                   "fp8_relu2", "multi_tile_swiglu", "short_k"])
 def test_grouped_gemm_shared(name):
