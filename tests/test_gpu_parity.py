@@ -982,6 +982,56 @@ def test_combine(name, with_shared, cf):
     assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_combine_random(seed):
+    """Seeded random slot maps (any T, k and dim on the 8 / 16 grid, slots dropped at random,
+    with and without a shared row, bf16 or fp32): the fixed-order sum against the oracle's
+    combine, one output rounding."""
+    g = np.random.default_rng(2000 + seed)
+    dt = "f32" if seed % 3 == 2 else "bf16"
+    T = int(g.choice([1, 3, 64, 777, 5000]))
+    k = int(g.integers(1, 13))
+    d = (16 if dt == "f32" else 8) * int(g.integers(1, 520 // (16 if dt == "f32" else 8) + 1))
+    slot_pos = g.permutation(T * k).astype(np.int32)
+    slot_pos[g.random(T * k) < float(g.choice([0.0, 0.2, 0.9]))] = -1
+    y = W.random_act((T * k, d), seed=2100 + seed, dtype=dt)
+    ysh = W.random_act((T, d), seed=2200 + seed, dtype=dt) if g.random() < 0.5 else None
+    print(f"{dt} T={T} k={k} d={d} dropped={int((slot_pos < 0).sum())} shared={ysh is not None}")
+    cfg = moe.make_config(T, d, max(k, 2), k, I=64, act_dtype=dt, weight_dtype=dt)
+    out = act_empty((T, d), dt)
+    moe.combine(cfg, to_dev(y), to_dev(slot_pos), to_dev(ysh), out)
+    torch.cuda.synchronize()
+    ref = O.combine(O.decode_act(y, dt), slot_pos, None if ysh is None else O.decode_act(ysh, dt), k)
+    got = act_to_f64(out, dt)
+    rel = 2.0 ** -8 if dt == "bf16" else 1e-6
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-6 * max(np.max(np.abs(ref)), 1e-30))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_quantize_rows_random(seed):
+    """Seeded random bf16 rows for the e4m3 row quantiser: per-row magnitudes from 1e-30 to
+    3e4, zero rows, single-spike rows and sign mixes, 1 to 3000 rows of 8 to 8192 columns:
+    codes and scales bit-exact against the oracle's quantiser."""
+    g = np.random.default_rng(1000 + seed)
+    rows = int(g.choice([1, 2, 63, 300, 3000]))
+    cols = 8 * int(g.integers(1, 1025))
+    mag = np.exp(g.uniform(np.log(1e-30), np.log(3e4), size=(rows, 1)))
+    a32 = (g.standard_normal((rows, cols)) * mag).astype(np.float32)
+    a32[g.random(rows) < 0.1] = 0.0
+    spikes = np.nonzero(g.random(rows) < 0.1)[0]
+    a32[spikes, g.integers(0, cols, size=spikes.size)] = np.float32(-2e4)
+    x = W.encode_bf16(a32)
+    print(f"rows={rows} cols={cols}")
+    cfg = moe.make_config(rows, 128, 8, 2, I=64, weight_dtype="e4m3", fp8_act=True)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    moe.quantize_rows(cfg, to_dev(x), rows, cols, q, sc)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_rows_e4m3(O.decode_bf16(x))
+    assert np.array_equal(sc.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
 # ----------------------------------------------------------------------------- forward
 FORWARD_CASES = ["tiny_fp32", "fusionllm_bf16", "decode_bf16", "skewed_bf16", "fp8_relu2",
                  "small_swiglu", "small_relu2_e4m3", "small_swiglu_e4m3", "small_f32",
