@@ -74,6 +74,28 @@ def test_noalloc_matches_forward_on_two_calls(name):
         assert err <= bound, f"{name} T={T}: max|delta| {err} > {bound}"
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_noalloc_random_configs(seed):
+    """The seeded random layers of the forward parity tests, two calls in a row on the shared
+    array (all tokens, then a third of them): bit for bit equal to moe_forward_ex."""
+    from test_gpu_parity import random_shape
+    shape = random_shape(seed)
+    lay = W.make_layer(shape, cache=False)
+    w = weights(lay)
+    x_all = to_dev(lay.x)
+    for T in (shape.T, max(1, shape.T // 3)):
+        cfg = config(shape, T=T)
+        assert moe.workspace_size(cfg) <= SCRATCH_BYTES
+        x = x_all[:T].contiguous()
+        out = act_empty((T, shape.d), shape.act_dtype)
+        out.fill_(0)
+        print(f"seed {seed} T={T}: moe_forward_noalloc", flush=True)
+        moe.forward_noalloc(cfg, w, x, out)
+        staged = _reference(shape, w, x, T, staged=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, staged), f"seed {seed} T={T}: differs from moe_forward_ex"
+
+
 def test_noalloc_on_a_caller_stream():
     shape = W.small_shape(T=300, d=320, E=16, k=4, G=4, Gk=2, S=2, I=192, seed=31)
     lay = W.make_layer(shape, cache=False)
