@@ -257,3 +257,17 @@ def test_gemm_kernel_path_rejects_bad_arguments(lib):
     assert lib.moe_gemm_kernel_path(ctypes.byref(cfg()), 2, 0, 10, ctypes.byref(p)) == 1
     assert lib.moe_gemm_kernel_path(ctypes.byref(cfg(S=0)), 0, 1, 10, ctypes.byref(p)) == 1
     assert lib.moe_gemm_kernel_path(ctypes.byref(cfg(d=2004)), 0, 0, 10, ctypes.byref(p)) == 2
+
+
+def test_random_test_layers_are_inside_the_contract(lib):
+    """The seeded random layers of the GPU sweeps are configurations the library accepts
+    (host-side validation only), so every GPU case exercises a kernel, not an error path."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from test_gpu_parity import random_shape
+    from test_gpu_backward import random_backward_shape
+    from _dev import config
+    for seed in range(96):
+        moe.workspace_size(config(random_shape(seed)))
+    for seed in range(32):
+        moe.backward_workspace_size(config(random_backward_shape(seed)))
