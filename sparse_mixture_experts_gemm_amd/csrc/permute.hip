@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void hist_kernel(int T, int E, int k, int chun
     if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);   // out-of-range ids are skipped
   }
   __syncthreads();
-  if (threadIdx.x < E) chunk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
+  if ((int)threadIdx.x < E) chunk_hist[(size_t)blockIdx.x * E + threadIdx.x] = h[threadIdx.x];
 }
 
 __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int capacity,
