@@ -97,7 +97,6 @@ class Runner:
 
     def counts(self):
         """Per-expert row counts of the last forward (from its workspace)."""
-        import ctypes
         s = self.s
         # the workspace starts with topk_idx [T*k] int32; counts follow topk_w, 256-aligned
         al = lambda n: (n + 255) // 256 * 256
