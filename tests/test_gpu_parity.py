@@ -512,6 +512,16 @@ def test_permute_bit_exact_on_oracle_routing(name):
     _check_permute(s.T, s.E, s.k, r["idx"], r["w"].astype(np.float32))
 
 
+def test_permute_large_batch_with_capacity():
+    """2.4 M slots (300000 tokens, k = 8 of 64 experts) with a capacity: each of the at most
+    64 chunks of the two-launch path spans thousands of tokens; maps bit-exact."""
+    T, E, k = 300000, 64, 8
+    rng = np.random.default_rng(300)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    _check_permute(T, E, k, idx, w, capacity_factor=0.9)
+
+
 @pytest.mark.parametrize("name,cf", [("fusionllm_bf16", 1.25), ("fusionllm_bf16", 0.5),
                                      ("decode_bf16", 1.0), ("skewed_bf16", 1.25),
                                      ("small_swiglu", 0.3), ("single_token", 0.01),
@@ -525,7 +535,8 @@ def test_permute_with_capacity_bit_exact(name, cf):
 @pytest.mark.parametrize("T,E,k,pattern", [(1, 64, 6, "random"), (63, 64, 6, "random"),
                                            (257, 8, 8, "random"), (1000, 64, 1, "one_expert"),
                                            (700, 64, 6, "first_six"), (5000, 16, 3, "random"),
-                                           (10000, 64, 6, "random"), (8192, 64, 6, "first_six")])
+                                           (10000, 64, 6, "random"), (8192, 64, 6, "first_six"),
+                                           (300000, 64, 8, "random")])
 def test_permute_edge_cases(T, E, k, pattern):
     rng = np.random.default_rng(T + E + k)
     if pattern == "random":
