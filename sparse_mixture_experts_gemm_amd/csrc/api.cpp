@@ -182,7 +182,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Workspace of moe_forward, in carve order.
 struct Carve {
   size_t topk_idx, topk_w, counts, offsets, perm_token, slot_pos, perm_weight, perm_ws;
-  size_t scores, stats_ws, x_norm, x_q, x_scale;
+  size_t scores, stats_ws, route_part, x_norm, x_q, x_scale;
   size_t h_routed, h_shared, y_routed, y_shared, total;
 };
 
@@ -203,6 +203,8 @@ Carve carve(const moe_config* c) {
   w.perm_ws = take(moe::permute_ws_bytes((int)T, (int)E));
   w.scores = take(T * E * 4);                    // only written when statistics are asked
   w.stats_ws = take(moe::stats_ws_bytes((int)T, (int)E));
+  // partial router logits of a small batch
+  w.route_part = take(T <= (size_t)moe::kSplitRouteTokens ? moe::split_route_part_bytes((int)T, (int)E) : 0);
   w.x_norm = take(c->pre_norm ? T * d * as : 0); // normalised input of a pre-norm layer
   w.x_q = take(c->fp8_act ? T * d : 0);          // e4m3 activations of the up projections
   w.x_scale = take(c->fp8_act ? T * 4 : 0);
@@ -614,11 +616,16 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* w, cons
       rp.x_norm = at(cv.x_norm);
     }
     float* scores = stats ? static_cast<float*>(at(cv.scores)) : nullptr;
+    // a small batch routes through partial logits spread over many CUs
+    const bool split = moe::split_route_applies(rp, cfg->act_dtype);
+    float* rpart = static_cast<float*>(at(cv.route_part));
     auto route = [&]() {
       mark(0);
       if (e == hipSuccess)
-        e = moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores, idx, tw,
-                              stream);
+        e = split ? moe::launch_route_split(rp, x, w->router, w->logit_bias, rpart, scores, idx,
+                                            tw, stream)
+                  : moe::launch_route(rp, cfg->act_dtype, x, w->router, w->logit_bias, scores,
+                                      idx, tw, stream);
       mark(1);
     };
     // the shared experts need only the up-projection input: x, or the normalised rows

@@ -54,6 +54,15 @@ enum class Stage { Up = 0, Down = 1 };
 hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, const void* router,
                         const float* bias, float* scores, int32_t* idx, float* w,
                         hipStream_t s);
+// Small batches of bf16 tokens (no pre-norm): the router's logits as four partial sums
+// spread over many workgroups (into part, split_route_part_bytes), then one wave per token
+// sums them, scores and selects.  Bit for bit launch_route.
+constexpr int kSplitRouteTokens = 256;
+bool split_route_applies(const RouteParams& p, int act_dtype);
+size_t split_route_part_bytes(int T, int E);
+hipError_t launch_route_split(const RouteParams& p, const void* x, const void* router,
+                              const float* bias, float* part, float* scores, int32_t* idx,
+                              float* w, hipStream_t s);
 hipError_t launch_select(const RouteParams& p, const float* scores, const float* keys,
                          int32_t* idx, float* w, hipStream_t s);
 

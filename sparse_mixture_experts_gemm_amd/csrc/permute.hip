@@ -16,9 +16,9 @@
 // With an expert capacity ("MoE 数学：路由、容量与平衡详解" of "大模型工程（一）": tokens beyond an
 // expert's capacity are dropped), a slot whose rank inside its expert reaches the
 // capacity gets slot_pos -1 and no row; counts and offsets count the kept rows.
-// Up to kFusedMaxTokens tokens (and kFusedMaxSlots pairs), one workgroup of 16 waves does both steps in a
-// single launch from an LDS copy of topk_idx (each wave owns a contiguous run of tokens; the
-// scan runs between two barriers).
+// Up to kFusedMaxTokens tokens (and kFusedMaxSlots pairs), one workgroup of 16 waves (of 4
+// waves up to kSmallSlots pairs) does both steps in a single launch from an LDS copy of
+// topk_idx (each wave owns a contiguous run of tokens; the scan runs between two barriers).
 #include "common.h"
 #include "internal.h"
 #include "permute_core.h"
@@ -137,29 +137,34 @@ __global__ __launch_bounds__(64) void scatter_kernel(int T, int E, int k, int ca
 
 constexpr int kFusedMaxTokens = 1024;   // above this, one workgroup is slower than two launches
 constexpr int kFusedMaxSlots = 28672;   // T * k staged in LDS (112 KB)
+// Small batches (T * k <= kSmallSlots): a workgroup of 4 waves and 8 KB of staged ids.  It
+// fits a CU beside the shared experts' GEMM that runs on the second stream meanwhile; the
+// 16-wave, 112 KB workgroup has to wait until one of that GEMM's workgroups leaves a CU.
+constexpr int kSmallSlots = 2048;
 
-// Up to kFusedMaxTokens tokens: one workgroup of 16 waves.  The whole topk_idx array is
-// first copied into LDS with every load in flight at once; histogram, scan and scatter
-// then read it from LDS.  Each wave owns a contiguous run of tokens.
-__global__ __launch_bounds__(1024) void permute_fused_kernel(int T, int E, int k, int capacity,
-                                                             const int32_t* __restrict__ idx,
-                                                             const float* __restrict__ topk_w,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ perm_token,
-                                                             int32_t* __restrict__ slot_pos,
-                                                             float* __restrict__ perm_weight) {
-  __shared__ __align__(16) int sidx[kFusedMaxSlots];
-  __shared__ PermuteLds pl;
+// One workgroup of W waves.  The whole topk_idx array is first copied into LDS with every
+// load in flight at once; histogram, scan and scatter then read it from LDS.  Each wave
+// owns a contiguous run of tokens.
+template <int W, int MAXSLOTS>
+__global__ __launch_bounds__(W * 64) void permute_fused_kernel(int T, int E, int k, int capacity,
+                                                               const int32_t* __restrict__ idx,
+                                                               const float* __restrict__ topk_w,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ perm_token,
+                                                               int32_t* __restrict__ slot_pos,
+                                                               float* __restrict__ perm_weight) {
+  __shared__ __align__(16) int sidx[MAXSLOTS];
+  __shared__ PermuteLds<W> pl;
   const int nslot = T * k;
   // stage topk_idx (16-byte loads where the array allows, then the tail)
   const int n4 = ((reinterpret_cast<uintptr_t>(idx) & 15) == 0) ? nslot / 4 : 0;
-  for (int i = threadIdx.x; i < n4; i += 1024)
+  for (int i = threadIdx.x; i < n4; i += W * 64)
     reinterpret_cast<int4*>(sidx)[i] = reinterpret_cast<const int4*>(idx)[i];
-  for (int i = 4 * n4 + threadIdx.x; i < nslot; i += 1024) sidx[i] = idx[i];
+  for (int i = 4 * n4 + threadIdx.x; i < nslot; i += W * 64) sidx[i] = idx[i];
   __syncthreads();
-  permute_lds(T, E, k, capacity, sidx, topk_w, pl, counts, offsets, perm_token, slot_pos,
-              perm_weight);
+  permute_lds<W>(T, E, k, capacity, sidx, topk_w, pl, counts, offsets, perm_token, slot_pos,
+                 perm_weight);
 }
 
 }  // namespace
@@ -174,9 +179,16 @@ hipError_t launch_permute(int T, int E, int k, int capacity, const int32_t* idx,
                           const float* topk_w, int32_t* counts, int32_t* offsets,
                           int32_t* perm_token, int32_t* slot_pos, float* perm_weight, void* ws,
                           hipStream_t s) {
+  if ((long long)T * k <= kSmallSlots && k <= 8) {
+    hipLaunchKernelGGL((permute_fused_kernel<4, kSmallSlots>), dim3(1), dim3(256), 0, s, T, E, k,
+                       capacity, idx, topk_w, counts, offsets, perm_token, slot_pos,
+                       perm_weight);
+    return hipGetLastError();
+  }
   if (T <= kFusedMaxTokens && (long long)T * k <= kFusedMaxSlots && k <= 8) {
-    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(1024), 0, s, T, E, k, capacity, idx,
-                       topk_w, counts, offsets, perm_token, slot_pos, perm_weight);
+    hipLaunchKernelGGL((permute_fused_kernel<16, kFusedMaxSlots>), dim3(1), dim3(1024), 0, s, T,
+                       E, k, capacity, idx, topk_w, counts, offsets, perm_token, slot_pos,
+                       perm_weight);
     return hipGetLastError();
   }
   const int chunk = chunk_tokens(T);

@@ -6,13 +6,13 @@
 
 namespace moe {
 
-constexpr int kPermWaves = 16;   // the workgroup is 16 waves (1024 threads)
-
+// LDS of a workgroup of W waves (W * 64 threads)
+template <int W>
 struct PermuteLds {
-  int hist[kPermWaves][64];
-  int run[kPermWaves][64];       // rank inside its expert of the wave's next slot
+  int hist[W][64];
+  int run[W][64];                // rank inside its expert of the wave's next slot
   int koff[64];                  // first permuted row of each expert
-  unsigned long long mask[kPermWaves][64];
+  unsigned long long mask[W][64];
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -22,9 +22,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // sidx: [T * k] expert ids in LDS; wsrc: [T * k] routing weights (LDS or global) or null.
 // Each expert keeps its first `capacity` slots (token order); the others get slot_pos -1.
-// Every thread of the workgroup must call it.  k <= 8, E <= 64.
+// Every thread of the workgroup (W waves) must call it.  k <= 8, E <= 64.
+template <int W>
 __device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, const int* sidx,
-                                            const float* wsrc, PermuteLds& pl,
+                                            const float* wsrc, PermuteLds<W>& pl,
                                             int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets,
                                             int32_t* __restrict__ perm_token,
@@ -33,7 +34,7 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, c
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // tokens per wave: a multiple of 64 so that every scatter step is a full wave of tokens
-  const int per = (((T + kPermWaves - 1) / kPermWaves) + 63) & ~63;
+  const int per = (((T + W - 1) / W) + 63) & ~63;
   const int tbeg = min(T, wave * per);
   const int tend = min(T, tbeg + per);
 
@@ -47,7 +48,7 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, c
   if (wave == 0) {
     const int e = lane;
     int total = 0;
-    for (int w = 0; w < kPermWaves; ++w) total += (e < E) ? pl.hist[w][e] : 0;
+    for (int w = 0; w < W; ++w) total += (e < E) ? pl.hist[w][e] : 0;
     const int kept = min(total, capacity);
     int incl = kept;
 #pragma unroll
@@ -60,7 +61,7 @@ __device__ __forceinline__ void permute_lds(int T, int E, int k, int capacity, c
       offsets[e] = incl - kept;
       pl.koff[e] = incl - kept;
       int rank = 0;
-      for (int w = 0; w < kPermWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         pl.run[w][e] = rank;
         rank += pl.hist[w][e];
       }

@@ -123,6 +123,13 @@ __device__ __forceinline__ void score_select_write(float logit, bool valid, int 
   select_write(s, key, valid, lane, p, t, idx, wout);
 }
 
+// The bf16 router's logit is the sum of 16 partial dot products, partial w over the
+// 32-wide K-steps w, w + 16, w + 32, ...  They are summed as four sums of four, always in
+// this order, so that a split of the partials over workgroups gives the same bits.
+__device__ __forceinline__ float sum4(float a, float b, float c, float d) {
+  return ((a + b) + c) + d;
+}
+
 // bf16 router: 16 tokens per workgroup; its 16 waves split K in 32-wide MFMA steps
 // (wave w takes steps w, w+16, ...), so each wave needs a single round of loads for d = 2048.
 constexpr int kRouteWaves = 16;
@@ -301,12 +308,99 @@ __global__ __launch_bounds__(1024) void route_bf16_kernel(RouteParams p,
   const bool valid = lane < p.E;
   float l = 0.0f;
   if (valid) {
+    float q[4];
 #pragma unroll
-    for (int w = 0; w < kRouteWaves; ++w) l += part[w][row][lane];   // fixed order
+    for (int j = 0; j < 4; ++j)
+      q[j] = sum4(part[4 * j][row][lane], part[4 * j + 1][row][lane], part[4 * j + 2][row][lane],
+                  part[4 * j + 3][row][lane]);
+    l = sum4(q[0], q[1], q[2], q[3]);
     if (bias != nullptr) l += bias[lane];
   }
   score_select_write(l, valid, lane, p, t, scores, idx, wout);
 }
+
+// Small batches (the decode shape): the one-workgroup-per-16-tokens router above reads the
+// whole E x d router matrix into each of its few CUs, which bounds it by one CU's load
+// rate.  Here the same logits are spread over (16-token block, 16-expert tile, quarter)
+// workgroups: wave w of quarter j computes partial 4j + w of the kernel above (the same
+// K-steps, MFMA chain and operands) and the workgroup writes the sum of its four, in the
+// same order, to part[j][t][e].  route_select_part_kernel finishes the sum, scores and
+// selects with one wave per token, so a small batch routes bit for bit like the kernel
+// above.  (Selection costs a few hundred instructions per token: one workgroup selecting
+// for the whole batch is bound by one CU's issue rate, so it stays spread over CUs.)
+template <bool KTAIL>
+__global__ __launch_bounds__(256) void route_part_kernel(RouteParams p,
+                                                         const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wr,
+                                                         float* __restrict__ part) {
+  __shared__ float red[4][16][17];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouteTok;
+  const int e0 = blockIdx.y * 16;
+  const int quarter = blockIdx.z;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const bool row_ok = (t0 + m) < p.T;
+  const bool col_ok = (e0 + m) < p.E;
+  const uint16_t* xrow = x + (size_t)(row_ok ? t0 + m : 0) * p.d;
+  const uint16_t* wrow = wr + (size_t)(col_ok ? e0 + m : 0) * p.d;
+  const int nsteps = KTAIL ? (p.d + 31) >> 5 : p.d >> 5;
+  auto load = [&](const uint16_t* r, bool ok, int kk) -> uint4 {
+    return (ok && (!KTAIL || kk < p.d)) ? *reinterpret_cast<const uint4*>(r + kk)
+                                        : make_uint4(0, 0, 0, 0);
+  };
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  int st = 4 * quarter + wave;
+  for (; st + 3 * kRouteWaves < nsteps; st += 4 * kRouteWaves) {
+    uint4 av[4], bv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = (st + kRouteWaves * u) * 32 + g * 8;
+      av[u] = load(xrow, row_ok, kk);
+      bv[u] = load(wrow, col_ok, kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                    __builtin_bit_cast(bf16x8, bv[u]), acc, 0,
+                                                    0, 0);
+  }
+  for (; st < nsteps; st += kRouteWaves) {
+    const int kk = st * 32 + g * 8;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8, load(xrow, row_ok, kk)),
+        __builtin_bit_cast(bf16x8, load(wrow, col_ok, kk)), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][4 * g + i][m] = acc[i];
+  __syncthreads();
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  if (t0 + r < p.T && e0 + c < p.E)
+    part[((size_t)quarter * p.T + t0 + r) * p.E + e0 + c] =
+        sum4(red[0][r][c], red[1][r][c], red[2][r][c], red[3][r][c]);
+}
+
+// One wave per token (lane = expert): the sum of the four quarters of each logit in order,
+// the logit bias, then scores and selection as in the kernels above.
+__global__ __launch_bounds__(256) void route_select_part_kernel(RouteParams p,
+                                                                const float* __restrict__ part,
+                                                                const float* __restrict__ bias,
+                                                                float* scores, int32_t* idx,
+                                                                float* wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;  // whole wave
+  const bool valid = lane < p.E;
+  float l = 0.0f;
+  if (valid) {
+    const size_t o = (size_t)t * p.E + lane, n = (size_t)p.T * p.E;
+    l = sum4(part[o], part[o + n], part[o + 2 * n], part[o + 3 * n]);
+    if (bias != nullptr) l += bias[lane];
+  }
+  score_select_write(l, valid, lane, p, t, scores, idx, wout);
+}
+
 
 // fp32 router: one wave per token, lane = expert, plain fp32 FMA over the dim.  Pre-norm:
 // the wave first computes the token's 1/rms and writes the normalised row, and every lane
@@ -375,6 +469,25 @@ hipError_t launch_route(const RouteParams& p, int act_dtype, const void* x, cons
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p, static_cast<const float*>(x),
                        static_cast<const float*>(router), bias, scores, idx, w);
   }
+  return hipGetLastError();
+}
+
+bool split_route_applies(const RouteParams& p, int act_dtype) {
+  return act_dtype == MOE_BF16 && p.norm_gamma == nullptr && p.T <= kSplitRouteTokens;
+}
+
+size_t split_route_part_bytes(int T, int E) { return (size_t)4 * T * E * sizeof(float); }
+
+hipError_t launch_route_split(const RouteParams& p, const void* x, const void* router,
+                              const float* bias, float* part, float* scores, int32_t* idx,
+                              float* w, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  dim3 grid((p.T + kRouteTok - 1) / kRouteTok, (p.E + 15) / 16, 4);
+  auto kern = (p.d & 31) == 0 ? route_part_kernel<false> : route_part_kernel<true>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, p, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(router), part);
+  hipLaunchKernelGGL(route_select_part_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p, part,
+                     bias, scores, idx, w);
   return hipGetLastError();
 }
 

@@ -621,13 +621,21 @@ def _ws_maps(ws, T, k, E):
 
 @pytest.mark.parametrize("name,T", [("decode_bf16", 1), ("decode_bf16", 17), ("decode_bf16", 64),
                                     ("fusionllm_bf16", 128), ("biased_groups_n2", 100),
-                                    ("tail_bf16", 77), ("small_relu2_e4m3", 128)])
+                                    ("tail_bf16", 77), ("small_relu2_e4m3", 128),
+                                    # last split-logit batch, first one-launch batch; the last
+                                    # and first batches of the 4-wave permutation
+                                    ("fusionllm_bf16", 256), ("fusionllm_bf16", 257),
+                                    ("fusionllm_bf16", 341), ("fusionllm_bf16", 342)])
 def test_small_batch_forward_routes_and_permutes_like_the_separate_calls(name, T):
     """The routing (indices, weights) and permutation maps that moe_forward leaves in its
     workspace for a small batch equal those of moe_route followed by moe_permute on the same
-    input, bit for bit (selection bias, capacity and a dim off the 32-grid included)."""
+    input, bit for bit (selection bias, capacity and a dim off the 32-grid included).  Up to
+    256 tokens the forward computes the router logits as partial sums spread over many
+    workgroups, moe_route in one launch per 16 tokens: both sum the same partials in the
+    same order."""
     s = shape_of(name)
     lay = layer_of(name)
+    assert T <= lay.x.shape[0], "the case must take its rows from the layer's input"
     wts = weights(lay)
     x = to_dev(lay.x)[:T].contiguous()
     cfg = config(s, T=T)
